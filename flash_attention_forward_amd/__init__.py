@@ -1,0 +1,16 @@
+"""Flash-attention forward for AMD Instinct MI355X (gfx950).
+
+The kernels live in ``libattn.so`` (C ABI in ``include/attn.h``); ``attn``
+is its thin Python binding. Importing this package does not load the
+library; the first call does, and fails loudly if it is missing.
+"""
+from .attn import (  # noqa: F401
+    AttnError,
+    DecodeWorkspace,
+    attn_decode_combine,
+    attn_decode_fwd,
+    attn_prefill_fwd,
+    decode,
+    lib,
+    prefill,
+)

@@ -1,0 +1,207 @@
+"""Thin ctypes binding of libattn (include/attn.h).
+
+The functions named like the C entry points (``attn_prefill_fwd``,
+``attn_decode_fwd``, ``attn_decode_combine``) take torch tensors on the GPU
+and only marshal arguments: data pointers, element strides, sizes and the
+current HIP stream. Every step of the computation runs in the HIP kernels.
+``prefill`` and ``decode`` are conveniences that allocate outputs and the
+decode workspace with torch, then call the entry points.
+
+Loading fails loudly when the library is missing or a tensor is not on a
+GPU: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn.so")
+
+ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "kernel launch failed"}
+SYMBOLS = ("attn_prefill_fwd", "attn_decode_fwd", "attn_decode_combine", "attn_decode_workspace_size",
+           "attn_status_string")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {STATUS.get(status, 'unknown')} (status {status})")
+        self.status = status
+
+
+class Strides(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seq", ctypes.c_int64), ("head", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libattn with argument types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m flash_attention_forward_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.attn_prefill_fwd.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, i32, i32, i32, i32, i32,
+                                   i32, i32, f32, i32, i32, vp]
+    L.attn_prefill_fwd.restype = i32
+    L.attn_decode_fwd.argtypes = [vp, Strides, vp, vp, Strides, vp, i32, i32, vp, i32, i32, i32, i32, i32, i32,
+                                  f32, i32, vp, vp, i32, i32, vp]
+    L.attn_decode_fwd.restype = i32
+    L.attn_decode_combine.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, Strides, i32, vp]
+    L.attn_decode_combine.restype = i32
+    L.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t),
+                                             ctypes.POINTER(ctypes.c_size_t)]
+    L.attn_decode_workspace_size.restype = i32
+    L.attn_status_string.argtypes = [i32]
+    L.attn_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+# ----------------------------------------------------------------------------- marshalling helpers
+def _dtype_code(t) -> int:
+    import torch
+
+    codes = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _gpu(t, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (libattn has no CPU path)")
+    return t
+
+
+def _strides4(t, name: str) -> Strides:
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError(f"{name} must be 4-D [batch, seq, heads, head_dim] with a contiguous last dim")
+    return Strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise AttnError(fn, rc)
+
+
+# ----------------------------------------------------------------------------- entry points
+def attn_prefill_fwd(q, k, v, o, scale: float, causal: bool, window: int = 0, stream=None) -> None:
+    """O <- attention(q, k, v). q, o: [B, Sq, Hq, D]; k, v: [B, Skv, Hkv, D]; same dtype."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _gpu(t, n)
+    B, Sq, Hq, D = q.shape
+    Bk, Skv, Hkv, Dk = k.shape
+    if v.shape != k.shape or o.shape != q.shape or Bk != B or Dk != D:
+        raise ValueError("shape mismatch between q, k, v, o")
+    dt = _dtype_code(q)
+    if not (k.dtype == v.dtype == o.dtype == q.dtype):
+        raise TypeError("q, k, v, o must share one dtype")
+    rc = lib().attn_prefill_fwd(_ptr(q), _strides4(q, "q"), _ptr(k), _strides4(k, "k"), _ptr(v), _strides4(v, "v"),
+                                _ptr(o), _strides4(o, "o"), dt, B, Hq, Hkv, Sq, Skv, D, float(scale), int(bool(causal)),
+                                int(window), _stream(stream))
+    _check("attn_prefill_fwd", rc)
+
+
+def attn_decode_fwd(q, k_cache, v_cache, cache_len, part_o, part_lse, split_len: int, max_splits: int,
+                    scale: float, block_table=None, window: int = 0, stream=None) -> None:
+    """Split-KV partials. Paged if block_table is given ([B, max_pages] uint32 stored as int32)."""
+    import torch
+
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (cache_len, "cache_len"),
+                 (part_o, "part_o"), (part_lse, "part_lse")):
+        _gpu(t, n)
+    if cache_len.dtype != torch.int32 or part_o.dtype != torch.float32 or part_lse.dtype != torch.float32:
+        raise TypeError("cache_len must be int32 and part_o / part_lse float32")
+    B, sa, Hq, D = q.shape
+    if k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
+        raise ValueError("k_cache and v_cache must have the same shape and strides")
+    Hkv = k_cache.shape[2]
+    if block_table is not None:
+        _gpu(block_table, "block_table")
+        if block_table.dtype not in (torch.int32, torch.uint32) or not block_table.is_contiguous():
+            raise TypeError("block_table must be a contiguous 32-bit tensor")
+        maxp, ps = block_table.shape[1], k_cache.shape[1]
+    else:
+        maxp, ps = 0, 0
+    rc = lib().attn_decode_fwd(_ptr(q), _strides4(q, "q"), _ptr(k_cache), _ptr(v_cache), _strides4(k_cache, "k_cache"),
+                               _ptr(block_table), maxp, ps, _ptr(cache_len), _dtype_code(q), B, sa, Hq, Hkv, D,
+                               float(scale), int(window), _ptr(part_o), _ptr(part_lse), int(split_len),
+                               int(max_splits), _stream(stream))
+    _check("attn_decode_fwd", rc)
+
+
+def attn_decode_combine(part_o, part_lse, cache_len, split_len: int, max_splits: int, o, stream=None) -> None:
+    """o [B, s_active, Hq, D] <- LSE merge of the partials."""
+    for t, n in ((part_o, "part_o"), (part_lse, "part_lse"), (cache_len, "cache_len"), (o, "o")):
+        _gpu(t, n)
+    B, sa, Hq, D = o.shape
+    rc = lib().attn_decode_combine(_ptr(part_o), _ptr(part_lse), _ptr(cache_len), int(split_len), int(max_splits),
+                                   B, sa, Hq, D, _ptr(o), _strides4(o, "o"), _dtype_code(o), _stream(stream))
+    _check("attn_decode_combine", rc)
+
+
+# ----------------------------------------------------------------------------- conveniences
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)
+
+
+def prefill(q, k, v, scale: float | None = None, causal: bool = False, window: int = 0, out=None, stream=None):
+    import torch
+
+    o = torch.empty_like(q) if out is None else out
+    attn_prefill_fwd(q, k, v, o, default_scale(q.shape[-1]) if scale is None else scale, causal, window, stream)
+    return o
+
+
+class DecodeWorkspace:
+    """part_o / part_lse buffers for attn_decode_fwd, reusable across calls of the same shape."""
+
+    def __init__(self, batch: int, s_active: int, n_q_heads: int, head_dim: int, max_splits: int, device):
+        import torch
+
+        self.max_splits = max_splits
+        self.part_o = torch.empty((batch, s_active, n_q_heads, max_splits, head_dim), dtype=torch.float32, device=device)
+        self.part_lse = torch.empty((batch, s_active, n_q_heads, max_splits), dtype=torch.float32, device=device)
+
+
+def max_splits_for(max_len: int, split_len: int) -> int:
+    return max(1, -(-max_len // split_len))
+
+
+def decode(q, k_cache, v_cache, cache_len, block_table=None, scale: float | None = None, window: int = 0,
+           split_len: int = 512, max_len: int | None = None, workspace: DecodeWorkspace | None = None, out=None,
+           stream=None):
+    """Split-KV decode followed by the combine, both on the current stream."""
+    import torch
+
+    B, sa, Hq, D = q.shape
+    if max_len is None:
+        max_len = block_table.shape[1] * k_cache.shape[1] if block_table is not None else k_cache.shape[1]
+    ms = max_splits_for(max_len, split_len)
+    ws = workspace or DecodeWorkspace(B, sa, Hq, D, ms, q.device)
+    if ws.max_splits < ms:
+        raise ValueError("workspace has too few splits")
+    o = torch.empty_like(q) if out is None else out
+    sc = default_scale(D) if scale is None else scale
+    attn_decode_fwd(q, k_cache, v_cache, cache_len, ws.part_o, ws.part_lse, split_len, ws.max_splits, sc,
+                    block_table, window, stream)
+    attn_decode_combine(ws.part_o, ws.part_lse, cache_len, split_len, ws.max_splits, o, stream)
+    return o

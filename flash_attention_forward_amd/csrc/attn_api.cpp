@@ -1,0 +1,153 @@
+// C ABI of libattn: argument validation, kernel selection, launch.
+//
+// Every host-checkable precondition is checked before the first HIP call,
+// so a rejected call enqueues nothing and leaves no HIP error state. After a
+// launch the HIP error state is read (which also clears it) and turned into
+// ATTN_ERR_LAUNCH.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+bool supported_head_dim(int d) { return d == 64 || d == 128 || d == 256; }
+
+int elem_bytes(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+bool strides_ok(const attn_strides& s, int eb) {
+    return s.batch >= 0 && s.seq >= 0 && s.head >= 0 && (s.batch * eb) % 16 == 0 && (s.seq * eb) % 16 == 0 &&
+           (s.head * eb) % 16 == 0;
+}
+
+attn::Strides3 conv(const attn_strides& s) { return attn::Strides3{s.batch, s.seq, s.head}; }
+
+// Sign flip applied to Q when scale < 0, so kernels only ever see |scale|.
+uint32_t q_flip_mask(float scale, int dtype) {
+    if (!(scale < 0.f)) return 0u;
+    return dtype == ATTN_F32 ? 0x80000000u : 0x80008000u;
+}
+
+float scaled_log2e(float scale) { return (float)(std::fabs((double)scale) * 1.4426950408889634); }
+
+int status_of(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_INVALID: return "invalid argument";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+        case ATTN_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int attn_prefill_fwd(const void* q, attn_strides q_st, const void* k, attn_strides k_st, const void* v,
+                     attn_strides v_st, void* o, attn_strides o_st, attn_dtype dtype, int batch, int n_q_heads,
+                     int n_kv_heads, int seqlen_q, int seqlen_kv, int head_dim, float scale, int causal, int window,
+                     void* hip_stream) {
+    if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
+    if (batch < 0 || n_q_heads < 0 || n_kv_heads < 0 || seqlen_q < 0 || seqlen_kv < 0 || head_dim <= 0)
+        return ATTN_ERR_INVALID;
+    if (!std::isfinite(scale)) return ATTN_ERR_INVALID;
+    if (batch == 0 || n_q_heads == 0 || seqlen_q == 0) return ATTN_OK;
+    if (n_kv_heads == 0 || n_q_heads % n_kv_heads != 0) return ATTN_ERR_INVALID;
+    if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
+    if (window > 0 && !causal) return ATTN_ERR_UNSUPPORTED;
+    const int eb = elem_bytes(dtype);
+    if (!q || !o || !aligned16(q) || !aligned16(o)) return ATTN_ERR_INVALID;
+    if (seqlen_kv > 0 && (!k || !v || !aligned16(k) || !aligned16(v))) return ATTN_ERR_INVALID;
+    if (!strides_ok(q_st, eb) || !strides_ok(k_st, eb) || !strides_ok(v_st, eb) || !strides_ok(o_st, eb))
+        return ATTN_ERR_INVALID;
+    const int64_t tiles = (seqlen_q + 63) / 64;
+    if (tiles * batch * n_q_heads >= (int64_t)1 << 31) return ATTN_ERR_UNSUPPORTED;
+
+    attn::PrefillParams p{};
+    p.q = q; p.k = k; p.v = v; p.o = o;
+    p.qs = conv(q_st); p.ks = conv(k_st); p.vs = conv(v_st); p.os = conv(o_st);
+    p.batch = batch; p.n_q_heads = n_q_heads; p.n_kv_heads = n_kv_heads; p.group = n_q_heads / n_kv_heads;
+    p.seqlen_q = seqlen_q; p.seqlen_kv = seqlen_kv; p.off = seqlen_kv - seqlen_q;
+    p.window = window > 0 ? window : 0;
+    p.c = scaled_log2e(scale);
+    p.qflip = q_flip_mask(scale, dtype);
+    const int mask = !causal ? attn::kMaskNone : (p.window > 0 ? attn::kMaskCausalWindow : attn::kMaskCausal);
+    return status_of(attn::launch_prefill(p, (int)dtype, head_dim, mask, (hipStream_t)hip_stream));
+}
+
+int attn_decode_workspace_size(int batch, int s_active, int n_q_heads, int head_dim, int max_splits,
+                               size_t* part_o_bytes, size_t* part_lse_bytes) {
+    if (batch < 0 || s_active < 0 || n_q_heads < 0 || head_dim < 0 || max_splits < 0) return ATTN_ERR_INVALID;
+    const size_t rows = (size_t)batch * (size_t)s_active * (size_t)n_q_heads * (size_t)max_splits;
+    if (part_o_bytes) *part_o_bytes = rows * (size_t)head_dim * sizeof(float);
+    if (part_lse_bytes) *part_lse_bytes = rows * sizeof(float);
+    return ATTN_OK;
+}
+
+int attn_decode_fwd(const void* q, attn_strides q_st, const void* k_cache, const void* v_cache, attn_strides kv_st,
+                    const uint32_t* block_table, int max_pages_per_seq, int page_size, const int32_t* cache_len,
+                    attn_dtype dtype, int batch, int s_active, int n_q_heads, int n_kv_heads, int head_dim,
+                    float scale, int window, float* part_o, float* part_lse, int split_len, int max_splits,
+                    void* hip_stream) {
+    if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
+    if (batch < 0 || s_active < 0 || n_q_heads < 0 || n_kv_heads < 0 || head_dim <= 0) return ATTN_ERR_INVALID;
+    if (!std::isfinite(scale)) return ATTN_ERR_INVALID;
+    if (batch == 0 || s_active == 0 || n_q_heads == 0) return ATTN_OK;
+    if (n_kv_heads == 0 || n_q_heads % n_kv_heads != 0) return ATTN_ERR_INVALID;
+    if (split_len <= 0 || split_len % 16 != 0 || max_splits <= 0) return ATTN_ERR_INVALID;
+    if (block_table) {
+        if (page_size <= 0 || max_pages_per_seq <= 0 || split_len % page_size != 0) return ATTN_ERR_INVALID;
+        if ((int64_t)max_splits * split_len < (int64_t)max_pages_per_seq * page_size) return ATTN_ERR_INVALID;
+    }
+    if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+    if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
+    if ((int64_t)(n_q_heads / n_kv_heads) * s_active > 16) return ATTN_ERR_UNSUPPORTED;
+    if (max_splits > 65535 * 32 || n_kv_heads > 65535 || batch > 65535) return ATTN_ERR_UNSUPPORTED;
+    const int eb = elem_bytes(dtype);
+    if (!q || !k_cache || !v_cache || !cache_len || !part_o || !part_lse) return ATTN_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(part_o)) return ATTN_ERR_INVALID;
+    if (!strides_ok(q_st, eb) || !strides_ok(kv_st, eb)) return ATTN_ERR_INVALID;
+
+    attn::DecodeParams p{};
+    p.q = q; p.k = k_cache; p.v = v_cache;
+    p.qs = conv(q_st); p.kvs = conv(kv_st);
+    p.block_table = block_table; p.cache_len = cache_len;
+    p.part_o = part_o; p.part_lse = part_lse;
+    p.batch = batch; p.s_active = s_active; p.n_q_heads = n_q_heads; p.n_kv_heads = n_kv_heads;
+    p.group = n_q_heads / n_kv_heads;
+    p.max_pages_per_seq = block_table ? max_pages_per_seq : 0;
+    p.page_size = block_table ? page_size : 1;
+    p.window = window > 0 ? window : 0;
+    p.split_len = split_len; p.max_splits = max_splits;
+    p.c = scaled_log2e(scale);
+    p.qflip = q_flip_mask(scale, dtype);
+    return status_of(attn::launch_decode(p, (int)dtype, head_dim, (hipStream_t)hip_stream));
+}
+
+int attn_decode_combine(const float* part_o, const float* part_lse, const int32_t* cache_len, int split_len,
+                        int max_splits, int batch, int s_active, int n_q_heads, int head_dim, void* o,
+                        attn_strides o_st, attn_dtype dtype, void* hip_stream) {
+    if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
+    if (batch < 0 || s_active < 0 || n_q_heads < 0 || head_dim <= 0) return ATTN_ERR_INVALID;
+    if (batch == 0 || s_active == 0 || n_q_heads == 0) return ATTN_OK;
+    if (split_len <= 0 || max_splits <= 0) return ATTN_ERR_INVALID;
+    if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+    if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
+    if ((int64_t)batch * s_active * n_q_heads >= (int64_t)1 << 31) return ATTN_ERR_UNSUPPORTED;
+    if (!part_o || !part_lse || !cache_len || !o || !aligned16(o)) return ATTN_ERR_INVALID;
+    if (!strides_ok(o_st, elem_bytes(dtype))) return ATTN_ERR_INVALID;
+
+    attn::CombineParams p{};
+    p.part_o = part_o; p.part_lse = part_lse; p.cache_len = cache_len; p.o = o; p.os = conv(o_st);
+    p.batch = batch; p.s_active = s_active; p.n_q_heads = n_q_heads;
+    p.split_len = split_len; p.max_splits = max_splits;
+    return status_of(attn::launch_combine(p, (int)dtype, head_dim, (hipStream_t)hip_stream));
+}
+
+}  // extern "C"

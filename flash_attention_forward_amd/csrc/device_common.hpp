@@ -1,0 +1,92 @@
+// Device-side helpers shared by the attention kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+// Initial running max, in scaled log2 units: finite, so that the first
+// rescale factor exp2(m_old - m_new) is exactly 0 instead of NaN.
+constexpr float kMaxInit = -1.0e30f;
+// Stand-in score for masked keys when reducing the tile max.
+constexpr float kMaskedScore = -3.4028234663852886e38f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of lane (l ^ 32) for every lane l, with one v_permlane32_swap.
+__device__ __forceinline__ float max_with_other_half(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_other_half(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Round-to-nearest-even conversions of f32 to 16-bit floats, returned as raw bits.
+template <bool BF16>
+__device__ __forceinline__ uint16_t f32_to_16(float x) {
+    if constexpr (BF16) {
+        __bf16 h = (__bf16)x;
+        return __builtin_bit_cast(uint16_t, h);
+    } else {
+        _Float16 h = (_Float16)x;
+        return __builtin_bit_cast(uint16_t, h);
+    }
+}
+template <bool BF16>
+__device__ __forceinline__ float f16bits_to_f32(uint16_t b) {
+    if constexpr (BF16) {
+        return __uint_as_float((uint32_t)b << 16);
+    } else {
+        return (float)__builtin_bit_cast(_Float16, b);
+    }
+}
+
+// 32x32x16 MFMA with f32 accumulation; operands are 8 16-bit values per lane.
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma32x32x16(s16x8 a, s16x8 b, f32x16 c) {
+    if constexpr (BF16) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+}
+
+// 16x16x32 MFMA with f32 accumulation.
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma16x16x32(s16x8 a, s16x8 b, f32x4 c) {
+    if constexpr (BF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+}
+
+// LDS transpose read: within each group of 16 lanes, lane i receives element
+// i%4 of the 8-byte rows supplied by lanes 4j + i/4 (j = 0..3). With lane s
+// of a group pointing at row (r0 + s/4), column (c0 + 4*(s%4)) of a row-major
+// 16-bit matrix, lane i gets column c0 + i of rows r0..r0+3.
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+__device__ __forceinline__ s16x8 concat4(s16x4 a, s16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+}  // namespace attn

@@ -1,0 +1,60 @@
+// Kernel parameter blocks and launchers (internal to libattn; the public
+// interface is include/attn.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct Strides3 {
+    int64_t batch, seq, head;
+};
+
+struct PrefillParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    Strides3 qs, ks, vs, os;
+    int batch, n_q_heads, n_kv_heads, group;  // group = n_q_heads / n_kv_heads
+    int seqlen_q, seqlen_kv, off;              // off = seqlen_kv - seqlen_q
+    int window;                                // > 0 only together with causal
+    int n_q_tiles;
+    float c;          // |scale| * log2(e): scores are kept in scaled log2 units
+    uint32_t qflip;   // 0x80008000 (16-bit) / 0x80000000 (f32) flips Q's sign when scale < 0
+};
+
+struct DecodeParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    Strides3 qs, kvs;
+    const uint32_t* block_table;  // NULL -> flat cache
+    const int32_t* cache_len;
+    float* part_o;
+    float* part_lse;
+    int batch, s_active, n_q_heads, n_kv_heads, group;
+    int max_pages_per_seq, page_size, page_shift;
+    int window, split_len, max_splits;
+    float c;
+    uint32_t qflip;
+};
+
+struct CombineParams {
+    const float* part_o;
+    const float* part_lse;
+    const int32_t* cache_len;
+    void* o;
+    Strides3 os;
+    int batch, s_active, n_q_heads, split_len, max_splits;
+};
+
+enum MaskMode { kMaskNone = 0, kMaskCausal = 1, kMaskCausalWindow = 2 };
+enum DType { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// Each returns the hipError_t of its launch (hipSuccess on success).
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int mask, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim, hipStream_t s);
+
+}  // namespace attn

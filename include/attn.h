@@ -1,0 +1,168 @@
+/*
+ * attn.h — flash-attention forward for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * Three entry points compute softmax attention
+ *
+ *     O = softmax(scale * Q K^T  restricted to the visible keys) V
+ *
+ * with the online-softmax recurrence (running row max m, running sum l,
+ * rescale alpha = exp(m_old - m_new) of O and l, final O * (1/l)):
+ *   - attn_prefill_fwd     long Q against K/V of the same sequence (compute bound);
+ *   - attn_decode_fwd      a few query tokens against a long, optionally paged,
+ *                          KV cache, split along the cache into partial results;
+ *   - attn_decode_combine  the log-sum-exp merge of those partials.
+ *
+ * The recurrence and its final normalisation are the ones described on the
+ * "Flash-Attention: Context (CTE)" page (section "The online-softmax
+ * recurrence") and on the minfer "03 · 8n — FA-style tiled prefill attention"
+ * page (section 2.1 "Online softmax").
+ *
+ * Conventions shared by all entry points
+ * --------------------------------------
+ * Tensors are row-major with element strides; the head_dim stride is 1.
+ *   q, o     : [batch, seqlen_q, n_q_heads, head_dim]
+ *   k, v     : [batch, seqlen_kv, n_kv_heads, head_dim]
+ * GQA: q-head h reads kv-head h / (n_q_heads / n_kv_heads); n_q_heads must
+ * be a multiple of n_kv_heads (CTE page, section "GQA and multi-head").
+ * Query row i sits at position i + (seqlen_kv - seqlen_q) (bottom-right
+ * alignment, so a decode query sits at the end of its cache). Key j is
+ * visible to row i iff
+ *     (!causal || j <= pos(i))  &&  (window <= 0 || j >= pos(i) - window + 1)
+ * (causal predicate: CTE page, "the diagonal affine_select mask"; window
+ * predicate: optimum-neuron attention guide, section "Sliding window";
+ * window <= 0 means no window, as that guide's default). A row that sees no
+ * key outputs zeros. `scale` multiplies the scores (CTE page, section
+ * "Scale"); the library never divides by sqrt(head_dim) itself.
+ *
+ * Supported: head_dim in {64, 128, 256}; dtype f32, f16 or bf16 for Q, K, V
+ * and O alike (f32 accumulation throughout; probabilities are rounded to
+ * the input dtype before the P*V product for f16/bf16).
+ *
+ * Memory and streams: every pointer argument named a tensor is a device
+ * pointer (hipMalloc / torch CUDA memory); the caller owns all of them and
+ * the library allocates nothing and keeps no state between calls. Work is
+ * enqueued on `hip_stream` (a hipStream_t; NULL = the default stream) and
+ * the functions return without synchronising. Base pointers must be 16-byte
+ * aligned and every stride times the element size must be a multiple of 16
+ * bytes.
+ *
+ * Errors: all host-checkable preconditions are validated before any HIP
+ * call; a violation returns ATTN_ERR_INVALID or ATTN_ERR_UNSUPPORTED and
+ * enqueues nothing. A failed launch returns ATTN_ERR_LAUNCH after the HIP
+ * error state has been read and cleared, so no sticky error is left behind
+ * (the minfer page's pitfall about clearing a failed launch's error).
+ * Zero-sized problems return ATTN_OK and enqueue nothing. Device-side data
+ * (block tables, cache lengths) is not validated: out-of-range page indices
+ * are undefined behaviour, as the decode page's gather treats them as a
+ * fault ("Flash-Attention: Decode (TKG)", section "Paged / block cache").
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID = 1,     /* malformed arguments (sizes, strides, alignment, NULL) */
+    ATTN_ERR_UNSUPPORTED = 2, /* well-formed but not implemented (head_dim, dtype, mask combination) */
+    ATTN_ERR_LAUNCH = 3       /* the HIP runtime rejected a launch */
+} attn_status;
+
+/* Element strides of a 4-D [batch, seq, head, head_dim] tensor. */
+typedef struct {
+    int64_t batch, seq, head;
+} attn_strides;
+
+/*
+ * Prefill / context attention.
+ *   q [batch, seqlen_q, n_q_heads, head_dim], k and v [batch, seqlen_kv,
+ *   n_kv_heads, head_dim], o [batch, seqlen_q, n_q_heads, head_dim], all of
+ *   type `dtype`, device memory, addressed through the given strides.
+ *   causal != 0 enables the causal mask; window > 0 (requires causal) adds
+ *   the sliding window. window > 0 without causal -> ATTN_ERR_UNSUPPORTED.
+ * Whole tiles of keys that no query of a tile can see are skipped; only
+ * tiles that straddle the diagonal or the window edge are masked element by
+ * element (CTE page, "Algorithm — compute-skip" and the affine_select masks).
+ */
+int attn_prefill_fwd(const void* q, attn_strides q_st, const void* k, attn_strides k_st,
+                     const void* v, attn_strides v_st, void* o, attn_strides o_st,
+                     attn_dtype dtype, int batch, int n_q_heads, int n_kv_heads,
+                     int seqlen_q, int seqlen_kv, int head_dim,
+                     float scale, int causal, int window, void* hip_stream);
+
+/*
+ * Decode attention against a KV cache, split along the cache (split-KV).
+ *   q       [batch, s_active, n_q_heads, head_dim] device, `dtype`.
+ *   Paged cache (block_table != NULL): k_cache, v_cache are
+ *           [num_pages, page_size, n_kv_heads, head_dim] with kv_st =
+ *           (page, slot, head) strides; block_table is device uint32
+ *           [batch, max_pages_per_seq]: logical token t of sequence b lives
+ *           in physical page block_table[b*max_pages_per_seq + t/page_size],
+ *           slot t%page_size (the decode page's `active_blocks_table`,
+ *           section "Paged / block cache").
+ *   Flat cache (block_table == NULL): k_cache, v_cache are
+ *           [batch, >= cache_len[b], n_kv_heads, head_dim] with kv_st =
+ *           (batch, seq, head); max_pages_per_seq and page_size are ignored.
+ *   cache_len  device int32 [batch]: valid cache tokens per sequence,
+ *           including the s_active current tokens, which the caller has
+ *           already written. Keys with index >= cache_len[b] are never used
+ *           (decode page, section "gen_mask_tkg": the index < cache length
+ *           cut); the current tokens see each other causally.
+ *   window  > 0: sliding window as in the prefill predicate; <= 0: none.
+ *   part_o  device float [batch, s_active, n_q_heads, max_splits, head_dim],
+ *   part_lse device float [batch, s_active, n_q_heads, max_splits]:
+ *           caller-owned workspace. Split s of sequence b covers cache
+ *           tokens [s*split_len, min(cache_len[b], (s+1)*split_len)). For
+ *           every split that starts below cache_len[b], part_o holds the
+ *           split's normalised attention output and part_lse its natural-log
+ *           log-sum-exp of the scaled visible scores (-inf and zeros if the
+ *           split has no visible key). Splits at or beyond cache_len[b] are
+ *           not written.
+ *   split_len must be a positive multiple of 16 (and of page_size when
+ *   paged); max_splits * split_len must cover the longest cache
+ *   (>= max_pages_per_seq * page_size when paged).
+ * Requires head_dim in {64, 128, 256}, dtype f16 or bf16, and
+ * (n_q_heads / n_kv_heads) * s_active <= 16.
+ */
+int attn_decode_fwd(const void* q, attn_strides q_st,
+                    const void* k_cache, const void* v_cache, attn_strides kv_st,
+                    const uint32_t* block_table, int max_pages_per_seq, int page_size,
+                    const int32_t* cache_len, attn_dtype dtype, int batch, int s_active,
+                    int n_q_heads, int n_kv_heads, int head_dim, float scale, int window,
+                    float* part_o, float* part_lse, int split_len, int max_splits,
+                    void* hip_stream);
+
+/*
+ * Merge of the split partials written by attn_decode_fwd with the same
+ * (cache_len, split_len, max_splits, batch, s_active, n_q_heads, head_dim):
+ *   M = max_s lse_s,  w_s = exp(lse_s - M),  O = sum_s w_s O_s / sum_s w_s
+ * over the splits that start below cache_len[b] — the cross-section merge
+ * O_acc = alpha * O_prev + O_section of the CTE page (section "Algorithm —
+ * running-sum update, reciprocal, output accumulate"), generalised to many
+ * partials. Rows whose splits are all empty output zeros.
+ *   o [batch, s_active, n_q_heads, head_dim] device, `dtype` (f16 or bf16).
+ */
+int attn_decode_combine(const float* part_o, const float* part_lse, const int32_t* cache_len,
+                        int split_len, int max_splits, int batch, int s_active, int n_q_heads,
+                        int head_dim, void* o, attn_strides o_st, attn_dtype dtype,
+                        void* hip_stream);
+
+/* Bytes of part_o and part_lse that attn_decode_fwd needs. Returns ATTN_OK or ATTN_ERR_INVALID. */
+int attn_decode_workspace_size(int batch, int s_active, int n_q_heads, int head_dim, int max_splits,
+                               size_t* part_o_bytes, size_t* part_lse_bytes);
+
+/* Static description of a status code. Never NULL. */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,153 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects malformed arguments with a status code before
+making any HIP call (the pointers passed here are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from flash_attention_forward_amd import attn as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+INVALID, UNSUPPORTED = 1, 2
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_functions_are_exported():
+    names = declared_functions()
+    assert names == sorted(A.SYMBOLS)
+    L = A.lib()
+    for n in names:
+        assert getattr(L, n) is not None
+    out = subprocess.run(["nm", "-D", "--defined-only", A.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+
+
+def test_status_strings():
+    L = A.lib()
+    assert L.attn_status_string(0) == b"ok"
+    assert L.attn_status_string(1) == b"invalid argument"
+    assert L.attn_status_string(2) == b"unsupported configuration"
+    assert L.attn_status_string(3) == b"kernel launch failed"
+    assert L.attn_status_string(99) == b"unknown status"
+
+
+def st(b, s, h):
+    return A.Strides(b, s, h)
+
+
+def prefill(**kw):
+    a = dict(q=FAKE, qs=st(2048 * 8 * 128, 8 * 128, 128), k=FAKE, ks=st(2048 * 128, 128, 128), v=FAKE,
+             vs=st(2048 * 128, 128, 128), o=FAKE, os=st(2048 * 8 * 128, 8 * 128, 128), dtype=A.ATTN_BF16, batch=1,
+             hq=8, hkv=1, sq=2048, skv=2048, d=128, scale=0.088, causal=1, window=0)
+    a.update(kw)
+    return A.lib().attn_prefill_fwd(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["o"], a["os"], a["dtype"],
+                                    a["batch"], a["hq"], a["hkv"], a["sq"], a["skv"], a["d"], a["scale"], a["causal"],
+                                    a["window"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), INVALID),
+    (dict(d=96), UNSUPPORTED),
+    (dict(d=512), UNSUPPORTED),
+    (dict(hq=6, hkv=4), INVALID),
+    (dict(hkv=0), INVALID),
+    (dict(window=64, causal=0), UNSUPPORTED),
+    (dict(q=FAKE + 2), INVALID),
+    (dict(o=0), INVALID),
+    (dict(k=0), INVALID),
+    (dict(qs=st(2048 * 8 * 128, 8 * 128 + 1, 128)), INVALID),
+    (dict(vs=st(-1, 128, 128)), INVALID),
+    (dict(batch=-1), INVALID),
+    (dict(sq=-5), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(scale=float("inf")), INVALID),
+])
+def test_prefill_rejects(kw, status):
+    assert prefill(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(sq=0), dict(hq=0), dict(batch=0, q=0, k=0, v=0, o=0)])
+def test_prefill_empty_is_noop(kw):
+    assert prefill(**kw) == 0
+
+
+def decode(**kw):
+    a = dict(q=FAKE, qs=st(32 * 128, 32 * 128, 128), k=FAKE, v=FAKE, kvs=st(16 * 8 * 128, 8 * 128, 128), bt=FAKE,
+             maxp=2048, ps=16, cl=FAKE, dtype=A.ATTN_BF16, batch=32, sa=1, hq=32, hkv=8, d=128, scale=0.088, window=0,
+             po=FAKE, pl=FAKE, split=512, ms=64)
+    a.update(kw)
+    return A.lib().attn_decode_fwd(a["q"], a["qs"], a["k"], a["v"], a["kvs"], a["bt"], a["maxp"], a["ps"], a["cl"],
+                                   a["dtype"], a["batch"], a["sa"], a["hq"], a["hkv"], a["d"], a["scale"],
+                                   a["window"], a["po"], a["pl"], a["split"], a["ms"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(split=500), INVALID),          # not a multiple of 16
+    (dict(split=0), INVALID),
+    (dict(ps=32, split=48), INVALID),    # not a multiple of the page size
+    (dict(ms=63), INVALID),              # splits do not cover max_pages * page_size
+    (dict(ps=0), INVALID),
+    (dict(dtype=A.ATTN_F32), UNSUPPORTED),
+    (dict(d=80), UNSUPPORTED),
+    (dict(sa=5), UNSUPPORTED),           # 4 q-heads per kv-head x 5 tokens > 16 rows
+    (dict(hq=30), INVALID),
+    (dict(cl=0), INVALID),
+    (dict(po=0), INVALID),
+    (dict(k=FAKE + 8), INVALID),
+    (dict(scale=float("nan")), INVALID),
+])
+def test_decode_rejects(kw, status):
+    assert decode(**kw) == status
+
+
+def test_decode_flat_ignores_page_args():
+    # flat cache: page_size/max_pages are not checked, but split_len still is
+    assert decode(bt=0, ps=0, maxp=0, split=24) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(sa=0), dict(hq=0)])
+def test_decode_empty_is_noop(kw):
+    assert decode(**kw) == 0
+
+
+def combine(**kw):
+    a = dict(po=FAKE, pl=FAKE, cl=FAKE, split=512, ms=64, batch=32, sa=1, hq=32, d=128, o=FAKE,
+             os=st(32 * 128, 32 * 128, 128), dtype=A.ATTN_BF16)
+    a.update(kw)
+    return A.lib().attn_decode_combine(a["po"], a["pl"], a["cl"], a["split"], a["ms"], a["batch"], a["sa"], a["hq"],
+                                       a["d"], a["o"], a["os"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(split=0), INVALID), (dict(ms=0), INVALID), (dict(dtype=A.ATTN_F32), UNSUPPORTED), (dict(d=32), UNSUPPORTED),
+    (dict(o=FAKE + 4), INVALID), (dict(pl=0), INVALID), (dict(os=st(3, 128, 128)), INVALID), (dict(dtype=9), INVALID),
+])
+def test_combine_rejects(kw, status):
+    assert combine(**kw) == status
+
+
+def test_workspace_size():
+    o, l = ctypes.c_size_t(), ctypes.c_size_t()
+    assert A.lib().attn_decode_workspace_size(32, 1, 32, 128, 64, ctypes.byref(o), ctypes.byref(l)) == 0
+    assert o.value == 32 * 32 * 64 * 128 * 4 and l.value == 32 * 32 * 64 * 4
+    assert A.lib().attn_decode_workspace_size(-1, 1, 32, 128, 64, ctypes.byref(o), ctypes.byref(l)) == INVALID
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    x = torch.zeros(1, 4, 1, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        A.attn_prefill_fwd(x, x, x, x, 1.0, False)

@@ -1,0 +1,198 @@
+"""GPU parity of attn_prefill_fwd against the fp64 oracle (tolerances in gpu_common)."""
+import numpy as np
+import pytest
+
+from flash_attention_forward_amd import workloads as W
+
+from gpu_common import check, gpu_prefill, oracle_prefill, sample_rows, say, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+WL = W.WORKLOADS
+
+# Same structure as the five workloads, at sizes the oracle finishes in seconds,
+# spanning several tiles with a ragged tail.
+SMALL = {
+    "c1_full": WL["c1_fp32_d64"],
+    "c1_ragged_causal": W.shrink(WL["c1_fp32_d64"], seqlen_q=200, seqlen_kv=200, causal=True),
+    "c1_d128_gqa_window": W.PrefillSpec(1, 4, 2, 150, 150, 128, "f32", causal=True, window=40),
+    "c1_d256": W.PrefillSpec(2, 2, 1, 97, 97, 256, "f32", causal=False),
+    "c2_ragged": W.shrink(WL["c2_f16_gqa_causal_2k"], seqlen_q=333, seqlen_kv=333),
+    "c3_ragged_spikes": W.shrink(WL["c3_bf16_causal_32k"], seqlen_q=700, seqlen_kv=700),
+    "c4_ragged": W.shrink(WL["c4_bf16_swa1024_d256"], n_q_heads=4, n_kv_heads=2, seqlen_q=600, seqlen_kv=600,
+                          window=150),
+    "bf16_d64_nocausal": W.PrefillSpec(2, 3, 3, 190, 190, 64, "bf16", causal=False),
+    "f16_d256_nocausal": W.PrefillSpec(1, 2, 1, 130, 130, 256, "f16", causal=False),
+    "bf16_sq_lt_skv": W.PrefillSpec(1, 4, 1, 77, 300, 128, "bf16", causal=True),
+    "bf16_sq_lt_skv_window": W.PrefillSpec(1, 4, 2, 150, 390, 128, "bf16", causal=True, window=70),
+    "bf16_sq_gt_skv": W.PrefillSpec(1, 2, 1, 260, 100, 128, "bf16", causal=True),  # early rows see nothing
+    "bf16_window1": W.PrefillSpec(1, 2, 1, 140, 140, 64, "bf16", causal=True, window=1),
+    "bf16_single_row": W.PrefillSpec(1, 8, 1, 1, 1, 128, "bf16", causal=True),
+    "f16_mqa_long_window": W.PrefillSpec(1, 8, 1, 520, 520, 128, "f16", causal=True, window=512),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_prefill_parity_small(name):
+    spec = SMALL[name]
+    inp = W.make_prefill(spec, seed=100 + len(name))
+    say("prefill parity", name, spec)
+    got = gpu_prefill(inp)
+    ref = oracle_prefill(inp)
+    check(got, ref, spec.dtype, name)
+
+
+@pytest.mark.parametrize("name", ["c2_f16_gqa_causal_2k", "c3_bf16_causal_32k", "c4_bf16_swa1024_d256"])
+def test_prefill_parity_full_size_sampled(name):
+    """Full-size workloads, launched as the benchmark launches them; oracle on sampled rows."""
+    spec = WL[name]
+    inp = W.make_prefill(spec, seed=W.WORKLOAD_SEEDS[name])
+    say("prefill full-size", name)
+    got = gpu_prefill(inp)
+    rows = sample_rows(spec, n_random=200, seed=1)
+    ref = oracle_prefill(inp, rows=rows)
+    sel = got[rows[:, 0], rows[:, 1], rows[:, 2]]
+    check(sel, ref, spec.dtype, name)
+    assert np.isfinite(got).all()
+
+
+def test_prefill_c1_full_fp32():
+    spec = WL["c1_fp32_d64"]
+    inp = W.make_prefill(spec, seed=W.WORKLOAD_SEEDS["c1_fp32_d64"])
+    say("prefill c1 full")
+    rel = check(gpu_prefill(inp), oracle_prefill(inp), "f32", "c1")
+    say("c1 normwise rel err", rel)
+
+
+def test_empty_kv_gives_zeros():
+    spec = W.PrefillSpec(1, 2, 1, 70, 0, 128, "bf16", causal=False)
+    inp = W.make_prefill(spec, seed=3)
+    say("prefill empty kv")
+    assert (gpu_prefill(inp) == 0).all()
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])
+def test_scale_sign_and_zero(scale):
+    spec = W.PrefillSpec(1, 2, 1, 150, 150, 128, "bf16", causal=True, window=60)
+    inp = W.make_prefill(spec, seed=4)
+    say("prefill scale", scale)
+    check(gpu_prefill(inp, scale=scale), oracle_prefill(inp, scale=scale), "bf16", f"scale={scale}")
+
+
+def test_gqa_equals_replicated_kv_bitwise():
+    torch = torch_cuda()
+    import flash_attention_forward_amd as F
+
+    spec = W.PrefillSpec(2, 8, 2, 300, 300, 128, "bf16", causal=True, window=100)
+    inp = W.make_prefill(spec, seed=5)
+    say("gqa vs replicated")
+    q, k, v = (W.to_torch(a, "bf16", "cuda") for a in (inp.q, inp.k, inp.v))
+    o1 = F.prefill(q, k, v, scale=spec.scale_f32, causal=True, window=100)
+    kr = k.repeat_interleave(4, dim=2).contiguous()
+    vr = v.repeat_interleave(4, dim=2).contiguous()
+    o2 = F.prefill(q, kr, vr, scale=spec.scale_f32, causal=True, window=100)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_strided_views_match_contiguous():
+    """q/k/v as slices of one packed [B, S, Hq + 2Hkv, D] tensor, o as a slice too."""
+    torch = torch_cuda()
+    import flash_attention_forward_amd as F
+
+    spec = W.PrefillSpec(1, 4, 2, 200, 200, 128, "f16", causal=True)
+    inp = W.make_prefill(spec, seed=6)
+    say("strided views")
+    q, k, v = (W.to_torch(a, "f16", "cuda") for a in (inp.q, inp.k, inp.v))
+    packed = torch.cat([q, k, v], dim=2)
+    qs, ks, vs = packed[:, :, :4], packed[:, :, 4:6], packed[:, :, 6:8]
+    obuf = torch.zeros(1, 200, 6, 128, dtype=torch.float16, device="cuda")
+    F.attn_prefill_fwd(qs, ks, vs, obuf[:, :, 1:5], spec.scale_f32, True)
+    o = F.prefill(q, k, v, scale=spec.scale_f32, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(obuf[:, :, 1:5], o)
+    assert (obuf[:, :, 0] == 0).all() and (obuf[:, :, 5] == 0).all()
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 37), (False, 0)])
+def test_needles_bit_exact(causal, window):
+    """Key j* aligned with query i (score gap >> 150 in log2 units): o_i == v[j*] bit-exactly
+    when j* is visible; when it is masked, o_i is bit-identical to the run without the needle.
+    j* sweeps tile (64), wave (32) and window edges."""
+    torch = torch_cuda()
+    import flash_attention_forward_amd as F
+
+    S, D = 260, 128
+    spec = W.PrefillSpec(1, 1, 1, S, S, D, "bf16", causal=causal, window=window)
+    inp = W.make_prefill(spec, seed=7)
+    q64 = W.as_f64(inp.q, "bf16")
+    q, k, v = (W.to_torch(a, "bf16", "cuda") for a in (inp.q, inp.k, inp.v))
+    base = F.prefill(q, k, v, scale=spec.scale_f32, causal=causal, window=window)
+    say("needles", causal, window)
+    for i in (0, 31, 32, 63, 64, 100, 127, 128, 200, 259):
+        qpos = i
+        cand = {0, 1, 31, 32, 63, 64, 65, 127, 128, qpos - 1, qpos, qpos + 1, qpos - window + 1, qpos - window,
+                S - 1}
+        for j in sorted(c for c in cand if 0 <= c < S):
+            kk = inp.k.copy()
+            needle = 300.0 * q64[0, i, 0] / (q64[0, i, 0] @ q64[0, i, 0]) / spec.scale_f32
+            kk[0, j, 0] = W.round_to(needle.astype(np.float32), "bf16")
+            o = F.prefill(q, W.to_torch(kk, "bf16", "cuda"), v, scale=spec.scale_f32, causal=causal, window=window)
+            visible = (not causal or j <= qpos) and (window <= 0 or j >= qpos - window + 1)
+            if visible:
+                assert torch.equal(o[0, i, 0].view(torch.int16), v[0, j, 0].view(torch.int16)), (i, j)
+            else:
+                assert torch.equal(o[0, i, 0].view(torch.int16), base[0, i, 0].view(torch.int16)), (i, j)
+
+
+def test_garbage_outside_kv_never_leaks():
+    """NaN in memory past seqlen_kv, and in keys before the first query's window, changes nothing."""
+    torch = torch_cuda()
+    import flash_attention_forward_amd as F
+
+    Sq, Skv, w = 130, 300, 90
+    spec = W.PrefillSpec(1, 2, 1, Sq, Skv, 128, "bf16", causal=True, window=w)
+    inp = W.make_prefill(spec, seed=8)
+    q, k, v = (W.to_torch(a, "bf16", "cuda") for a in (inp.q, inp.k, inp.v))
+    say("garbage outside kv")
+    ref = F.prefill(q, k, v, scale=spec.scale_f32, causal=True, window=w)
+    kbig = torch.full((1, Skv + 70, 1, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vbig = kbig.clone()
+    kbig[:, :Skv] = k
+    vbig[:, :Skv] = v
+    first_visible = (Skv - Sq) - w + 1  # no query sees keys below this
+    kbig[:, :first_visible] = float("nan")
+    vbig[:, :first_visible] = float("nan")
+    o = F.prefill(q, kbig[:, :Skv], vbig[:, :Skv], scale=spec.scale_f32, causal=True, window=w)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
+
+
+def test_constant_v_is_exact():
+    """V = c (bf16-representable) gives O = c exactly: P is summed as rounded."""
+    torch = torch_cuda()
+    import flash_attention_forward_amd as F
+
+    spec = W.PrefillSpec(1, 4, 2, 333, 333, 128, "bf16", causal=True, window=200)
+    inp = W.make_prefill(spec, seed=9)
+    q, k = (W.to_torch(a, "bf16", "cuda") for a in (inp.q, inp.k))
+    v = torch.full_like(k, -1.375)
+    say("constant v")
+    o = F.prefill(q, k, v, scale=spec.scale_f32, causal=True, window=200)
+    torch.cuda.synchronize()
+    assert (o == -1.375).all()
+
+
+def test_repeated_runs_bit_identical():
+    """The same launch repeated gives bit-identical outputs (no scheduling-dependent races)."""
+    torch = torch_cuda()
+    import flash_attention_forward_amd as F
+
+    spec = W.shrink(WL["c3_bf16_causal_32k"], seqlen_q=4096, seqlen_kv=4096)
+    inp = W.make_prefill(spec, seed=10)
+    q, k, v = (W.to_torch(a, "bf16", "cuda") for a in (inp.q, inp.k, inp.v))
+    say("repeated runs")
+    ref = F.prefill(q, k, v, scale=spec.scale_f32, causal=True)
+    for _ in range(30):
+        o = F.prefill(q, k, v, scale=spec.scale_f32, causal=True)
+        assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
