@@ -1,0 +1,305 @@
+"""Benchmark of the flash-attention forward hot path on one MI355X.
+
+One step = one long-context causal prefill (8 q-heads over 1 kv-head, 32768
+tokens, head_dim 128, bf16, 1% of keys doubled) followed by one paged decode
+(32 sequences, 32 q-heads over 8 kv-heads, head_dim 128, bf16, 16-token pages,
+cache_len uniform in [1024, 32768]): attn_prefill_fwd, then attn_decode_fwd and
+attn_decode_combine, all on one stream with every input resident in HBM.
+
+Prints ONE JSON line. `value` is the prefill's effective TFLOP/s (only visible
+(q, k) pairs count, 4*head_dim FLOPs each); the decode's achieved HBM GB/s over
+the K/V bytes of tokens below cache_len is reported beside it. Kernel times
+come from HIP events recorded on the launch stream around each kernel.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --calibrate-copy     # plain 1 GiB device copy, for counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E, published
+PREFILL = "c3_bf16_causal_32k"
+DECODE = "c5_paged_decode"
+CONTEXT = "c2_f16_gqa_causal_2k"  # the 7B-shaped 2K prefill the minfer page times
+PAGES_CONTEXT_MS_PER_LAYER = 8.5   # minfer 8n page, results: 7B @2K prefill attention, on its own (NVIDIA) GPU
+
+
+def visible_pairs(spec) -> int:
+    """Visible (query, key) pairs of one (batch, q-head) under the spec's mask."""
+    off = spec.seqlen_kv - spec.seqlen_q
+    i = np.arange(spec.seqlen_q, dtype=np.int64)
+    pos = i + off
+    hi = np.minimum(spec.seqlen_kv - 1, pos) if spec.causal else np.full_like(i, spec.seqlen_kv - 1)
+    lo = np.maximum(0, pos - spec.window + 1) if spec.window > 0 else np.zeros_like(i)
+    return int(np.maximum(0, hi - lo + 1).sum())
+
+
+def prefill_flops(spec) -> float:
+    return 4.0 * spec.head_dim * visible_pairs(spec) * spec.batch * spec.n_q_heads
+
+
+def decode_kv_bytes(inp) -> int:
+    s = inp.spec
+    return int(inp.cache_len.astype(np.int64).sum()) * s.n_kv_heads * s.head_dim * 2 * 2
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "flash_attention_forward_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_key: str):
+    """HBM bytes per launch from the committed counter summary, or None if the
+    kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    e = d.get(kernel_key)
+    if not e or e.get("source_digest") != kernel_source_digest():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def calibrate_copy():
+    import torch
+
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
+
+
+def cpu_baseline(inp, seconds_target: float = 15.0):
+    """The fp64 oracle, timed on a bounded random sample of the prefill's rows."""
+    import oracle
+    from flash_attention_forward_amd import workloads as W
+
+    s = inp.spec
+    q, k, v = W.as_f64(inp.q, s.dtype), W.as_f64(inp.k, s.dtype), W.as_f64(inp.v, s.dtype)
+    rng = np.random.default_rng(0)
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+    def run(n):
+        rows = np.stack([np.zeros(n, np.int64), rng.integers(0, s.seqlen_q, n), rng.integers(0, s.n_q_heads, n)], 1)
+        t = time.perf_counter()
+        oracle.attention_rows(q, k, v, s.scale_f32, s.causal, s.window, rows)
+        dt = time.perf_counter() - t
+        pairs = (rows[:, 1] + 1 + (s.seqlen_kv - s.seqlen_q)).clip(0, s.seqlen_kv).sum()  # causal rows, no window
+        return n, dt, 4.0 * s.head_dim * float(pairs)
+
+    n, dt, fl = run(256)
+    n2 = int(min(200000, max(256, n * seconds_target / max(dt, 1e-3))))
+    n, dt, fl = run(n2)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} random query rows of the 32768-token causal prefill (all keys each row sees), "
+                      f"{dt:.1f} s wall, fp64, OpenMP over rows"}
+
+
+def cpu_baseline_decode(inp):
+    import oracle
+    from flash_attention_forward_amd import workloads as W
+
+    s = inp.spec
+    f64 = lambda a: W.as_f64(a, s.dtype)
+    order = np.argsort(inp.cache_len)
+    batches = [int(order[len(order) // 2]), int(order[-1])]
+    t = time.perf_counter()
+    oracle.decode(f64(inp.q), inp.k_pool, inp.v_pool, inp.block_table, inp.cache_len, s.scale_f32,
+                  batches=batches, to_f64=f64)
+    dt = time.perf_counter() - t
+    nbytes = int(inp.cache_len[batches].astype(np.int64).sum()) * s.n_kv_heads * s.head_dim * 2 * 2
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
+            "kind": "oracle", "sample": f"sequences {batches} of the paged decode (gather + fp64 attention), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--split-len", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    import torch
+
+    import flash_attention_forward_amd as F
+    from flash_attention_forward_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda"
+
+    def log(*a):
+        print(*a, file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- inputs (resident in HBM)
+    pspec = W.WORKLOADS[PREFILL]
+    log("generating", PREFILL)
+    pin = W.make_prefill(pspec, W.WORKLOAD_SEEDS[PREFILL])
+    q, k, v = (W.to_torch(a, pspec.dtype, dev) for a in (pin.q, pin.k, pin.v))
+    o = torch.empty_like(q)
+
+    dspec = W.WORKLOADS[DECODE]
+    log("generating", DECODE)
+    din = W.make_decode(dspec, W.WORKLOAD_SEEDS[DECODE])
+    dq = W.to_torch(din.q, dspec.dtype, dev)
+    kc = W.to_torch(din.k_pool, dspec.dtype, dev)
+    vc = W.to_torch(din.v_pool, dspec.dtype, dev)
+    cl = torch.from_numpy(din.cache_len.astype(np.int32)).to(dev)
+    bt = torch.from_numpy(din.block_table.view(np.int32)).to(dev)
+    max_len = dspec.max_pages_per_seq * dspec.page_size
+    ms = F.attn.max_splits_for(max_len, args.split_len)
+    ws = F.DecodeWorkspace(dspec.batch, dspec.s_active, dspec.n_q_heads, dspec.head_dim, ms, dev)
+    do = torch.empty_like(dq)
+
+    cspec = W.WORKLOADS[CONTEXT]
+    cin = W.make_prefill(cspec, W.WORKLOAD_SEEDS[CONTEXT])
+    cq, ck, cv = (W.to_torch(a, cspec.dtype, dev) for a in (cin.q, cin.k, cin.v))
+    co = torch.empty_like(cq)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        F.attn_prefill_fwd(q, k, v, o, pspec.scale_f32, True, 0)
+        if events is not None:
+            events[1].record(stream)
+        F.attn_decode_fwd(dq, kc, vc, cl, ws.part_o, ws.part_lse, args.split_len, ms, dspec.scale_f32, bt)
+        if events is not None:
+            events[2].record(stream)
+        F.attn_decode_combine(ws.part_o, ws.part_lse, cl, args.split_len, ms, do)
+        if events is not None:
+            events[3].record(stream)
+
+    log("warmup", args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    log("timing", args.steps, "steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pre_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    split_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    comb_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    dec_ms = split_ms + comb_ms
+
+    # 7B-shaped 2K context prefill, timed the same way (context only)
+    for _ in range(3):
+        F.attn_prefill_fwd(cq, ck, cv, co, cspec.scale_f32, True, 0)
+    cev = [[ev(), ev()] for _ in range(20)]
+    for e in cev:
+        e[0].record(stream)
+        F.attn_prefill_fwd(cq, ck, cv, co, cspec.scale_f32, True, 0)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ctx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in cev]))
+
+    flops = prefill_flops(pspec)
+    kv_bytes = decode_kv_bytes(din)
+    pre_tflops = flops / (pre_ms.mean() * 1e-3) / 1e12
+    dec_gbps = kv_bytes / (dec_ms.mean() * 1e-3) / 1e9
+    split_gbps = kv_bytes / (split_ms.mean() * 1e-3) / 1e9
+
+    line = {
+        "metric": "prefill causal TFLOP/s + decode KV GB/s, % of MI355X peak",
+        "value": round(pre_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{PREFILL} + {DECODE}",
+            "prefill": "B1 Sq=Skv=32768 Hq8 Hkv1 D128 bf16 causal, 327 K rows x2, scale 1/sqrt(128)",
+            "decode": f"B32 s_active1 Hq32 Hkv8 D128 bf16 page16, sum(cache_len)={int(din.cache_len.sum())}, "
+                      f"split_len {args.split_len}",
+            "prefill_flops": flops,
+            "decode_kv_bytes": kv_bytes,
+        },
+        "prefill_ms": round(float(pre_ms.mean()), 4),
+        "decode_us": round(float(dec_ms.mean()) * 1e3, 2),
+        "decode_split_us": round(float(split_ms.mean()) * 1e3, 2),
+        "decode_combine_us": round(float(comb_ms.mean()) * 1e3, 2),
+        "decode": {"value": round(dec_gbps, 1), "unit": "GB/s", "frac_of_peak": round(dec_gbps / PEAK_HBM_GBPS, 4)},
+        "roofline": {
+            "kernel": "prefill_mfma<bf16, D128, causal>",
+            "bound": "mfma",
+            "achieved": round(pre_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_from_profiles("prefill_c3"),
+        },
+        "roofline_decode": {
+            "kernel": "decode_split<bf16, D128>",
+            "bound": "hbm",
+            "achieved": round(split_gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(split_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": traffic_from_profiles("decode_c5"),
+        },
+        "context": {
+            "workload": CONTEXT,
+            "ms_per_layer": round(ctx_ms, 4),
+            "tflops": round(prefill_flops(cspec) / (ctx_ms * 1e-3) / 1e12, 2),
+            "pages_ms_per_layer": PAGES_CONTEXT_MS_PER_LAYER,
+            "pages_hardware": "unnamed NVIDIA GPU (minfer 8n page); context only",
+        },
+        "kernel_source_digest": kernel_source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(pin)
+        line["cpu_baseline_decode"] = cpu_baseline_decode(din)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
