@@ -65,16 +65,16 @@ def kernel_source_digest() -> str:
 
 
 def traffic_from_profiles(kernel_key: str):
-    """HBM bytes per launch from the committed counter summary, or None if the
-    kernels changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch from the committed counter summary (profiles/hbm_traffic.md),
+    or None if the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
     if not os.path.exists(path):
         return None
-    d = json.load(open(path))
-    e = d.get(kernel_key)
-    if not e or e.get("source_digest") != kernel_source_digest():
-        return None
-    return e.get("hbm_bytes_per_launch")
+    for line in open(path):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 3 and cells[0] == kernel_key:
+            return int(cells[2]) if cells[1] == kernel_source_digest() else None
+    return None
 
 
 def calibrate_copy():
