@@ -104,11 +104,12 @@ int attn_decode_fwd(const void* q, attn_strides q_st, const void* k_cache, const
     if (block_table) {
         if (page_size <= 0 || max_pages_per_seq <= 0 || split_len % page_size != 0) return ATTN_ERR_INVALID;
         if ((int64_t)max_splits * split_len < (int64_t)max_pages_per_seq * page_size) return ATTN_ERR_INVALID;
+        if (split_len / page_size > attn::kDecodeMaxSplitPages) return ATTN_ERR_UNSUPPORTED;
     }
     if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
     if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
     if ((int64_t)(n_q_heads / n_kv_heads) * s_active > 16) return ATTN_ERR_UNSUPPORTED;
-    if (max_splits > 65535 * 32 || n_kv_heads > 65535 || batch > 65535) return ATTN_ERR_UNSUPPORTED;
+    if (max_splits > 65535 || batch > 65535) return ATTN_ERR_UNSUPPORTED;
     const int eb = elem_bytes(dtype);
     if (!q || !k_cache || !v_cache || !cache_len || !part_o || !part_lse) return ATTN_ERR_INVALID;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(part_o)) return ATTN_ERR_INVALID;
@@ -123,6 +124,9 @@ int attn_decode_fwd(const void* q, attn_strides q_st, const void* k_cache, const
     p.group = n_q_heads / n_kv_heads;
     p.max_pages_per_seq = block_table ? max_pages_per_seq : 0;
     p.page_size = block_table ? page_size : 1;
+    p.page_shift = -1;
+    for (int sh = 0; sh < 31; ++sh)
+        if ((1 << sh) == p.page_size) p.page_shift = sh;
     p.window = window > 0 ? window : 0;
     p.split_len = split_len; p.max_splits = max_splits;
     p.c = scaled_log2e(scale);

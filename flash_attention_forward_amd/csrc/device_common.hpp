@@ -53,6 +53,31 @@ __device__ __forceinline__ float f16bits_to_f32(uint16_t b) {
     }
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two f32 -> one dword of two 16-bit floats (round to nearest even), low half first.
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack2_16(float a, float b) {
+    const f32x2 v = {a, b};
+    if constexpr (BF16) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    } else {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+    }
+}
+
+// acc + x.lo * y.lo + x.hi * y.hi with 16-bit float pairs (one v_dot2c_f32_*).
+template <bool BF16>
+__device__ __forceinline__ float dot2_16(uint32_t x, uint32_t y, float acc) {
+    if constexpr (BF16) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y), acc, false);
+    } else {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, y), acc, false);
+    }
+}
+
 // 32x32x16 MFMA with f32 accumulation; operands are 8 16-bit values per lane.
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma32x32x16(s16x8 a, s16x8 b, f32x16 c) {

@@ -49,6 +49,9 @@ struct CombineParams {
     int batch, s_active, n_q_heads, split_len, max_splits;
 };
 
+// Largest number of pages one decode split may span (split_len / page_size).
+constexpr int kDecodeMaxSplitPages = 256;
+
 enum MaskMode { kMaskNone = 0, kMaskCausal = 1, kMaskCausalWindow = 2 };
 enum DType { kF32 = 0, kF16 = 1, kBF16 = 2 };
 

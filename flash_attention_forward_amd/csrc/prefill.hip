@@ -37,14 +37,20 @@ constexpr int PF_THREADS = 256;
 constexpr int PF_KPAD = 8;   // K row padding (elements): 16 B keeps 16-lane b128 reads conflict-free
 constexpr int PF_VPAD = 32;  // V row padding (elements): rows land 64 B apart for the transpose reads
 
+template <bool B>
+struct BoolC {
+    static constexpr bool value = B;
+};
+
 template <bool BF16, int D, int MASK>
 __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(PrefillParams p) {
     constexpr int KSTR = D + PF_KPAD;
     constexpr int VSTR = D + PF_VPAD;
     constexpr int CH = PF_BN * D / 8 / PF_THREADS;  // 16-byte chunks per thread per tensor
     constexpr int NDT = D / 32;                      // 32-wide d tiles of O^T
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[PF_BN * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[PF_BN * VSTR];
+    // Two K/V tile buffers: tile j+1 is written while tile j is read, one barrier per tile.
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][PF_BN * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][PF_BN * VSTR];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -110,37 +116,29 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
             }
         }
     };
-    auto lstore = [&]() {
+    auto lstore = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             const int c = tid + i * PF_THREADS;
             const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-            *(uint4*)&Ks[row * KSTR + col] = kreg[i];
-            *(uint4*)&Vs[row * VSTR + col] = vreg[i];
+            *(uint4*)&Ks[buf][row * KSTR + col] = kreg[i];
+            *(uint4*)&Vs[buf][row * VSTR + col] = vreg[i];
         }
     };
 
+    // Running max in scaled log2 units. It only moves when a row's tile max
+    // exceeds it by more than kLazyRescale, so O and l are rescaled rarely;
+    // in between, probabilities are at most 2^kLazyRescale (the result is the
+    // same softmax for any m >= the true running max minus that margin).
+    constexpr float kLazyRescale = 8.0f;
     float m_i = kMaxInit, l_i = 0.f;
     f32x16 o[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
+    const uint32_t one2 = BF16 ? 0x3F803F80u : 0x3C003C00u;  // two 16-bit 1.0s for the row-sum dot2
 
-    if (j_begin < j_end) gload(j_begin);
-    for (int j = j_begin; j < j_end; ++j) {
-        __syncthreads();
-        lstore();
-        __syncthreads();
-        if (j + 1 < j_end) gload(j + 1);
-
-        const int kv0 = j * PF_BN;
-        bool empty = !wave_live;
-        if (MASK >= kMaskCausal) empty |= kv0 > wq1 + p.off;
-        if (MASK == kMaskCausalWindow) empty |= kv0 + PF_BN - 1 < wq0 + p.off - p.window + 1;
-        if (empty) continue;
-        bool full = kv0 + PF_BN <= p.seqlen_kv;
-        if (MASK >= kMaskCausal) full &= kv0 + PF_BN - 1 <= wq0 + p.off;
-        if (MASK == kMaskCausalWindow) full &= kv0 >= wq1 + p.off - p.window + 1;
-
+    auto tile = [&](const uint16_t* Kt, const uint16_t* Vt, int kv0, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
         // S^T tile: two 32-key blocks x 32 queries; lane holds keys
         // 32t + 8(r/4) + 4hf + r%4 of its query row in register r.
         f32x16 sacc[2] = {f32x16{}, f32x16{}};
@@ -148,18 +146,11 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
         for (int s = 0; s < D / 16; ++s) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const s16x8 a = *(const s16x8*)&Ks[(32 * t + l32) * KSTR + 16 * s + 8 * hf];
+                const s16x8 a = *(const s16x8*)&Kt[(32 * t + l32) * KSTR + 16 * s + 8 * hf];
                 sacc[t] = mfma32x32x16<BF16>(a, qf[s], sacc[t]);
             }
         }
-
-        float mx = kMaskedScore;
-        if (full) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
-        } else {
+        if constexpr (!FULL) {
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -169,13 +160,25 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
                     if (MASK >= kMaskCausal) keep &= key <= my_pos;
                     if (MASK == kMaskCausalWindow) keep &= key >= my_pos - p.window + 1;
                     sacc[t][r] = keep ? sacc[t][r] : kMaskedScore;
-                    mx = fmaxf(mx, sacc[t][r]);
                 }
         }
+        float mx = kMaskedScore;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
         mx = max_with_other_half(mx);
-        const float m_new = fmaxf(m_i, mx * p.c);
-        const float alpha = fast_exp2(m_i - m_new);
-        m_i = m_new;
+        const float m_cand = mx * p.c;
+        const bool grow = m_cand > m_i + kLazyRescale;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float m_new = grow ? m_cand : m_i;
+            const float alpha = fast_exp2(m_i - m_new);
+            m_i = m_new;
+            l_i *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        }
+        const float neg_m = -m_i;
 
         // P in 16-bit, packed as the B operand of O^T += V^T P^T: chunk u
         // covers keys 16u..16u+15 of the tile; slot j of lane half hf is key
@@ -183,19 +186,24 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
         s16x8 pb[4];
         float psum = 0.f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 4; ++u) {
+            uint32_t pk[4];
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const float s = sacc[u >> 1][8 * (u & 1) + jj];
-                float pv = fast_exp2(fmaf(s, p.c, -m_new));
-                if (!full) pv = (s == kMaskedScore) ? 0.f : pv;
-                const uint16_t pr = f32_to_16<BF16>(pv);
-                psum += f16bits_to_f32<BF16>(pr);
-                pb[u][jj] = (short)pr;
+            for (int jj = 0; jj < 8; jj += 2) {
+                const float s0 = sacc[u >> 1][8 * (u & 1) + jj];
+                const float s1 = sacc[u >> 1][8 * (u & 1) + jj + 1];
+                float p0 = fast_exp2(fmaf(s0, p.c, neg_m));
+                float p1 = fast_exp2(fmaf(s1, p.c, neg_m));
+                if constexpr (!FULL) {
+                    p0 = s0 == kMaskedScore ? 0.f : p0;
+                    p1 = s1 == kMaskedScore ? 0.f : p1;
+                }
+                pk[jj / 2] = pack2_16<BF16>(p0, p1);
+                psum = dot2_16<BF16>(pk[jj / 2], one2, psum);  // sum of the rounded P
             }
-        l_i = l_i * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+            pb[u] = __builtin_bit_cast(s16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+        }
+        l_i += psum;
 
         // O^T[d, q] += V^T[d, keys] P^T[keys, q]. A operand via transpose
         // reads: lane r16 of group g points at row 16u + 4hf + r16/4 (and +8),
@@ -207,11 +215,35 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
                 const int col = 32 * dt + 16 * (g & 1) + 4 * (r16 & 3);
-                const s16x4 lo = lds_read_tr16(&Vs[row0 * VSTR + col]);
-                const s16x4 hi4 = lds_read_tr16(&Vs[(row0 + 8) * VSTR + col]);
+                const s16x4 lo = lds_read_tr16(&Vt[row0 * VSTR + col]);
+                const s16x4 hi4 = lds_read_tr16(&Vt[(row0 + 8) * VSTR + col]);
                 o[dt] = mfma32x32x16<BF16>(concat4(lo, hi4), pb[u], o[dt]);
             }
         }
+    };
+
+    if (j_begin < j_end) {
+        gload(j_begin);
+        lstore(0);
+        __syncthreads();
+        if (j_begin + 1 < j_end) gload(j_begin + 1);
+    }
+    for (int j = j_begin; j < j_end; ++j) {
+        const int buf = (j - j_begin) & 1;
+        const int kv0 = j * PF_BN;
+        bool empty = !wave_live;
+        if (MASK >= kMaskCausal) empty |= kv0 > wq1 + p.off;
+        if (MASK == kMaskCausalWindow) empty |= kv0 + PF_BN - 1 < wq0 + p.off - p.window + 1;
+        if (!empty) {
+            bool full = kv0 + PF_BN <= p.seqlen_kv;
+            if (MASK >= kMaskCausal) full &= kv0 + PF_BN - 1 <= wq0 + p.off;
+            if (MASK == kMaskCausalWindow) full &= kv0 >= wq1 + p.off - p.window + 1;
+            if (full) tile(Ks[buf], Vs[buf], kv0, BoolC<true>{});
+            else tile(Ks[buf], Vs[buf], kv0, BoolC<false>{});
+        }
+        if (j + 1 < j_end) lstore(buf ^ 1);  // the other buffer's tile (j-1) is done: barrier of the last step
+        __syncthreads();
+        if (j + 2 < j_end) gload(j + 2);
     }
 
     // Epilogue: O * (1/l); rows that saw no key are written as zeros.
@@ -226,10 +258,8 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
             for (int rq = 0; rq < 4; ++rq) {
                 const int d = 32 * dt + 8 * rq + 4 * hf;
                 uint2 pk;
-                pk.x = (uint32_t)f32_to_16<BF16>(o[dt][4 * rq + 0] * inv) |
-                       ((uint32_t)f32_to_16<BF16>(o[dt][4 * rq + 1] * inv) << 16);
-                pk.y = (uint32_t)f32_to_16<BF16>(o[dt][4 * rq + 2] * inv) |
-                       ((uint32_t)f32_to_16<BF16>(o[dt][4 * rq + 3] * inv) << 16);
+                pk.x = pack2_16<BF16>(o[dt][4 * rq + 0] * inv, o[dt][4 * rq + 1] * inv);
+                pk.y = pack2_16<BF16>(o[dt][4 * rq + 2] * inv, o[dt][4 * rq + 3] * inv);
                 *(uint2*)(orow + d) = pk;
             }
     }

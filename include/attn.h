@@ -127,7 +127,8 @@ int attn_prefill_fwd(const void* q, attn_strides q_st, const void* k, attn_strid
  *           not written.
  *   split_len must be a positive multiple of 16 (and of page_size when
  *   paged); max_splits * split_len must cover the longest cache
- *   (>= max_pages_per_seq * page_size when paged).
+ *   (>= max_pages_per_seq * page_size when paged); a split may span at most
+ *   256 pages (split_len / page_size <= 256, else ATTN_ERR_UNSUPPORTED).
  * Requires head_dim in {64, 128, 256}, dtype f16 or bf16, and
  * (n_q_heads / n_kv_heads) * s_active <= 16.
  */
