@@ -31,7 +31,14 @@ uint32_t q_flip_mask(float scale, int dtype) {
     return dtype == ATTN_F32 ? 0x80000000u : 0x80008000u;
 }
 
-float scaled_log2e(float scale) { return (float)(std::fabs((double)scale) * 1.4426950408889634); }
+// |scale| * log2(e), kept >= 1e-30 so that the float32-min stand-in of a
+// masked score always maps to probability exactly 0. A zero scale becomes
+// 1e-30: every visible score is then a tiny number whose exp2 rounds to 1, the
+// same uniform weights.
+float scaled_log2e(float scale) {
+    const double c = std::fabs((double)scale) * 1.4426950408889634;
+    return (float)(c < 1e-30 ? 1e-30 : c);
+}
 
 int status_of(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
 
@@ -66,6 +73,9 @@ int attn_prefill_fwd(const void* q, attn_strides q_st, const void* k, attn_strid
     if (seqlen_kv > 0 && (!k || !v || !aligned16(k) || !aligned16(v))) return ATTN_ERR_INVALID;
     if (!strides_ok(q_st, eb) || !strides_ok(k_st, eb) || !strides_ok(v_st, eb) || !strides_ok(o_st, eb))
         return ATTN_ERR_INVALID;
+    // lane offsets inside one 64-row K/V tile are kept in 32 bits
+    if (k_st.seq * 64 + head_dim >= ((int64_t)1 << 31) || v_st.seq * 64 + head_dim >= ((int64_t)1 << 31))
+        return ATTN_ERR_UNSUPPORTED;
     const int64_t tiles = (seqlen_q + 63) / 64;
     if (tiles * batch * n_q_heads >= (int64_t)1 << 31) return ATTN_ERR_UNSUPPORTED;
 

@@ -23,6 +23,17 @@ constexpr float kMaskedScore = -3.4028234663852886e38f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Instruction-scheduling hint for the device compiler: the next group of the
+// current scheduling region holds N instructions of class MASK (0x002 VALU,
+// 0x008 MFMA, 0x100 LDS read). It only shapes the order of independent
+// instructions; the host pass of the compiler never sees it.
+template <int MASK, int N>
+__device__ __forceinline__ void sched_group() {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
+#endif
+}
+
 // Value of lane (l ^ 32) for every lane l, with one v_permlane32_swap.
 __device__ __forceinline__ float max_with_other_half(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -31,26 +31,41 @@
 
 namespace attn {
 
-constexpr int PF_BM = 128;  // query rows per workgroup
-constexpr int PF_BN = 64;   // keys per tile
-constexpr int PF_THREADS = 256;
-constexpr int PF_KPAD = 8;   // K row padding (elements): 16 B keeps 16-lane b128 reads conflict-free
-constexpr int PF_VPAD = 32;  // V row padding (elements): rows land 64 B apart for the transpose reads
-
 template <bool B>
 struct BoolC {
     static constexpr bool value = B;
 };
 
+constexpr int PF_BM = 128;  // query rows per workgroup
+constexpr int PF_BN = 64;   // keys per tile
+constexpr int PF_THREADS = 256;
+
+// LDS layout of the K and V tiles: row-major, 16-byte chunk c of row r stored
+// at chunk c ^ f(r). Tiles are filled with direct-to-LDS loads (each 1 KB load
+// covers whole rows), so bank conflicts are avoided by swizzling, not padding.
+// K: a 16-lane group of a b128 read hits rows r..r+15 at one chunk.
+template <int D>
+__device__ __forceinline__ int pf_kswz(int row) {
+    return D == 64 ? ((row >> 1) & 7) : (row & 15);
+}
+// V: 32 lanes of a transpose read hit rows R..R+3 (R % 4 == 0) at four adjacent chunks.
+template <int D>
+__device__ __forceinline__ int pf_vswz(int row) {
+    return D == 64 ? 4 * ((row >> 1) & 1) : 4 * (row & 3);
+}
+
 template <bool BF16, int D, int MASK>
 __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(PrefillParams p) {
-    constexpr int KSTR = D + PF_KPAD;
-    constexpr int VSTR = D + PF_VPAD;
-    constexpr int CH = PF_BN * D / 8 / PF_THREADS;  // 16-byte chunks per thread per tensor
-    constexpr int NDT = D / 32;                      // 32-wide d tiles of O^T
-    // Two K/V tile buffers: tile j+1 is written while tile j is read, one barrier per tile.
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][PF_BN * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][PF_BN * VSTR];
+    constexpr int CPR = D / 8;              // 16-byte chunks per row
+    constexpr int TILE = PF_BN * D;         // elements of one K or V tile
+    constexpr int LPW = TILE / 512 / 4;     // 1 KB direct loads per wave per tile
+    constexpr int NDT = D / 32;             // 32-wide d tiles of O^T
+    // Two K and two V tiles, separate objects so waits on one buffer's refill
+    // never cover reads of the other.
+    __shared__ __attribute__((aligned(16))) uint16_t Ks0[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks1[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs0[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs1[TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -99,32 +114,48 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
 
     const uint16_t* kbase = (const uint16_t*)p.k + (int64_t)b * p.ks.batch + (int64_t)hk * p.ks.head;
     const uint16_t* vbase = (const uint16_t*)p.v + (int64_t)b * p.vs.batch + (int64_t)hk * p.vs.head;
-    uint4 kreg[CH], vreg[CH];
-    auto gload = [&](int j) {
-        const int kv0 = j * PF_BN;
+    // Tile rows outside [kv_lo, seqlen_kv) are loaded as copies of the nearest
+    // valid row: they are masked out (probability exactly 0) and no memory
+    // outside the visible key range is touched. Every load is unconditional.
+    const int key_min = kv_lo, key_max = p.seqlen_kv - 1;
+    // Lane part of each direct load's source offset (row within the tile and
+    // swizzled chunk), computed once: interior tiles then only add a uniform
+    // tile base. Edge tiles clamp row by row.
+    int koff[LPW], voff[LPW];
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + i * PF_THREADS;
-            const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-            const int key = kv0 + row;
-            kreg[i] = make_uint4(0, 0, 0, 0);
-            vreg[i] = make_uint4(0, 0, 0, 0);
-            // rows outside [kv_lo, seqlen_kv) are never visible to this tile: zero them
-            if (key < p.seqlen_kv && key >= kv_lo) {
-                kreg[i] = *(const uint4*)(kbase + (int64_t)key * p.ks.seq + col);
-                vreg[i] = *(const uint4*)(vbase + (int64_t)key * p.vs.seq + col);
+    for (int ii = 0; ii < LPW; ++ii) {
+        const int slot = 64 * (w * LPW + ii) + lane;
+        const int row = slot / CPR, cs = slot % CPR;
+        koff[ii] = row * (int)p.ks.seq + 8 * (cs ^ pf_kswz<D>(row));
+        voff[ii] = row * (int)p.vs.seq + 8 * (cs ^ pf_vswz<D>(row));
+    }
+    // (Two plain lambdas rather than one generic one: a generic lambda that
+    // captures these arrays keeps the compiler's host pass from emitting the
+    // kernel's launch stub.)
+    auto load_tile_impl = [&](uint16_t* dst, const uint16_t* base, int64_t seq, int j, const int* off, bool is_k) {
+        const int kv0 = j * PF_BN;
+        if (kv0 >= key_min && kv0 + PF_BN - 1 <= key_max) {
+            const uint16_t* tbase = base + (int64_t)kv0 * seq;
+#pragma unroll
+            for (int ii = 0; ii < LPW; ++ii)
+                __builtin_amdgcn_global_load_lds(tbase + off[ii],
+                                                 (__attribute__((address_space(3))) void*)(dst + 512 * (w * LPW + ii)),
+                                                 16, 0, 0);
+        } else {
+#pragma unroll
+            for (int ii = 0; ii < LPW; ++ii) {
+                const int i = w * LPW + ii;
+                const int slot = 64 * i + lane;
+                const int row = slot / CPR, cs = slot % CPR;
+                const int key = min(max(kv0 + row, key_min), key_max);
+                const int c = cs ^ (is_k ? pf_kswz<D>(row) : pf_vswz<D>(row));
+                __builtin_amdgcn_global_load_lds(base + (int64_t)key * seq + 8 * c,
+                                                 (__attribute__((address_space(3))) void*)(dst + 512 * i), 16, 0, 0);
             }
         }
     };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + i * PF_THREADS;
-            const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-            *(uint4*)&Ks[buf][row * KSTR + col] = kreg[i];
-            *(uint4*)&Vs[buf][row * VSTR + col] = vreg[i];
-        }
-    };
+    auto load_k_tile = [&](uint16_t* dst, int j) { load_tile_impl(dst, kbase, p.ks.seq, j, koff, true); };
+    auto load_v_tile = [&](uint16_t* dst, int j) { load_tile_impl(dst, vbase, p.vs.seq, j, voff, false); };
 
     // Running max in scaled log2 units. It only moves when a row's tile max
     // exceeds it by more than kLazyRescale, so O and l are rescaled rarely;
@@ -137,37 +168,83 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
     for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
     const uint32_t one2 = BF16 ? 0x3F803F80u : 0x3C003C00u;  // two 16-bit 1.0s for the row-sum dot2
 
-    auto tile = [&](const uint16_t* Kt, const uint16_t* Vt, int kv0, auto full_tag) {
-        constexpr bool FULL = decltype(full_tag)::value;
-        // S^T tile: two 32-key blocks x 32 queries; lane holds keys
-        // 32t + 8(r/4) + 4hf + r%4 of its query row in register r.
-        f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    auto tile_empty = [&](int j) {
+        const int kv0 = j * PF_BN;
+        bool e = !wave_live || j >= j_end;
+        if (MASK >= kMaskCausal) e |= kv0 > wq1 + p.off;
+        if (MASK == kMaskCausalWindow) e |= kv0 + PF_BN - 1 < wq0 + p.off - p.window + 1;
+        return e;
+    };
+    auto tile_full = [&](int j) {
+        const int kv0 = j * PF_BN;
+        bool f = kv0 + PF_BN <= p.seqlen_kv;
+        if (MASK >= kMaskCausal) f &= kv0 + PF_BN - 1 <= wq0 + p.off;
+        if (MASK == kMaskCausalWindow) f &= kv0 >= wq1 + p.off - p.window + 1;
+        return f;
+    };
+
+    // S^T: two 32-key blocks x 32 queries; lane holds keys
+    // 32t + 8(r/4) + 4hf + r%4 of its query row in register r of block t.
+    auto qk_half = [&](f32x16& sacc, const uint16_t* Kt, int t) {
+        sacc = f32x16{};
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const s16x8 a = *(const s16x8*)&Kt[(32 * t + l32) * KSTR + 16 * s + 8 * hf];
-                sacc[t] = mfma32x32x16<BF16>(a, qf[s], sacc[t]);
-            }
+            const int row = 32 * t + l32;
+            const s16x8 a = *(const s16x8*)&Kt[row * D + 8 * ((2 * s + hf) ^ pf_kswz<D>(row))];
+            sacc = mfma32x32x16<BF16>(a, qf[s], sacc);
         }
-        if constexpr (!FULL) {
+    };
+    auto mask_half = [&](f32x16& sacc, int kv0, int t) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
-                    bool keep = key < p.seqlen_kv;
-                    if (MASK >= kMaskCausal) keep &= key <= my_pos;
-                    if (MASK == kMaskCausalWindow) keep &= key >= my_pos - p.window + 1;
-                    sacc[t][r] = keep ? sacc[t][r] : kMaskedScore;
-                }
+        for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
+            bool keep = key < p.seqlen_kv;
+            if (MASK >= kMaskCausal) keep &= key <= my_pos;
+            if (MASK == kMaskCausalWindow) keep &= key >= my_pos - p.window + 1;
+            sacc[r] = keep ? sacc[r] : kMaskedScore;
         }
+    };
+    auto max_half = [&](const f32x16& sacc) {
         float mx = kMaskedScore;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+        return mx;
+    };
+    // P for one 32-key block, packed as B operands of O^T += V^T P^T: chunk
+    // u (keys 16u..16u+15) takes registers 8(u%2)..8(u%2)+7 of block u/2; slot
+    // j of lane half hf is key 16u + 8(j/4) + 4hf + j%4. Masked scores
+    // (float32 min) give exactly 0: the host keeps p.c >= 1e-30.
+    auto softmax_half = [&](const f32x16& sacc, s16x8& pb0, s16x8& pb1) {
+        const float neg_m = -m_i;
+        float psum = 0.f;
+        uint32_t pk[8];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
-        mx = max_with_other_half(mx);
+        for (int jj = 0; jj < 16; jj += 2) {
+            const float p0 = fast_exp2(fmaf(sacc[jj], p.c, neg_m));
+            const float p1 = fast_exp2(fmaf(sacc[jj + 1], p.c, neg_m));
+            pk[jj / 2] = pack2_16<BF16>(p0, p1);
+            psum = dot2_16<BF16>(pk[jj / 2], one2, psum);  // sum of the rounded P
+        }
+        pb0 = __builtin_bit_cast(s16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+        pb1 = __builtin_bit_cast(s16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
+        return psum;
+    };
+    // O^T[d, q] += V^T[d, keys] P^T[keys, q] for key chunk u. A operand via
+    // transpose reads: lane r16 of group g points at row 16u + 4hf + r16/4
+    // (and +8), column 32dt + 16(g%2) + 4(r16%4), and receives column
+    // 32dt + 16(g%2) + r16 of four consecutive key rows.
+    auto pv_chunk = [&](const s16x8& pb, const uint16_t* Vt, int u) {
+        const int r0 = 16 * u + 4 * hf + (r16 >> 2), r1 = r0 + 8;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int c = 4 * dt + 2 * (g & 1) + ((r16 & 3) >> 1), e = 4 * (r16 & 1);
+            const s16x4 lo = lds_read_tr16(&Vt[r0 * D + 8 * (c ^ pf_vswz<D>(r0)) + e]);
+            const s16x4 hi4 = lds_read_tr16(&Vt[r1 * D + 8 * (c ^ pf_vswz<D>(r1)) + e]);
+            o[dt] = mfma32x32x16<BF16>(concat4(lo, hi4), pb, o[dt]);
+        }
+    };
+    // Move m (and rescale O and l) for rows whose tile max passed m + margin.
+    auto rescale = [&](float mx) {
         const float m_cand = mx * p.c;
         const bool grow = m_cand > m_i + kLazyRescale;
         if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -177,73 +254,75 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
             l_i *= alpha;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+            return true;
         }
-        const float neg_m = -m_i;
-
-        // P in 16-bit, packed as the B operand of O^T += V^T P^T: chunk u
-        // covers keys 16u..16u+15 of the tile; slot j of lane half hf is key
-        // 16u + 8(j/4) + 4hf + j%4, i.e. register 8(u%2) + j of block u/2.
-        s16x8 pb[4];
-        float psum = 0.f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            uint32_t pk[4];
-#pragma unroll
-            for (int jj = 0; jj < 8; jj += 2) {
-                const float s0 = sacc[u >> 1][8 * (u & 1) + jj];
-                const float s1 = sacc[u >> 1][8 * (u & 1) + jj + 1];
-                float p0 = fast_exp2(fmaf(s0, p.c, neg_m));
-                float p1 = fast_exp2(fmaf(s1, p.c, neg_m));
-                if constexpr (!FULL) {
-                    p0 = s0 == kMaskedScore ? 0.f : p0;
-                    p1 = s1 == kMaskedScore ? 0.f : p1;
-                }
-                pk[jj / 2] = pack2_16<BF16>(p0, p1);
-                psum = dot2_16<BF16>(pk[jj / 2], one2, psum);  // sum of the rounded P
-            }
-            pb[u] = __builtin_bit_cast(s16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-        }
-        l_i += psum;
-
-        // O^T[d, q] += V^T[d, keys] P^T[keys, q]. A operand via transpose
-        // reads: lane r16 of group g points at row 16u + 4hf + r16/4 (and +8),
-        // column 32dt + 16(g%2) + 4(r16%4), and receives column 32dt + 16(g%2)
-        // + r16 of four consecutive key rows.
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int row0 = 16 * u + 4 * hf + (r16 >> 2);
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const int col = 32 * dt + 16 * (g & 1) + 4 * (r16 & 3);
-                const s16x4 lo = lds_read_tr16(&Vt[row0 * VSTR + col]);
-                const s16x4 hi4 = lds_read_tr16(&Vt[(row0 + 8) * VSTR + col]);
-                o[dt] = mfma32x32x16<BF16>(concat4(lo, hi4), pb[u], o[dt]);
-            }
-        }
+        return false;
     };
 
-    if (j_begin < j_end) {
-        gload(j_begin);
-        lstore(0);
-        __syncthreads();
-        if (j_begin + 1 < j_end) gload(j_begin + 1);
-    }
-    for (int j = j_begin; j < j_end; ++j) {
-        const int buf = (j - j_begin) & 1;
-        const int kv0 = j * PF_BN;
-        bool empty = !wave_live;
-        if (MASK >= kMaskCausal) empty |= kv0 > wq1 + p.off;
-        if (MASK == kMaskCausalWindow) empty |= kv0 + PF_BN - 1 < wq0 + p.off - p.window + 1;
-        if (!empty) {
-            bool full = kv0 + PF_BN <= p.seqlen_kv;
-            if (MASK >= kMaskCausal) full &= kv0 + PF_BN - 1 <= wq0 + p.off;
-            if (MASK == kMaskCausalWindow) full &= kv0 >= wq1 + p.off - p.window + 1;
-            if (full) tile(Ks[buf], Vs[buf], kv0, BoolC<true>{});
-            else tile(Ks[buf], Vs[buf], kv0, BoolC<false>{});
+    // One key tile. The probabilities of keys 0..31 are computed with the
+    // current m while the QK MFMAs of keys 32..63 run; if the tile's max then
+    // moves m (rare after the first tile), they are recomputed before any P V.
+    // The exps of keys 32..63 run alongside the P V MFMAs of keys 0..31.
+    auto tile = [&](const uint16_t* Kt, const uint16_t* Vt, int kv0, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        f32x16 s0, s1;
+        s16x8 pb[4];
+        qk_half(s0, Kt, 0);
+        if constexpr (!FULL) mask_half(s0, kv0, 0);
+        qk_half(s1, Kt, 1);
+        float psum0 = softmax_half(s0, pb[0], pb[1]);
+        if constexpr (FULL) {
+            sched_group<0x100, 2>();
+#pragma unroll
+            for (int i = 0; i < D / 16; ++i) {
+                sched_group<0x008, 1>();
+                if (i + 2 < D / 16) sched_group<0x100, 1>();
+                sched_group<0x002, 56 / (D / 16) + 1>();
+            }
         }
-        if (j + 1 < j_end) lstore(buf ^ 1);  // the other buffer's tile (j-1) is done: barrier of the last step
+        if constexpr (!FULL) mask_half(s1, kv0, 1);
+        const float mx = max_with_other_half(fmaxf(max_half(s0), max_half(s1)));
+        if (rescale(mx)) psum0 = softmax_half(s0, pb[0], pb[1]);
+        pv_chunk(pb[0], Vt, 0);
+        pv_chunk(pb[1], Vt, 1);
+        const float psum1 = softmax_half(s1, pb[2], pb[3]);
+        pv_chunk(pb[2], Vt, 2);
+        pv_chunk(pb[3], Vt, 3);
+        if constexpr (FULL) {
+            sched_group<0x100, 4>();
+#pragma unroll
+            for (int i = 0; i < 4 * NDT; ++i) {
+                sched_group<0x008, 1>();
+                if (i + 2 < 4 * NDT) sched_group<0x100, 2>();
+                if (i < 2 * NDT) sched_group<0x002, 56 / (2 * NDT) + 1>();
+            }
+        }
+        l_i += psum0 + psum1;
+    };
+
+    // Key tile t lives in buffer (t - j_begin) % 2; tile j+1 is requested while
+    // tile j is used, then one wait and one barrier per tile.
+    auto iter = [&](int j, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kl, uint16_t* Vl) {
+        load_k_tile(Kl, j + 1);
+        load_v_tile(Vl, j + 1);
+        if (!tile_empty(j)) {
+            if (tile_full(j)) tile(Kc, Vc, j * PF_BN, BoolC<true>{});
+            else tile(Kc, Vc, j * PF_BN, BoolC<false>{});
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (j + 2 < j_end) gload(j + 2);
+    };
+
+    const int nt = j_end - j_begin;
+    if (nt > 0) {
+        load_k_tile(Ks0, j_begin);
+        load_v_tile(Vs0, j_begin);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+    for (int r = 0; r < nt; r += 2) {
+        iter(j_begin + r, Ks0, Vs0, Ks1, Vs1);
+        if (r + 1 < nt) iter(j_begin + r + 1, Ks1, Vs1, Ks0, Vs0);
     }
 
     // Epilogue: O * (1/l); rows that saw no key are written as zeros.
