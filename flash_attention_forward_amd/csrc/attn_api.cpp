@@ -35,9 +35,16 @@ uint32_t q_flip_mask(float scale, int dtype) {
 // masked score always maps to probability exactly 0. A zero scale becomes
 // 1e-30: every visible score is then a tiny number whose exp2 rounds to 1, the
 // same uniform weights.
-float scaled_log2e(float scale) {
+// |scale| * log2(e), kept at or above `floor` so that a masked score (float32
+// min) times it stays far below every real scaled score and below the kernels'
+// initial running max (-1e30): its exp2 is then exactly 0 and it never moves
+// the max. The 16-bit prefill kernel relies on this arithmetic alone (floor
+// 1e-8, which changes the weights by at most |score| * 1e-8 relative for
+// smaller scales); the other kernels also zero masked entries explicitly and
+// keep the floor at 1e-30, which only separates a zero scale from the mask.
+float scaled_log2e(float scale, double floor) {
     const double c = std::fabs((double)scale) * 1.4426950408889634;
-    return (float)(c < 1e-30 ? 1e-30 : c);
+    return (float)(c < floor ? floor : c);
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
@@ -85,7 +92,7 @@ int attn_prefill_fwd(const void* q, attn_strides q_st, const void* k, attn_strid
     p.batch = batch; p.n_q_heads = n_q_heads; p.n_kv_heads = n_kv_heads; p.group = n_q_heads / n_kv_heads;
     p.seqlen_q = seqlen_q; p.seqlen_kv = seqlen_kv; p.off = seqlen_kv - seqlen_q;
     p.window = window > 0 ? window : 0;
-    p.c = scaled_log2e(scale);
+    p.c = scaled_log2e(scale, dtype == ATTN_F32 ? 1e-30 : 1e-8);
     p.qflip = q_flip_mask(scale, dtype);
     const int mask = !causal ? attn::kMaskNone : (p.window > 0 ? attn::kMaskCausalWindow : attn::kMaskCausal);
     return status_of(attn::launch_prefill(p, (int)dtype, head_dim, mask, (hipStream_t)hip_stream));
@@ -139,7 +146,7 @@ int attn_decode_fwd(const void* q, attn_strides q_st, const void* k_cache, const
         if ((1 << sh) == p.page_size) p.page_shift = sh;
     p.window = window > 0 ? window : 0;
     p.split_len = split_len; p.max_splits = max_splits;
-    p.c = scaled_log2e(scale);
+    p.c = scaled_log2e(scale, 1e-30);
     p.qflip = q_flip_mask(scale, dtype);
     return status_of(attn::launch_decode(p, (int)dtype, head_dim, (hipStream_t)hip_stream));
 }

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
     const int l32 = lane & 31;
     const int hf = lane >> 5;   // wave half
     const int g = lane >> 4;    // 16-lane group
@@ -118,44 +118,54 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
     // valid row: they are masked out (probability exactly 0) and no memory
     // outside the visible key range is touched. Every load is unconditional.
     const int key_min = kv_lo, key_max = p.seqlen_kv - 1;
-    // Lane part of each direct load's source offset (row within the tile and
-    // swizzled chunk), computed once: interior tiles then only add a uniform
-    // tile base. Edge tiles clamp row by row.
-    int koff[LPW], voff[LPW];
-#pragma unroll
-    for (int ii = 0; ii < LPW; ++ii) {
-        const int slot = 64 * (w * LPW + ii) + lane;
-        const int row = slot / CPR, cs = slot % CPR;
-        koff[ii] = row * (int)p.ks.seq + 8 * (cs ^ pf_kswz<D>(row));
-        voff[ii] = row * (int)p.vs.seq + 8 * (cs ^ pf_vswz<D>(row));
-    }
-    // (Two plain lambdas rather than one generic one: a generic lambda that
-    // captures these arrays keeps the compiler's host pass from emitting the
-    // kernel's launch stub.)
-    auto load_tile_impl = [&](uint16_t* dst, const uint16_t* base, int64_t seq, int j, const int* off, bool is_k) {
+    // Tiles are filled with buffer loads straight into LDS: the tile's first
+    // row is the buffer base (a uniform descriptor), lane offsets are 32-bit
+    // byte offsets. Direct load i (0 <= i < TILE/512) covers tile rows RPL*i
+    // .. RPL*i + RPL-1; lane l takes row RPL*i + l/CPR and the swizzled chunk
+    // (l%CPR ^ g(l/CPR)) ^ U(i) (the K or V swizzle factored into a lane part
+    // and a uniform part), so a lane keeps two offsets per tensor. A tile
+    // spans fewer than 64 * seq elements, which the host keeps below 2^31.
+    // Edge tiles clamp row by row.
+    constexpr int RPL = 64 / CPR;
+    const int lrow = lane / CPR, lcs = lane % CPR;
+    const uint32_t kx = 16u * (uint32_t)(lcs ^ (D == 64 ? lrow >> 1 : lrow));
+    const uint32_t vx = 16u * (uint32_t)(lcs ^ (D == 64 ? 4 * ((lrow >> 1) & 1) : 4 * lrow));
+    const uint32_t kl = 2u * (uint32_t)lrow * (uint32_t)p.ks.seq, vl = 2u * (uint32_t)lrow * (uint32_t)p.vs.seq;
+    // (Two plain lambdas rather than one generic one: a generic lambda here
+    // keeps the compiler's host pass from emitting the kernel's launch stub.)
+    auto load_tile_impl = [&](uint16_t* dst, const uint16_t* base, int64_t seq, int j, uint32_t lane_row_off,
+                              uint32_t lane_chunk_off, bool is_k) __attribute__((always_inline)) {
         const int kv0 = j * PF_BN;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kv0 * seq), (short)0, 0x7fffffff, 0x00020000);
         if (kv0 >= key_min && kv0 + PF_BN - 1 <= key_max) {
-            const uint16_t* tbase = base + (int64_t)kv0 * seq;
-#pragma unroll
-            for (int ii = 0; ii < LPW; ++ii)
-                __builtin_amdgcn_global_load_lds(tbase + off[ii],
-                                                 (__attribute__((address_space(3))) void*)(dst + 512 * (w * LPW + ii)),
-                                                 16, 0, 0);
-        } else {
 #pragma unroll
             for (int ii = 0; ii < LPW; ++ii) {
                 const int i = w * LPW + ii;
-                const int slot = 64 * i + lane;
-                const int row = slot / CPR, cs = slot % CPR;
-                const int key = min(max(kv0 + row, key_min), key_max);
+                const uint32_t u = is_k ? (D == 64 ? (4 * i) & 7 : (D == 128 ? (4 * i) & 15 : (2 * i) & 15))
+                                        : (D <= 128 ? 0 : 4 * ((2 * i) & 3));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 512 * i), 16,
+                                                         lane_row_off + (lane_chunk_off ^ (16u * u)),
+                                                         (uint32_t)(2 * RPL * i) * (uint32_t)seq, 0, 0);
+            }
+        } else {
+            // Rare path: recomputed on each use (the opaque copy keeps the
+            // compiler from hoisting per-load lane values out of the loop).
+            int lr = lrow;
+            asm volatile("" : "+v"(lr));
+#pragma unroll
+            for (int ii = 0; ii < LPW; ++ii) {
+                const int i = w * LPW + ii;
+                const int row = RPL * i + lr, cs = lcs;
+                const int key = min(max(kv0 + row, key_min), key_max);  // kv0 <= key <= kv0 + 63
                 const int c = cs ^ (is_k ? pf_kswz<D>(row) : pf_vswz<D>(row));
-                __builtin_amdgcn_global_load_lds(base + (int64_t)key * seq + 8 * c,
-                                                 (__attribute__((address_space(3))) void*)(dst + 512 * i), 16, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 512 * i), 16,
+                                                         2u * ((uint32_t)(key - kv0) * (uint32_t)seq + 8u * c), 0, 0, 0);
             }
         }
     };
-    auto load_k_tile = [&](uint16_t* dst, int j) { load_tile_impl(dst, kbase, p.ks.seq, j, koff, true); };
-    auto load_v_tile = [&](uint16_t* dst, int j) { load_tile_impl(dst, vbase, p.vs.seq, j, voff, false); };
+    auto load_k_tile = [&](uint16_t* dst, int j) __attribute__((always_inline)) { load_tile_impl(dst, kbase, p.ks.seq, j, kl, kx, true); };
+    auto load_v_tile = [&](uint16_t* dst, int j) __attribute__((always_inline)) { load_tile_impl(dst, vbase, p.vs.seq, j, vl, vx, false); };
 
     // Running max in scaled log2 units. It only moves when a row's tile max
     // exceeds it by more than kLazyRescale, so O and l are rescaled rarely;
@@ -168,14 +178,14 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
     for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
     const uint32_t one2 = BF16 ? 0x3F803F80u : 0x3C003C00u;  // two 16-bit 1.0s for the row-sum dot2
 
-    auto tile_empty = [&](int j) {
+    auto tile_empty = [&](int j) __attribute__((always_inline)) {
         const int kv0 = j * PF_BN;
         bool e = !wave_live || j >= j_end;
         if (MASK >= kMaskCausal) e |= kv0 > wq1 + p.off;
         if (MASK == kMaskCausalWindow) e |= kv0 + PF_BN - 1 < wq0 + p.off - p.window + 1;
         return e;
     };
-    auto tile_full = [&](int j) {
+    auto tile_full = [&](int j) __attribute__((always_inline)) {
         const int kv0 = j * PF_BN;
         bool f = kv0 + PF_BN <= p.seqlen_kv;
         if (MASK >= kMaskCausal) f &= kv0 + PF_BN - 1 <= wq0 + p.off;
@@ -183,18 +193,45 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
         return f;
     };
 
-    // S^T: two 32-key blocks x 32 queries; lane holds keys
+    // LDS byte offsets of the MFMA fragments. The swizzled chunk of a K
+    // fragment is (2s + hf) ^ kswz(row) = 2s ^ (hf ^ kswz(row)), and kswz is
+    // the same for rows l32 and 32 + l32, so fragment s of the first block
+    // sits at kfrag ^ 32s and the second block 64*D bytes further. A V^T
+    // fragment of d tile dt sits at vfrag ^ 64dt plus a row offset that is a
+    // compile-time constant (vswz depends on the row only through row % 4 for
+    // D >= 128 and (row / 2) % 2 for D = 64, which the u and +8 row steps
+    // leave unchanged). One register per tensor; the per-fragment XOR is
+    // redone at each use from an opaque copy, so the compiler keeps no
+    // per-fragment addresses live across the loop.
+    const uint32_t kfrag = (uint32_t)(l32 * D * 2) | (16u * (uint32_t)(hf ^ pf_kswz<D>(l32)));
+    const int vr0 = 4 * hf + (r16 >> 2);                  // V^T row of this lane in chunk 0
+    const int vcl = 2 * (g & 1) + ((r16 & 3) >> 1);       // chunk within a 32-wide d tile
+    const uint32_t vfrag = (uint32_t)(vr0 * D * 2) | (16u * (uint32_t)(vcl ^ pf_vswz<D>(vr0))) | (8u * (r16 & 1));
+    auto opaque = [](uint32_t x) __attribute__((always_inline)) {
+        asm volatile("" : "+v"(x));
+        return x;
+    };
+    auto lds_frag8 = [](const uint16_t* base, uint32_t byte_off) __attribute__((always_inline)) {
+        return *(const s16x8*)((const char*)base + byte_off);
+    };
+
+    // S^T of one 64-key tile: two 32-key blocks x 32 queries; lane holds keys
     // 32t + 8(r/4) + 4hf + r%4 of its query row in register r of block t.
-    auto qk_half = [&](f32x16& sacc, const uint16_t* Kt, int t) {
-        sacc = f32x16{};
+    // The two blocks' MFMA chains are interleaved.
+    auto qk_tile = [&](f32x16& s0, f32x16& s1, const uint16_t* Kt) __attribute__((always_inline)) {
+        const uint32_t kf = opaque(kfrag);
+        s0 = f32x16{};
+        s1 = f32x16{};
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-            const int row = 32 * t + l32;
-            const s16x8 a = *(const s16x8*)&Kt[row * D + 8 * ((2 * s + hf) ^ pf_kswz<D>(row))];
-            sacc = mfma32x32x16<BF16>(a, qf[s], sacc);
+            const uint32_t off = kf ^ (32u * s);
+            const s16x8 a0 = lds_frag8(Kt, off);
+            const s16x8 a1 = lds_frag8(Kt + 32 * D, off);
+            s0 = mfma32x32x16<BF16>(a0, qf[s], s0);
+            s1 = mfma32x32x16<BF16>(a1, qf[s], s1);
         }
     };
-    auto mask_half = [&](f32x16& sacc, int kv0, int t) {
+    auto mask_half = [&](f32x16& sacc, int kv0, int t) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
@@ -204,47 +241,17 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
             sacc[r] = keep ? sacc[r] : kMaskedScore;
         }
     };
-    auto max_half = [&](const f32x16& sacc) {
+    // Row max of a tile (raw scores), combined over the two lane halves.
+    auto max_tile = [&](const f32x16& s0, const f32x16& s1) __attribute__((always_inline)) {
         float mx = kMaskedScore;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-        return mx;
-    };
-    // P for one 32-key block, packed as B operands of O^T += V^T P^T: chunk
-    // u (keys 16u..16u+15) takes registers 8(u%2)..8(u%2)+7 of block u/2; slot
-    // j of lane half hf is key 16u + 8(j/4) + 4hf + j%4. Masked scores
-    // (float32 min) give exactly 0: the host keeps p.c >= 1e-30.
-    auto softmax_half = [&](const f32x16& sacc, s16x8& pb0, s16x8& pb1) {
-        const float neg_m = -m_i;
-        float psum = 0.f;
-        uint32_t pk[8];
-#pragma unroll
-        for (int jj = 0; jj < 16; jj += 2) {
-            const float p0 = fast_exp2(fmaf(sacc[jj], p.c, neg_m));
-            const float p1 = fast_exp2(fmaf(sacc[jj + 1], p.c, neg_m));
-            pk[jj / 2] = pack2_16<BF16>(p0, p1);
-            psum = dot2_16<BF16>(pk[jj / 2], one2, psum);  // sum of the rounded P
-        }
-        pb0 = __builtin_bit_cast(s16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-        pb1 = __builtin_bit_cast(s16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
-        return psum;
-    };
-    // O^T[d, q] += V^T[d, keys] P^T[keys, q] for key chunk u. A operand via
-    // transpose reads: lane r16 of group g points at row 16u + 4hf + r16/4
-    // (and +8), column 32dt + 16(g%2) + 4(r16%4), and receives column
-    // 32dt + 16(g%2) + r16 of four consecutive key rows.
-    auto pv_chunk = [&](const s16x8& pb, const uint16_t* Vt, int u) {
-        const int r0 = 16 * u + 4 * hf + (r16 >> 2), r1 = r0 + 8;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const int c = 4 * dt + 2 * (g & 1) + ((r16 & 3) >> 1), e = 4 * (r16 & 1);
-            const s16x4 lo = lds_read_tr16(&Vt[r0 * D + 8 * (c ^ pf_vswz<D>(r0)) + e]);
-            const s16x4 hi4 = lds_read_tr16(&Vt[r1 * D + 8 * (c ^ pf_vswz<D>(r1)) + e]);
-            o[dt] = mfma32x32x16<BF16>(concat4(lo, hi4), pb, o[dt]);
-        }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+        return max_with_other_half(mx);
     };
     // Move m (and rescale O and l) for rows whose tile max passed m + margin.
-    auto rescale = [&](float mx) {
+    // A row that sees no key of the tile has max = the mask value, and
+    // mask * c is far below any m, so such a row keeps its m.
+    auto rescale = [&](float mx) __attribute__((always_inline)) {
         const float m_cand = mx * p.c;
         const bool grow = m_cand > m_i + kLazyRescale;
         if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -254,75 +261,118 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
             l_i *= alpha;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-            return true;
         }
-        return false;
     };
-
-    // One key tile. The probabilities of keys 0..31 are computed with the
-    // current m while the QK MFMAs of keys 32..63 run; if the tile's max then
-    // moves m (rare after the first tile), they are recomputed before any P V.
-    // The exps of keys 32..63 run alongside the P V MFMAs of keys 0..31.
-    auto tile = [&](const uint16_t* Kt, const uint16_t* Vt, int kv0, auto full_tag) {
-        constexpr bool FULL = decltype(full_tag)::value;
-        f32x16 s0, s1;
-        s16x8 pb[4];
-        qk_half(s0, Kt, 0);
-        if constexpr (!FULL) mask_half(s0, kv0, 0);
-        qk_half(s1, Kt, 1);
-        float psum0 = softmax_half(s0, pb[0], pb[1]);
-        if constexpr (FULL) {
-            sched_group<0x100, 2>();
+    // P of one 32-key block as packed 16-bit pairs: pk[j/2] holds keys j, j+1
+    // of the block's register order. Chunk u of the tile (keys 16u..16u+15)
+    // is pk[4u .. 4u+3] when pk spans both blocks; slot j of lane half hf is
+    // key 16u + 8(j/4) + 4hf + j%4, the B-operand layout of O^T += V^T P^T.
+    // A masked score gives exactly 0.
+    auto probs_half = [&](const f32x16& sacc, uint32_t* pk) __attribute__((always_inline)) {
+        const float neg_m = -m_i;
 #pragma unroll
-            for (int i = 0; i < D / 16; ++i) {
-                sched_group<0x008, 1>();
-                if (i + 2 < D / 16) sched_group<0x100, 1>();
-                sched_group<0x002, 56 / (D / 16) + 1>();
+        for (int jj = 0; jj < 16; jj += 2) {
+            const float p0 = fast_exp2(fmaf(sacc[jj], p.c, neg_m));
+            const float p1 = fast_exp2(fmaf(sacc[jj + 1], p.c, neg_m));
+            pk[jj / 2] = pack2_16<BF16>(p0, p1);
+        }
+    };
+    // Sum of the rounded P of a tile (the same values the P V product uses).
+    auto psum_tile = [&](const uint32_t* pk) __attribute__((always_inline)) {
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ps = dot2_16<BF16>(pk[i], one2, ps);
+        return ps;
+    };
+    // O^T[d, q] += V^T[d, keys] P^T[keys, q] for the whole tile. A operand via
+    // transpose reads: lane r16 of group g points at row 16u + 4hf + r16/4
+    // (and +8), column 32dt + 16(g%2) + 4(r16%4), and receives column
+    // 32dt + 16(g%2) + r16 of four consecutive key rows.
+    auto pv_tile = [&](const uint32_t* pk, const uint16_t* Vt) __attribute__((always_inline)) {
+        const uint32_t vf = opaque(vfrag);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const s16x8 pb = __builtin_bit_cast(s16x8, make_uint4(pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]));
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const char* vb = (const char*)Vt + (vf ^ (64u * dt));
+                const s16x4 lo = lds_read_tr16((const uint16_t*)(vb + 2 * D * (16 * u)));
+                const s16x4 hi4 = lds_read_tr16((const uint16_t*)(vb + 2 * D * (16 * u + 8)));
+                o[dt] = mfma32x32x16<BF16>(concat4(lo, hi4), pb, o[dt]);
             }
         }
-        if constexpr (!FULL) mask_half(s1, kv0, 1);
-        const float mx = max_with_other_half(fmaxf(max_half(s0), max_half(s1)));
-        if (rescale(mx)) psum0 = softmax_half(s0, pb[0], pb[1]);
-        pv_chunk(pb[0], Vt, 0);
-        pv_chunk(pb[1], Vt, 1);
-        const float psum1 = softmax_half(s1, pb[2], pb[3]);
-        pv_chunk(pb[2], Vt, 2);
-        pv_chunk(pb[3], Vt, 3);
-        if constexpr (FULL) {
-            sched_group<0x100, 4>();
-#pragma unroll
-            for (int i = 0; i < 4 * NDT; ++i) {
-                sched_group<0x008, 1>();
-                if (i + 2 < 4 * NDT) sched_group<0x100, 2>();
-                if (i < 2 * NDT) sched_group<0x002, 56 / (2 * NDT) + 1>();
-            }
-        }
-        l_i += psum0 + psum1;
     };
 
-    // Key tile t lives in buffer (t - j_begin) % 2; tile j+1 is requested while
-    // tile j is used, then one wait and one barrier per tile.
-    auto iter = [&](int j, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kl, uint16_t* Vl) {
-        load_k_tile(Kl, j + 1);
-        load_v_tile(Vl, j + 1);
-        if (!tile_empty(j)) {
-            if (tile_full(j)) tile(Kc, Vc, j * PF_BN, BoolC<true>{});
-            else tile(Kc, Vc, j * PF_BN, BoolC<false>{});
+    // Software pipeline over key tiles, two tiles of scores in registers:
+    // step j runs the QK MFMAs of tile j+1 while the VALU turns the scores of
+    // tile j into probabilities (with the m settled at the end of step j-1),
+    // then the P V MFMAs of tile j, and finally takes the row max of tile j+1
+    // and settles m for it (rescaling O, which by then includes tile j). K(j+1) and V(j) are read in step j; K(j+2) and V(j+1)
+    // are loaded meanwhile into the buffers that held K(j) and V(j-1).
+    //
+    // Every step runs the same code. A tile that is not fully visible to all
+    // rows of the wave gets its hidden scores replaced by the mask value, whose
+    // probability is exactly 0 and which never moves m (the host keeps
+    // p.c >= 1e-8, so mask * c lies far below the initial m); this covers the
+    // diagonal and window-edge tiles, the ragged end of K, tiles past the
+    // wave's last visible key, and the tile after the last one (read from a
+    // stale or unfilled buffer and never used).
+    auto step = [&](int j, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1, const uint16_t* Kn, const uint16_t* Vc,
+                    uint16_t* Kl, uint16_t* Vl) __attribute__((always_inline)) {
+        if (j + 2 < j_end) load_k_tile(Kl, j + 2);
+        if (j + 1 < j_end) load_v_tile(Vl, j + 1);
+        uint32_t pk[16];
+        qk_tile(n0, n1, Kn);
+        probs_half(c0, pk);
+        probs_half(c1, pk + 8);
+        sched_group<0x100, 2>();
+#pragma unroll
+        for (int i = 0; i < 2 * (D / 16); ++i) {
+            sched_group<0x008, 1>();
+            if (i + 2 < 2 * (D / 16)) sched_group<0x100, 1>();
+            sched_group<0x002, 80 / (2 * (D / 16)) + 1>();
         }
+        pv_tile(pk, Vc);
+        l_i += psum_tile(pk);
+        sched_group<0x100, 4>();
+#pragma unroll
+        for (int i = 0; i < 4 * NDT; ++i) {
+            sched_group<0x008, 1>();
+            if (i + 2 < 4 * NDT) sched_group<0x100, 2>();
+            sched_group<0x002, 1>();
+        }
+        if (!(wave_live && tile_full(j + 1))) {
+            mask_half(n0, (j + 1) * PF_BN, 0);
+            mask_half(n1, (j + 1) * PF_BN, 1);
+        }
+        rescale(max_tile(n0, n1));
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     };
 
+    // Prologue: K(j_begin), V(j_begin), K(j_begin + 1) in, S(j_begin) and its m.
+    f32x16 sa0, sa1, sb0, sb1;
     const int nt = j_end - j_begin;
     if (nt > 0) {
         load_k_tile(Ks0, j_begin);
         load_v_tile(Vs0, j_begin);
+        if (nt > 1) load_k_tile(Ks1, j_begin + 1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        qk_tile(sa0, sa1, Ks0);
+        if (!(wave_live && tile_full(j_begin))) {
+            mask_half(sa0, j_begin * PF_BN, 0);
+            mask_half(sa1, j_begin * PF_BN, 1);
+        }
+        rescale(max_tile(sa0, sa1));
+        __syncthreads();  // K(j_begin) is read by every wave before its buffer is refilled
     }
+    // Step r = j - j_begin: K(j+1) sits in buffer (r+1)%2, V(j) in buffer r%2.
+    // Unrolled by two so that every LDS access names its buffer (the compiler
+    // then waits on a refill only before reads of the buffer being refilled).
     for (int r = 0; r < nt; r += 2) {
-        iter(j_begin + r, Ks0, Vs0, Ks1, Vs1);
-        if (r + 1 < nt) iter(j_begin + r + 1, Ks1, Vs1, Ks0, Vs0);
+        step(j_begin + r, sa0, sa1, sb0, sb1, Ks1, Vs0, Ks0, Vs1);
+        if (r + 1 < nt) step(j_begin + r + 1, sb0, sb1, sa0, sa1, Ks0, Vs1, Ks1, Vs0);
     }
 
     // Epilogue: O * (1/l); rows that saw no key are written as zeros.
