@@ -55,17 +55,6 @@ __device__ __forceinline__ int dc_vswz(int row) {
 // lookup. GENERIC: any page size; one lookup per key row.
 enum DecodeMode { kDecodeFlat = 0, kDecodeFast = 1, kDecodeGeneric = 2 };
 
-// s_waitcnt vmcnt(N) with N a compile-time constant.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N <= 63, "vmcnt range");
-    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if constexpr (N == 32) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-    else static_assert(N == 0, "add this count");
-}
-
 template <bool BF16, int D, int MODE>
 __global__ __launch_bounds__(64, (D >= 256 ? 1 : 2)) void decode_split(DecodeParams p) {
     constexpr int NKS = D / 32;              // k-steps of S^T = K Q^T

@@ -34,6 +34,21 @@ __device__ __forceinline__ void sched_group() {
 #endif
 }
 
+// Wait until at most N vector-memory operations of this wave are in flight
+// (loads complete in issue order, so this waits for all but the last N).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Scheduling fence: the compiler moves no instruction across it.
+__device__ __forceinline__ void sched_fence() {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+
 // Value of lane (l ^ 32) for every lane l, with one v_permlane32_swap.
 __device__ __forceinline__ float max_with_other_half(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -3,13 +3,16 @@
 // f16 / bf16: prefill_mfma — one workgroup per (128-row Q tile, q-head,
 // batch), four waves of 32 query rows each. Q stays in VGPRs as MFMA
 // operands for the whole kernel ("Q resident, KV streams": CTE page,
-// section "Tile shapes and residency"); 64-key K/V tiles stream through LDS,
-// register-prefetched one tile ahead. Each wave computes the transposed
-// score tile S^T = K Q^T with v_mfma_f32_32x32x16, so every lane owns one
-// query row and the row max / row sum are in-lane plus one v_permlane32_swap.
-// The f32 S^T accumulator layout is exactly the B-operand layout of
-// O^T += V^T P^T, so P never leaves registers; V^T is read from the
-// row-major V tile with ds_read_b64_tr_b16. O^T (f32) and m, l stay in VGPRs.
+// section "Tile shapes and residency"); 64-key K/V tiles stream through LDS
+// in two buffers each, filled by buffer loads that write LDS directly. Each
+// wave computes the transposed score tile S^T = K Q^T with
+// v_mfma_f32_32x32x16, so every lane owns one query row and the row max /
+// row sum are in-lane plus one v_permlane32_swap. The f32 S^T accumulator
+// layout is exactly the B-operand layout of O^T += V^T P^T, so P never
+// leaves registers; V^T is read from the row-major V tile with
+// ds_read_b64_tr_b16. O^T (f32) and m, l stay in VGPRs. The key loop is
+// software-pipelined: the QK MFMAs of tile j+1 run while the VALU
+// exponentiates tile j.
 //
 // Online softmax per tile (CTE page, "The online-softmax recurrence"; minfer
 // 8n page, section 2.1): scores are kept in scaled log2 units t = s*scale*log2e,
@@ -317,47 +320,112 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
     // diagonal and window-edge tiles, the ragged end of K, tiles past the
     // wave's last visible key, and the tile after the last one (read from a
     // stale or unfilled buffer and never used).
-    auto step = [&](int j, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1, const uint16_t* Kn, const uint16_t* Vc,
-                    uint16_t* Kl, uint16_t* Vl) __attribute__((always_inline)) {
-        if (j + 2 < j_end) load_k_tile(Kl, j + 2);
+    // The step body is laid out by hand in stages separated by scheduling
+    // fences: stage s of the QK part issues the two MFMAs of K chunk s, the
+    // LDS reads of chunk s+2 and 1/NS of the probabilities; stage i of the
+    // P V part issues MFMA i, the transpose reads of MFMA i+4, one row-sum
+    // dot2 and part of the raw row max of tile j+1. LDS reads thus run two
+    // stages (at least 128 MFMA cycles) ahead of their use.
+    //
+    // Loads and barriers: step j issues V(j+1) at its start (into the buffer
+    // of V(j-1)) and K(j+3) after a mid-step barrier that follows the QK part
+    // (into the buffer of K(j+1), which that part has just read). The
+    // mid-step barrier also publishes V(j), the end-of-step barrier K(j+2):
+    // every tile has about one and a half steps to arrive. Loads complete in
+    // issue order (V(j), K(j+2), V(j+1), K(j+3), ...), so each barrier waits
+    // with vmcnt = the loads issued after the one it needs.
+    constexpr int NS = D / 16;          // K chunks of 16 along d
+    constexpr int NPV = 4 * NDT;        // P V MFMAs per tile
+    constexpr int VPRE = 4;             // P V MFMAs whose fragments are in flight
+    static_assert(NS >= 4, "the V prefetch is issued in the last two QK stages");
+    auto wait_tiles = [&](int n_after) __attribute__((always_inline)) {
+        if (n_after >= 2) wait_vmcnt<2 * LPW>();
+        else if (n_after == 1) wait_vmcnt<LPW>();
+        else wait_vmcnt<0>();
+    };
+    auto step = [&](int j, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1, uint16_t* Kn, uint16_t* Vc,
+                    uint16_t* Vl) __attribute__((always_inline)) {
         if (j + 1 < j_end) load_v_tile(Vl, j + 1);
+        const uint32_t kf = opaque(kfrag);
+        const uint32_t vf = opaque(vfrag);
+        s16x8 ka[NS][2];
+        s16x8 vb[NPV];
         uint32_t pk[16];
-        qk_tile(n0, n1, Kn);
-        probs_half(c0, pk);
-        probs_half(c1, pk + 8);
-        sched_group<0x100, 2>();
+        auto kread = [&](int s) __attribute__((always_inline)) {
+            ka[s][0] = lds_frag8(Kn, kf ^ (32u * s));
+            ka[s][1] = lds_frag8(Kn + 32 * D, kf ^ (32u * s));
+        };
+        auto vread = [&](int i) __attribute__((always_inline)) {
+            const int u = i / NDT, dt = i % NDT;
+            const char* vb0 = (const char*)Vc + (vf ^ (64u * dt));
+            vb[i] = concat4(lds_read_tr16((const uint16_t*)(vb0 + 2 * D * (16 * u))),
+                            lds_read_tr16((const uint16_t*)(vb0 + 2 * D * (16 * u + 8))));
+        };
+        // probabilities pk[i] from scores 2(i%8), 2(i%8)+1 of block i/8 of the current tile
+        const float neg_m = -m_i;
+        auto prob_pair = [&](int i) __attribute__((always_inline)) {
+            const f32x16& sc = i < 8 ? c0 : c1;
+            const int r = 2 * (i % 8);
+            pk[i] = pack2_16<BF16>(fast_exp2(fmaf(sc[r], p.c, neg_m)), fast_exp2(fmaf(sc[r + 1], p.c, neg_m)));
+            asm volatile("" ::"v"(pk[i]));  // computed here, not sunk below the mid-step barrier
+        };
+        kread(0);
+        kread(1);
+        sched_fence();
+        n0 = f32x16{};
+        n1 = f32x16{};
 #pragma unroll
-        for (int i = 0; i < 2 * (D / 16); ++i) {
-            sched_group<0x008, 1>();
-            if (i + 2 < 2 * (D / 16)) sched_group<0x100, 1>();
-            sched_group<0x002, 80 / (2 * (D / 16)) + 1>();
-        }
-        pv_tile(pk, Vc);
-        l_i += psum_tile(pk);
-        sched_group<0x100, 4>();
+        for (int s = 0; s < NS; ++s) {
+            n0 = mfma32x32x16<BF16>(ka[s][0], qf[s], n0);
+            n1 = mfma32x32x16<BF16>(ka[s][1], qf[s], n1);
+            if (s + 2 < NS) kread(s + 2);
 #pragma unroll
-        for (int i = 0; i < 4 * NDT; ++i) {
-            sched_group<0x008, 1>();
-            if (i + 2 < 4 * NDT) sched_group<0x100, 2>();
-            sched_group<0x002, 1>();
+            for (int i = s * 16 / NS; i < (s + 1) * 16 / NS; ++i) prob_pair(i);
+            sched_fence();
         }
+        // V(j) in; every wave is past its reads of K(j+1).
+        wait_tiles((j + 2 < j_end) + (j + 1 < j_end));
+        __syncthreads();
+        if (j + 3 < j_end) load_k_tile(Kn, j + 3);
+#pragma unroll
+        for (int i = 0; i < VPRE; ++i) vread(i);
+        sched_fence();
+        float ps = 0.f, mx = kMaskedScore;
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            const int u = i / NDT, dt = i % NDT;
+            const s16x8 pb = __builtin_bit_cast(s16x8, make_uint4(pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]));
+            o[dt] = mfma32x32x16<BF16>(vb[i], pb, o[dt]);
+            if (i + VPRE < NPV) vread(i + VPRE);
+#pragma unroll
+            for (int e = i * 16 / NPV; e < (i + 1) * 16 / NPV; ++e) {
+                ps = dot2_16<BF16>(pk[e], one2, ps);
+                mx = fmaxf(mx, fmaxf(n0[e], n1[e]));
+            }
+            sched_fence();
+        }
+        l_i += ps;
+        mx = max_with_other_half(mx);
         if (!(wave_live && tile_full(j + 1))) {
             mask_half(n0, (j + 1) * PF_BN, 0);
             mask_half(n1, (j + 1) * PF_BN, 1);
+            mx = fminf(mx, max_tile(n0, n1));  // masking only lowers the max
         }
-        rescale(max_tile(n0, n1));
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        rescale(mx);
+        // K(j+2) in; every wave is past its reads of V(j).
+        wait_tiles((j + 1 < j_end) + (j + 3 < j_end));
         __syncthreads();
     };
 
-    // Prologue: K(j_begin), V(j_begin), K(j_begin + 1) in, S(j_begin) and its m.
+    // Prologue: K(j_begin), V(j_begin), K(j_begin + 1) in, S(j_begin) and its
+    // m, then K(j_begin + 2) requested into the buffer of K(j_begin).
     f32x16 sa0, sa1, sb0, sb1;
     const int nt = j_end - j_begin;
     if (nt > 0) {
         load_k_tile(Ks0, j_begin);
         load_v_tile(Vs0, j_begin);
         if (nt > 1) load_k_tile(Ks1, j_begin + 1);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wait_vmcnt<0>();
         __syncthreads();
         qk_tile(sa0, sa1, Ks0);
         if (!(wave_live && tile_full(j_begin))) {
@@ -365,15 +433,17 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
             mask_half(sa1, j_begin * PF_BN, 1);
         }
         rescale(max_tile(sa0, sa1));
-        __syncthreads();  // K(j_begin) is read by every wave before its buffer is refilled
+        __syncthreads();  // every wave is past its reads of K(j_begin)
+        if (nt > 2) load_k_tile(Ks0, j_begin + 2);
     }
     // Step r = j - j_begin: K(j+1) sits in buffer (r+1)%2, V(j) in buffer r%2.
     // Unrolled by two so that every LDS access names its buffer (the compiler
     // then waits on a refill only before reads of the buffer being refilled).
     for (int r = 0; r < nt; r += 2) {
-        step(j_begin + r, sa0, sa1, sb0, sb1, Ks1, Vs0, Ks0, Vs1);
-        if (r + 1 < nt) step(j_begin + r + 1, sb0, sb1, sa0, sa1, Ks0, Vs1, Ks1, Vs0);
+        step(j_begin + r, sa0, sa1, sb0, sb1, Ks1, Vs0, Vs1);
+        if (r + 1 < nt) step(j_begin + r + 1, sb0, sb1, sa0, sa1, Ks0, Vs1, Vs0);
     }
+    wait_vmcnt<0>();  // nothing is left in flight when the wave ends
 
     // Epilogue: O * (1/l); rows that saw no key are written as zeros.
     const float l_tot = sum_with_other_half(l_i);

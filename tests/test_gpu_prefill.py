@@ -79,6 +79,19 @@ def test_scale_sign_and_zero(scale):
     check(gpu_prefill(inp, scale=scale), oracle_prefill(inp, scale=scale), "bf16", f"scale={scale}")
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64), ("bf16", 256), ("f32", 128)])
+@pytest.mark.parametrize("scale", [0.0, 1e-12, 0.1])
+def test_rows_without_keys_and_tiny_scales(dtype, d, scale):
+    """seqlen_q > seqlen_kv with the causal mask: the first rows see no key and must be zeros,
+    also when |scale| is zero or far below any normal softmax scale."""
+    spec = W.PrefillSpec(1, 2, 1, 300, 120, d, dtype, causal=True)
+    inp = W.make_prefill(spec, seed=41)
+    say("prefill rows without keys", dtype, d, scale)
+    out = gpu_prefill(inp, scale=scale)
+    assert (out[:, :180] == 0).all()
+    check(out, oracle_prefill(inp, scale=scale), dtype, f"{dtype} d={d} scale={scale}")
+
+
 def test_gqa_equals_replicated_kv_bitwise():
     torch = torch_cuda()
     import flash_attention_forward_amd as F
