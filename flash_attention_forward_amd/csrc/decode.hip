@@ -1,16 +1,19 @@
 // Split-KV decode attention and the log-sum-exp combine for gfx950.
 //
-// decode_split: one wavefront per (split, kv-head, sequence). The G * s_active
+// decode_split: one wavefront per (split, kv-head, sequence), HW of them (the
+// kv-heads of one split) per workgroup, so that the rows of all heads of a
+// page are read by one CU at about the same time. The G * s_active
 // query rows that share a kv-head (G = n_q_heads / n_kv_heads) ride one MFMA
 // together, so each K/V byte is read once for all of them — the decode page's
 // grouped-query "free broadcast" ("Flash-Attention: Decode (TKG)", section
 // "GQA / MQA grouped-query broadcast"), done here with v_mfma_f32_16x16x32
 // (16 key rows x 16 query columns, query columns beyond G * s_active are
 // zero). Keys are gathered through the uint32 page table, 32 per iteration
-// (decode page, section "Paged / block cache"): K goes from HBM straight into
-// the MFMA A operand, V is staged through LDS and read back transposed with
-// ds_read_b64_tr_b16 for O^T += V^T P^T. The next 32 keys are in flight while
-// the current ones are used. Rows of a split's last page at or beyond
+// (decode page, section "Paged / block cache"): whole 256-byte K and V rows
+// are loaded straight into LDS, K read back as the MFMA A operand and V read
+// back transposed with ds_read_b64_tr_b16 for O^T += V^T P^T. The next 32 keys
+// are in flight while the current ones are used. All loads go to LDS, so the
+// only waits on them are the explicit per-block ones. Rows of a split's last page at or beyond
 // cache_len are neither read nor used (decode page, section "gen_mask_tkg":
 // index < cache length), and their V rows are zero so that nothing there can
 // leak into the product.
@@ -55,32 +58,48 @@ __device__ __forceinline__ int dc_vswz(int row) {
 // lookup. GENERIC: any page size; one lookup per key row.
 enum DecodeMode { kDecodeFlat = 0, kDecodeFast = 1, kDecodeGeneric = 2 };
 
-template <bool BF16, int D, int MODE>
-__global__ __launch_bounds__(64, (D >= 256 ? 1 : 2)) void decode_split(DecodeParams p) {
+// Kv-heads (waves) per workgroup: each wave holds 32 KB * D / 128 of LDS, and a
+// workgroup stays at or below 64 KB so that two fit on a CU (the next one's
+// start-up then overlaps the current one's streaming).
+template <int D>
+constexpr int dc_max_heads() {
+    return D >= 256 ? 1 : (D >= 128 ? 2 : 4);
+}
+
+// 16-byte chunk swizzle of a K row in LDS: the 16 lanes of a fragment read hit
+// rows r..r+15 at one chunk, spread over 16 bank groups.
+template <int D>
+__device__ __forceinline__ int dc_kswz(int row) {
+    return D == 64 ? ((row >> 1) & 7) : (row & 15);
+}
+
+template <bool BF16, int D, int MODE, int HW>
+__global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
     constexpr int NKS = D / 32;              // k-steps of S^T = K Q^T
     constexpr int NDT = D / 16;              // 16-row d tiles of O^T
     constexpr int CPR = D / 8;               // 16-byte chunks per V row
     constexpr int RPL = 64 / CPR;            // V rows covered by one direct-to-LDS load
-    constexpr int VLD = DC_KB / RPL;         // direct-to-LDS loads per lane per block
-    constexpr int KLD = 2 * NKS;             // K loads per lane per block
-    // Two V tiles in LDS and two K register sets: block i+2 is requested while
+    constexpr int VLD = DC_KB / RPL;         // direct-to-LDS loads per lane per block and tensor
+    // Two K and two V tiles per wave in LDS: block i+2 is requested while
     // block i is used, so each block's loads have a whole iteration to land.
-    __shared__ __attribute__((aligned(16))) uint16_t VsA[DC_KB * D];
-    __shared__ __attribute__((aligned(16))) uint16_t VsB[DC_KB * D];
+    // The tiles are private to their wave.
+    __shared__ __attribute__((aligned(16))) uint16_t KsA[HW][DC_KB * D];
+    __shared__ __attribute__((aligned(16))) uint16_t KsB[HW][DC_KB * D];
+    __shared__ __attribute__((aligned(16))) uint16_t VsA[HW][DC_KB * D];
+    __shared__ __attribute__((aligned(16))) uint16_t VsB[HW][DC_KB * D];
     // This split's slice of the page table, read once: address generation in
     // the loop then never waits on a global load.
     __shared__ uint32_t pages[kDecodeMaxSplitPages];
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave index, uniform
     const int n = lane & 15;   // query column / key row within a 16-block
     const int g = lane >> 4;   // 16-lane group
-    // x = kv-head fastest: the waves of one split are dispatched together and
-    // read the same pages at about the same time.
-    const int hk = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
+    const int hk = blockIdx.x * HW + w, split = blockIdx.y, b = blockIdx.z;
 
     const int len = p.cache_len[b];
     const int t0 = split * p.split_len;
-    if (t0 >= len) return;  // this split is past the cache: nothing is written
+    if (t0 >= len) return;  // this split is past the cache: nothing is written (uniform in the workgroup)
     const int t1 = min(len, t0 + p.split_len);
 
     const int nrows = p.group * p.s_active;
@@ -109,8 +128,8 @@ __global__ __launch_bounds__(64, (D >= 256 ? 1 : 2)) void decode_split(DecodePar
         const int first = t0 / p.page_size;
         const int npg = (t1 - 1) / p.page_size - first + 1;
         const uint32_t* row = p.block_table + (int64_t)b * p.max_pages_per_seq + first;
-        for (int i = lane; i < npg; i += 64) pages[i] = row[i];
-        __syncthreads();
+        for (int i = threadIdx.x; i < npg; i += 64 * HW) pages[i] = row[i];
+        __syncthreads();  // the only workgroup barrier: every early return above is uniform
     }
 
     // Q fragments: B operand of S^T = K Q^T (lane: column n, d = 32ks + 8g .. +8).
@@ -153,7 +172,7 @@ __global__ __launch_bounds__(64, (D >= 256 ? 1 : 2)) void decode_split(DecodePar
     // token: rows past the end (and whole blocks past the last one) re-read
     // finite cache data, get probability exactly 0 in the softmax and so add
     // exactly nothing to P V. Nothing at or beyond cache_len is ever read. With
-    // no conditional loads, each lane has exactly KLD + VLD loads per block in
+    // no conditional loads, each lane has exactly 2 * VLD loads per block in
     // flight and the wait counts below hold on every path.
     const int tlast = t1 - 1;
     // FAST: offset of the 16-aligned group holding token t, plus the row within it
@@ -162,26 +181,17 @@ __global__ __launch_bounds__(64, (D >= 256 ? 1 : 2)) void decode_split(DecodePar
         const int tg = tc & ~15;
         return row_off(tg) + (int64_t)(tc - tg) * seq;
     };
-    auto load_k = [&](uint4 (&kr)[2][NKS], int tb) {
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-            const int t = tb + 16 * gi + n;
-            const uint16_t* src = kbase + (MODE == kDecodeGeneric ? row_off(min(t, tlast)) : fast_off(t)) + 8 * g;
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) kr[gi][ks] = *(const uint4*)(src + 32 * ks);
-        }
-    };
-    // V block straight into LDS: load i writes LDS bytes [1 KB * i, 1 KB * (i + 1)),
-    // lane L landing at row i * RPL + L / CPR, swizzled chunk L % CPR.
+    // A K or V block straight into LDS: load i writes LDS bytes [1 KB * i,
+    // 1 KB * (i + 1)), lane L landing at row i * RPL + L / CPR, swizzled chunk L % CPR.
     const int cs = lane % CPR;
-    auto load_v = [&](uint16_t* V, int tb) {
+    auto load_rows = [&](uint16_t* dst, const uint16_t* base, int tb, bool is_k) {
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
             const int row = i * RPL + lane / CPR;
             const int t = tb + row;
-            const int c = cs ^ dc_vswz<D>(row);
+            const int c = cs ^ (is_k ? dc_kswz<D>(row) : dc_vswz<D>(row));
             const int64_t off = MODE == kDecodeGeneric ? row_off(min(t, tlast)) : fast_off(t);
-            __builtin_amdgcn_global_load_lds(vbase + off + 8 * c, (__attribute__((address_space(3))) void*)(V + 512 * i),
+            __builtin_amdgcn_global_load_lds(base + off + 8 * c, (__attribute__((address_space(3))) void*)(dst + 512 * i),
                                              16, 0, 0);
         }
     };
@@ -193,18 +203,22 @@ __global__ __launch_bounds__(64, (D >= 256 ? 1 : 2)) void decode_split(DecodePar
 
     // One block: wait for its loads, S^T = K Q^T, refill these K registers with
     // block it+2, online softmax, O^T += V^T P^T, refill this V tile with block it+2.
-    auto step = [&](uint4 (&kr)[2][NKS], uint16_t* V, int it) {
+    auto step = [&](uint16_t* K, uint16_t* V, int it) {
         const int tb = tb0 + it * DC_KB;
-        wait_vmcnt<KLD + VLD>();  // only block it+1's loads may still be in flight
-        __syncthreads();
+        wait_vmcnt<2 * VLD>();  // only block it+1's loads may still be in flight
 
+        // S^T = K Q^T: lane (n, g) reads key row 16gi + n, d chunk 4ks + g.
         f32x4 sacc[2] = {f32x4{}, f32x4{}};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-            for (int gi = 0; gi < 2; ++gi)
-                sacc[gi] = mfma16x16x32<BF16>(__builtin_bit_cast(s16x8, kr[gi][ks]), qf[ks], sacc[gi]);
-        load_k(kr, tb + 2 * DC_KB);  // block it+2 (clamped rows when past the end)
+            for (int gi = 0; gi < 2; ++gi) {
+                const int row = 16 * gi + n;
+                const s16x8 a = *(const s16x8*)&K[row * D + 8 * ((4 * ks + g) ^ dc_kswz<D>(row))];
+                sacc[gi] = mfma16x16x32<BF16>(a, qf[ks], sacc[gi]);
+            }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // K fragment reads done before the tile is refilled
+        load_rows(K, kbase, tb + 2 * DC_KB, true);  // block it+2 (clamped rows when past the end)
 
         // rows at or beyond t1 hold another row's keys: masked here
         float mx = kMaskedScore;
@@ -250,19 +264,17 @@ __global__ __launch_bounds__(64, (D >= 256 ? 1 : 2)) void decode_split(DecodePar
             o[dt] = mfma16x16x32<BF16>(concat4(lo, hi4), pb, o[dt]);
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // transpose reads done before the tile is refilled
-        __syncthreads();
-        load_v(V, tb + 2 * DC_KB);
+        load_rows(V, vbase, tb + 2 * DC_KB, false);
     };
 
-    uint4 ka[2][NKS], kb[2][NKS];
-    load_k(ka, tb0);
-    load_v(VsA, tb0);
-    load_k(kb, tb0 + DC_KB);
-    load_v(VsB, tb0 + DC_KB);
+    load_rows(KsA[w], kbase, tb0, true);
+    load_rows(VsA[w], vbase, tb0, false);
+    load_rows(KsB[w], kbase, tb0 + DC_KB, true);
+    load_rows(VsB[w], vbase, tb0 + DC_KB, false);
     // An odd block count runs one extra, fully masked block (no loads beyond the clamp).
     for (int it = 0; it < nblk; it += 2) {
-        step(ka, VsA, it);
-        step(kb, VsB, it + 1);
+        step(KsA[w], VsA[w], it);
+        step(KsB[w], VsB[w], it + 1);
     }
     wait_vmcnt<0>();  // drain the clamped prefetches before the wave ends
 
@@ -277,11 +289,15 @@ __global__ __launch_bounds__(64, (D >= 256 ? 1 : 2)) void decode_split(DecodePar
     }
 }
 
+// One wave per output row. A split's partial row is read as float4s by
+// D / 4 lanes, so one load instruction covers 64 / (D / 4) splits and up to 16
+// instructions per lane are in flight; the lane groups that took different
+// splits are summed with lane swaps at the end.
 template <bool BF16, int D>
 __global__ __launch_bounds__(64) void decode_combine(CombineParams p) {
-    constexpr int PER = D / 64;
-    constexpr int MAXS = 256;  // splits weighted in parallel per pass
-    __shared__ float wts[MAXS];
+    constexpr int LPR = D / 4;      // lanes per split row
+    constexpr int RPW = 64 / LPR;   // split rows per load instruction
+    constexpr int U = 16;           // load instructions in flight per lane
     const int lane = threadIdx.x;
     const int row = blockIdx.x;  // ((b * s_active + i) * n_q_heads + h)
     const int h = row % p.n_q_heads;
@@ -298,56 +314,81 @@ __global__ __launch_bounds__(64) void decode_combine(CombineParams p) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
 
-    float acc[PER], wsum = 0.f;
+    const int r = lane / LPR, c = lane % LPR;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float wsum = 0.f;
+    if (M > -__builtin_inff()) {  // else every split is empty: the row is zeros
+        for (int s0 = 0; s0 < ns; s0 += RPW * U) {
+            float4 x[U];
+            float wt[U];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-    if (M > -__builtin_inff()) {
-        for (int s0 = 0; s0 < ns; s0 += MAXS) {
-            const int cnt = min(MAXS, ns - s0);
-            __syncthreads();
-            for (int s = lane; s < cnt; s += 64) wts[s] = fast_exp2((lse[s0 + s] - M) * kLog2e);
-            __syncthreads();
-            int s = 0;
-            for (; s + 4 <= cnt; s += 4) {  // four independent loads in flight per lane
-                float x[4][PER];
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-#pragma unroll
-                    for (int e = 0; e < PER; ++e) x[u][e] = po[(int64_t)(s0 + s + u) * D + lane + 64 * e];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    wsum += wts[s + u];
-#pragma unroll
-                    for (int e = 0; e < PER; ++e) acc[e] = fmaf(wts[s + u], x[u][e], acc[e]);
-                }
+            for (int u = 0; u < U; ++u) {
+                const int sp = s0 + RPW * u + r;
+                const int sc = min(sp, ns - 1);  // every split below ns was written
+                x[u] = *(const float4*)(po + (int64_t)sc * D + 4 * c);
+                wt[u] = lse[sc];
+                wt[u] = sp < ns ? fast_exp2((wt[u] - M) * kLog2e) : 0.f;
             }
-            for (; s < cnt; ++s) {
-                wsum += wts[s];
 #pragma unroll
-                for (int e = 0; e < PER; ++e) acc[e] = fmaf(wts[s], po[(int64_t)(s0 + s) * D + lane + 64 * e], acc[e]);
+            for (int u = 0; u < U; ++u) {
+                wsum += wt[u];
+                acc.x = fmaf(wt[u], x[u].x, acc.x);
+                acc.y = fmaf(wt[u], x[u].y, acc.y);
+                acc.z = fmaf(wt[u], x[u].z, acc.z);
+                acc.w = fmaf(wt[u], x[u].w, acc.w);
             }
         }
     }
+    // sum over the RPW lane groups (same float4 column, different splits)
+    auto add_other = [&](float v, bool sixteen) {
+        const uint32_t u = __float_as_uint(v);
+        auto sw = sixteen ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                          : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    };
+    if constexpr (RPW >= 2) {
+        acc.x = add_other(acc.x, false); acc.y = add_other(acc.y, false);
+        acc.z = add_other(acc.z, false); acc.w = add_other(acc.w, false);
+        wsum = add_other(wsum, false);
+    }
+    if constexpr (RPW >= 4) {
+        acc.x = add_other(acc.x, true); acc.y = add_other(acc.y, true);
+        acc.z = add_other(acc.z, true); acc.w = add_other(acc.w, true);
+        wsum = add_other(wsum, true);
+    }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    uint16_t* orow = (uint16_t*)p.o + (int64_t)b * p.os.batch + (int64_t)i * p.os.seq + (int64_t)h * p.os.head;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) orow[lane + 64 * e] = f32_to_16<BF16>(acc[e] * inv);
+    if (r == 0) {
+        uint16_t* orow = (uint16_t*)p.o + (int64_t)b * p.os.batch + (int64_t)i * p.os.seq + (int64_t)h * p.os.head;
+        uint2 pk;
+        pk.x = pack2_16<BF16>(acc.x * inv, acc.y * inv);
+        pk.y = pack2_16<BF16>(acc.z * inv, acc.w * inv);
+        *(uint2*)(orow + 4 * c) = pk;
+    }
 }
 
+template <bool BF16, int D, int HW>
+static void launch_decode_hw(const DecodeParams& p, hipStream_t s) {
+    const dim3 grid((unsigned)(p.n_kv_heads / HW), (unsigned)p.max_splits, (unsigned)p.batch), block(64 * HW);
+    if (!p.block_table) hipLaunchKernelGGL((decode_split<BF16, D, kDecodeFlat, HW>), grid, block, 0, s, p);
+    else if (p.page_shift >= 4) hipLaunchKernelGGL((decode_split<BF16, D, kDecodeFast, HW>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((decode_split<BF16, D, kDecodeGeneric, HW>), grid, block, 0, s, p);
+}
+
+// Waves per workgroup: the largest power of two up to dc_max_heads that divides n_kv_heads.
 template <bool BF16, int D>
-static void launch_decode_d(const DecodeParams& p, dim3 grid, hipStream_t s) {
-    if (!p.block_table) hipLaunchKernelGGL((decode_split<BF16, D, kDecodeFlat>), grid, dim3(64), 0, s, p);
-    else if (p.page_shift >= 4) hipLaunchKernelGGL((decode_split<BF16, D, kDecodeFast>), grid, dim3(64), 0, s, p);
-    else hipLaunchKernelGGL((decode_split<BF16, D, kDecodeGeneric>), grid, dim3(64), 0, s, p);
+static void launch_decode_d(const DecodeParams& p, hipStream_t s) {
+    constexpr int MH = dc_max_heads<D>();
+    if (MH >= 4 && p.n_kv_heads % 4 == 0) launch_decode_hw<BF16, D, (MH >= 4 ? 4 : 1)>(p, s);
+    else if (MH >= 2 && p.n_kv_heads % 2 == 0) launch_decode_hw<BF16, D, (MH >= 2 ? 2 : 1)>(p, s);
+    else launch_decode_hw<BF16, D, 1>(p, s);
 }
 
 template <bool BF16>
 static hipError_t launch_decode_t(const DecodeParams& p, int head_dim, hipStream_t s) {
-    const dim3 grid((unsigned)p.n_kv_heads, (unsigned)p.max_splits, (unsigned)p.batch);
     switch (head_dim) {
-        case 64: launch_decode_d<BF16, 64>(p, grid, s); break;
-        case 128: launch_decode_d<BF16, 128>(p, grid, s); break;
-        default: launch_decode_d<BF16, 256>(p, grid, s); break;
+        case 64: launch_decode_d<BF16, 64>(p, s); break;
+        case 128: launch_decode_d<BF16, 128>(p, s); break;
+        default: launch_decode_d<BF16, 256>(p, s); break;
     }
     return hipGetLastError();
 }

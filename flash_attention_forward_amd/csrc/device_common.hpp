@@ -36,10 +36,17 @@ __device__ __forceinline__ void sched_group() {
 
 // Wait until at most N vector-memory operations of this wave are in flight
 // (loads complete in issue order, so this waits for all but the last N).
+// Emitted as the s_waitcnt builtin (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt and lgkmcnt left at their maxima) so that the compiler's own
+// wait insertion knows about it, between two compiler memory barriers.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N <= 63, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    asm volatile("" ::: "memory");
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+#endif
+    asm volatile("" ::: "memory");
 }
 
 // Scheduling fence: the compiler moves no instruction across it.
