@@ -23,7 +23,8 @@
 // output plus the statistics needed to merge it later).
 //
 // decode_combine: per (sequence, query, q-head), M = max_s lse_s,
-// w_s = exp(lse_s - M), O = sum_s w_s O_s / sum_s w_s — the CTE page's
+// w_s = exp(lse_s - M), O = sum_s w_s O_s / sum_s w_s (M kept as a running
+// maximum over rounds of splits, rescaling what was summed before) — the CTE page's
 // cross-section merge (section "Algorithm — running-sum update, reciprocal,
 // output accumulate") over any number of splits.
 #include "device_common.hpp"
@@ -290,14 +291,15 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
 }
 
 // One wave per output row. A split's partial row is read as float4s by
-// D / 4 lanes, so one load instruction covers 64 / (D / 4) splits and up to 16
-// instructions per lane are in flight; the lane groups that took different
-// splits are summed with lane swaps at the end.
+// D / 4 lanes, so one load instruction covers 64 / (D / 4) splits; up to 32
+// instructions per lane are issued together with the matching log-sum-exps,
+// whose maximum is taken while the rows are in flight. The lane groups that
+// took different splits are summed with lane swaps at the end.
 template <bool BF16, int D>
 __global__ __launch_bounds__(64) void decode_combine(CombineParams p) {
     constexpr int LPR = D / 4;      // lanes per split row
     constexpr int RPW = 64 / LPR;   // split rows per load instruction
-    constexpr int U = 16;           // load instructions in flight per lane
+    constexpr int U = 32;           // load instructions per lane and round
     const int lane = threadIdx.x;
     const int row = blockIdx.x;  // ((b * s_active + i) * n_q_heads + h)
     const int h = row % p.n_q_heads;
@@ -308,35 +310,37 @@ __global__ __launch_bounds__(64) void decode_combine(CombineParams p) {
     const float* lse = p.part_lse + (int64_t)row * p.max_splits;
     const float* po = p.part_o + (int64_t)row * p.max_splits * D;
 
-    // M = max_s lse_s, one split per lane, then a wave reduction
-    float M = -__builtin_inff();
-    for (int s = lane; s < ns; s += 64) M = fmaxf(M, lse[s]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-
     const int r = lane / LPR, c = lane % LPR;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float wsum = 0.f;
-    if (M > -__builtin_inff()) {  // else every split is empty: the row is zeros
-        for (int s0 = 0; s0 < ns; s0 += RPW * U) {
-            float4 x[U];
-            float wt[U];
+    float wsum = 0.f, M = -__builtin_inff();
+    for (int s0 = 0; s0 < ns; s0 += RPW * U) {
+        float4 x[U];
+        float ls[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int sp = s0 + RPW * u + r;
-                const int sc = min(sp, ns - 1);  // every split below ns was written
-                x[u] = *(const float4*)(po + (int64_t)sc * D + 4 * c);
-                wt[u] = lse[sc];
-                wt[u] = sp < ns ? fast_exp2((wt[u] - M) * kLog2e) : 0.f;
-            }
+        for (int u = 0; u < U; ++u) {
+            const int sc = min(s0 + RPW * u + r, ns - 1);  // every split below ns was written
+            x[u] = *(const float4*)(po + (int64_t)sc * D + 4 * c);
+            ls[u] = lse[sc];
+        }
+        // running max over the splits seen so far (a repeated clamped split changes nothing)
+        float mr = M;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                wsum += wt[u];
-                acc.x = fmaf(wt[u], x[u].x, acc.x);
-                acc.y = fmaf(wt[u], x[u].y, acc.y);
-                acc.z = fmaf(wt[u], x[u].z, acc.z);
-                acc.w = fmaf(wt[u], x[u].w, acc.w);
-            }
+        for (int u = 0; u < U; ++u) mr = fmaxf(mr, ls[u]);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) mr = fmaxf(mr, __shfl_xor(mr, off));
+        if (mr == -__builtin_inff()) continue;  // every split so far is empty
+        const float alpha = fast_exp2((M - mr) * kLog2e);  // 0 on the first non-empty round
+        M = mr;
+        wsum *= alpha;
+        acc.x *= alpha; acc.y *= alpha; acc.z *= alpha; acc.w *= alpha;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float wt = s0 + RPW * u + r < ns ? fast_exp2((ls[u] - M) * kLog2e) : 0.f;
+            wsum += wt;
+            acc.x = fmaf(wt, x[u].x, acc.x);
+            acc.y = fmaf(wt, x[u].y, acc.y);
+            acc.z = fmaf(wt, x[u].z, acc.z);
+            acc.w = fmaf(wt, x[u].w, acc.w);
         }
     }
     // sum over the RPW lane groups (same float4 column, different splits)
