@@ -98,15 +98,43 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
     const int g = lane >> 4;   // 16-lane group
     const int hk = blockIdx.x * HW + w, split = blockIdx.y, b = blockIdx.z;
 
-    const int len = p.cache_len[b];
     const int t0 = split * p.split_len;
-    if (t0 >= len) return;  // this split is past the cache: nothing is written (uniform in the workgroup)
-    const int t1 = min(len, t0 + p.split_len);
-
     const int nrows = p.group * p.s_active;
     const bool row_real = n < nrows;
     const int qi = row_real ? n / p.group : 0;
     const int qh = hk * p.group + (row_real ? n % p.group : 0);
+
+    // Requested together before anything waits: cache_len[b], this split's
+    // whole slice of the page table (clamped to the table row; entries past
+    // the cache are never used) and the Q fragments.
+    constexpr int PPT = (kDecodeMaxSplitPages + 64 * HW - 1) / (64 * HW);  // page entries per thread
+    uint32_t pe[PPT];
+    const int spp = MODE == kDecodeFlat ? 0 : p.split_len / p.page_size;  // pages per split, <= 256
+    if constexpr (MODE != kDecodeFlat) {
+        const uint32_t* trow = p.block_table + (int64_t)b * p.max_pages_per_seq;
+        const int first = t0 / p.page_size, last = p.max_pages_per_seq - 1;
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int i = (int)threadIdx.x + k * 64 * HW;
+            pe[k] = i < spp && last >= 0 ? trow[min(first + i, last)] : 0u;
+        }
+    }
+    // Q fragments: B operand of S^T = K Q^T (lane: column n, d = 32ks + 8g .. +8).
+    s16x8 qf[NKS];
+    {
+        const uint16_t* qrow = (const uint16_t*)p.q + (int64_t)b * p.qs.batch + (int64_t)qi * p.qs.seq +
+                               (int64_t)qh * p.qs.head + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            uint4 x = make_uint4(0, 0, 0, 0);
+            if (row_real) x = *(const uint4*)(qrow + 32 * ks);
+            x.x ^= p.qflip; x.y ^= p.qflip; x.z ^= p.qflip; x.w ^= p.qflip;
+            qf[ks] = __builtin_bit_cast(s16x8, x);
+        }
+    }
+    const int len = p.cache_len[b];
+    if (t0 >= len) return;  // this split is past the cache: nothing is written (uniform in the workgroup)
+    const int t1 = min(len, t0 + p.split_len);
     const int qpos = len - p.s_active + qi;  // the query sits at the end of its cache
     const int64_t prow = (((int64_t)b * p.s_active + qi) * p.n_q_heads + qh) * p.max_splits + split;
 
@@ -125,26 +153,12 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
     const int tb0 = t0 + ((tlo - t0) / DC_KB) * DC_KB;  // first iteration's key block
     const int nblk = (t1 - tb0 + DC_KB - 1) / DC_KB;
     if constexpr (MODE != kDecodeFlat) {
-        // pages holding tokens [t0, t1); t0 is a multiple of page_size
-        const int first = t0 / p.page_size;
-        const int npg = (t1 - 1) / p.page_size - first + 1;
-        const uint32_t* row = p.block_table + (int64_t)b * p.max_pages_per_seq + first;
-        for (int i = threadIdx.x; i < npg; i += 64 * HW) pages[i] = row[i];
-        __syncthreads();  // the only workgroup barrier: every early return above is uniform
-    }
-
-    // Q fragments: B operand of S^T = K Q^T (lane: column n, d = 32ks + 8g .. +8).
-    s16x8 qf[NKS];
-    {
-        const uint16_t* qrow = (const uint16_t*)p.q + (int64_t)b * p.qs.batch + (int64_t)qi * p.qs.seq +
-                               (int64_t)qh * p.qs.head + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (row_real) x = *(const uint4*)(qrow + 32 * ks);
-            x.x ^= p.qflip; x.y ^= p.qflip; x.z ^= p.qflip; x.w ^= p.qflip;
-            qf[ks] = __builtin_bit_cast(s16x8, x);
+        for (int k = 0; k < PPT; ++k) {
+            const int i = (int)threadIdx.x + k * 64 * HW;
+            if (i < spp) pages[i] = pe[k];
         }
+        __syncthreads();  // the only workgroup barrier: every early return above is uniform
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // from here on vmcnt counts K/V block loads only
 
