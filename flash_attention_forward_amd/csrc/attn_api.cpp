@@ -7,7 +7,7 @@
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/attn.h"
+#include "attn.h"
 #include "kernels.hpp"
 
 namespace {

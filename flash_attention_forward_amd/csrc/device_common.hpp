@@ -49,12 +49,35 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("" ::: "memory");
 }
 
+// Workgroup barrier for LDS tiles filled by direct-to-LDS loads. Unlike
+// __syncthreads(), whose release fence makes the compiler wait for every
+// outstanding load that writes LDS (vmcnt(0)) and so drains all prefetches at
+// each barrier, this waits only for this wave's own LDS instructions
+// (lgkmcnt(0): its reads are done before others overwrite the data, its
+// writes are visible after the barrier); the caller waits for exactly the
+// direct loads the barrier publishes (wait_vmcnt). The compiler memory
+// barriers keep LDS accesses on their side of it.
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("" ::: "memory");
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt at their maxima
+    __builtin_amdgcn_s_barrier();
+#endif
+    asm volatile("" ::: "memory");
+}
+
 // Scheduling fence: the compiler moves no instruction across it.
 __device__ __forceinline__ void sched_fence() {
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_sched_barrier(0);
 #endif
 }
+
+// max(max(a, b), c): with NaNs ignored (-fno-honor-nans) the compiler emits
+// one v_max3_f32 per call when the calls are chained through the first
+// argument. (Not inline asm: the compiler must see these reads, because they
+// often consume MFMA results and need its hazard wait states.)
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // Value of lane (l ^ 32) for every lane l, with one v_permlane32_swap.
 __device__ __forceinline__ float max_with_other_half(float x) {

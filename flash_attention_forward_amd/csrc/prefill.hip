@@ -39,9 +39,8 @@ struct BoolC {
     static constexpr bool value = B;
 };
 
-constexpr int PF_BM = 128;  // query rows per workgroup
+constexpr int PF_ROWS_PER_WAVE = 32;  // query rows per wave
 constexpr int PF_BN = 64;   // keys per tile
-constexpr int PF_THREADS = 256;
 
 // LDS layout of the K and V tiles: row-major, 16-byte chunk c of row r stored
 // at chunk c ^ f(r). Tiles are filled with direct-to-LDS loads (each 1 KB load
@@ -57,11 +56,17 @@ __device__ __forceinline__ int pf_vswz(int row) {
     return D == 64 ? 4 * ((row >> 1) & 1) : 4 * (row & 3);
 }
 
-template <bool BF16, int D, int MASK>
-__global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(PrefillParams p) {
+// NW waves per workgroup: 4 (two workgroups per CU for D <= 128) or 8 (one
+// workgroup per CU, twice the query rows per K/V tile: half the L2-to-LDS
+// traffic per FLOP).
+template <bool BF16, int D, int MASK, int NW>
+__global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefill_mfma(PrefillParams p) {
+    constexpr int PF_BM = PF_ROWS_PER_WAVE * NW;  // query rows per workgroup
+    constexpr int PF_THREADS = 64 * NW;
     constexpr int CPR = D / 8;              // 16-byte chunks per row
     constexpr int TILE = PF_BN * D;         // elements of one K or V tile
-    constexpr int LPW = TILE / 512 / 4;     // 1 KB direct loads per wave per tile
+    constexpr int LPW = TILE / 512 / NW;    // 1 KB direct loads per wave per tile
+    static_assert(LPW >= 1, "every wave loads part of each tile");
     constexpr int NDT = D / 32;             // 32-wide d tiles of O^T
     // Two K and two V tiles, separate objects so waits on one buffer's refill
     // never cover reads of the other.
@@ -169,6 +174,34 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
     };
     auto load_k_tile = [&](uint16_t* dst, int j) __attribute__((always_inline)) { load_tile_impl(dst, kbase, p.ks.seq, j, kl, kx, true); };
     auto load_v_tile = [&](uint16_t* dst, int j) __attribute__((always_inline)) { load_tile_impl(dst, vbase, p.vs.seq, j, vl, vx, false); };
+    // In-loop loads: one direct load at a time, so that they can be spread
+    // over the MFMA stages. Tiles past the first one lie above kv_lo, so only
+    // their end can leave the visible range; the descriptor's record count
+    // stops at the end of row key_max and the range check drops the rows past
+    // it (their LDS rows keep zeros or an earlier tile's finite rows, which
+    // are masked). Each load's row offset is in its own lane offset register
+    // (computed once), so the range check covers the whole offset.
+    uint32_t kvo[LPW], vvo[LPW];
+#pragma unroll
+    for (int ii = 0; ii < LPW; ++ii) {
+        const int i = w * LPW + ii;
+        const uint32_t uk = D == 64 ? (4 * i) & 7 : (D == 128 ? (4 * i) & 15 : (2 * i) & 15);
+        const uint32_t uv = D <= 128 ? 0 : 4 * ((2 * i) & 3);
+        uint32_t ko = kl + (kx ^ (16u * uk)) + (uint32_t)(2 * RPL * i) * (uint32_t)p.ks.seq;
+        uint32_t vo = vl + (vx ^ (16u * uv)) + (uint32_t)(2 * RPL * i) * (uint32_t)p.vs.seq;
+        asm volatile("" : "+v"(ko), "+v"(vo));
+        kvo[ii] = ko;
+        vvo[ii] = vo;
+    }
+    auto tile_rsrc = [&](const uint16_t* base, int64_t seq, int j) __attribute__((always_inline)) {
+        const int kv0 = j * PF_BN;
+        const int nrec = kv0 + PF_BN - 1 <= key_max ? 0x7fffffff : 2 * ((key_max - kv0) * (int)seq + D);
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kv0 * seq), (short)0, nrec, 0x00020000);
+    };
+    auto load_part = [&](uint16_t* dst, __amdgpu_buffer_rsrc_t rs, uint32_t voff, int ii) __attribute__((always_inline)) {
+        const int i = w * LPW + ii;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 512 * i), 16, voff, 0, 0, 0);
+    };
 
     // Running max in scaled log2 units. It only moves when a row's tile max
     // exceeds it by more than kLazyRescale, so O and l are rescaled rarely;
@@ -203,9 +236,12 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
     // fragment of d tile dt sits at vfrag ^ 64dt plus a row offset that is a
     // compile-time constant (vswz depends on the row only through row % 4 for
     // D >= 128 and (row / 2) % 2 for D = 64, which the u and +8 row steps
-    // leave unchanged). One register per tensor; the per-fragment XOR is
-    // redone at each use from an opaque copy, so the compiler keeps no
-    // per-fragment addresses live across the loop.
+    // leave unchanged). For D <= 128 every fragment offset is computed once
+    // and kept in its own register (made opaque so the compiler cannot
+    // recompute it in the loop); the buffer and row steps are constants
+    // folded into the LDS instructions' offset fields. For D = 256 (twice as
+    // many fragments and no spare VGPRs) the XOR is redone at each use from
+    // one opaque register per tensor.
     const uint32_t kfrag = (uint32_t)(l32 * D * 2) | (16u * (uint32_t)(hf ^ pf_kswz<D>(l32)));
     const int vr0 = 4 * hf + (r16 >> 2);                  // V^T row of this lane in chunk 0
     const int vcl = 2 * (g & 1) + ((r16 & 3) >> 1);       // chunk within a 32-wide d tile
@@ -217,6 +253,15 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
     auto lds_frag8 = [](const uint16_t* base, uint32_t byte_off) __attribute__((always_inline)) {
         return *(const s16x8*)((const char*)base + byte_off);
     };
+    constexpr int NS = D / 16;          // K chunks of 16 along d
+    constexpr bool PRE = D <= 128;      // per-fragment offset registers
+    uint32_t koff[PRE ? NS : 1], voff[PRE ? NDT : 1];
+    if constexpr (PRE) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) koff[s] = opaque(kfrag ^ (32u * s));
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) voff[dt] = opaque(vfrag ^ (64u * dt));
+    }
 
     // S^T of one 64-key tile: two 32-key blocks x 32 queries; lane holds keys
     // 32t + 8(r/4) + 4hf + r%4 of its query row in register r of block t.
@@ -248,7 +293,7 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
     auto max_tile = [&](const f32x16& s0, const f32x16& s1) __attribute__((always_inline)) {
         float mx = kMaskedScore;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+        for (int r = 0; r < 16; ++r) mx = max3f(mx, s0[r], s1[r]);
         return max_with_other_half(mx);
     };
     // Move m (and rescale O and l) for rows whose tile max passed m + margin.
@@ -266,98 +311,67 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
             for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
         }
     };
-    // P of one 32-key block as packed 16-bit pairs: pk[j/2] holds keys j, j+1
-    // of the block's register order. Chunk u of the tile (keys 16u..16u+15)
-    // is pk[4u .. 4u+3] when pk spans both blocks; slot j of lane half hf is
-    // key 16u + 8(j/4) + 4hf + j%4, the B-operand layout of O^T += V^T P^T.
-    // A masked score gives exactly 0.
-    auto probs_half = [&](const f32x16& sacc, uint32_t* pk) __attribute__((always_inline)) {
-        const float neg_m = -m_i;
-#pragma unroll
-        for (int jj = 0; jj < 16; jj += 2) {
-            const float p0 = fast_exp2(fmaf(sacc[jj], p.c, neg_m));
-            const float p1 = fast_exp2(fmaf(sacc[jj + 1], p.c, neg_m));
-            pk[jj / 2] = pack2_16<BF16>(p0, p1);
-        }
-    };
-    // Sum of the rounded P of a tile (the same values the P V product uses).
-    auto psum_tile = [&](const uint32_t* pk) __attribute__((always_inline)) {
-        float ps = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ps = dot2_16<BF16>(pk[i], one2, ps);
-        return ps;
-    };
-    // O^T[d, q] += V^T[d, keys] P^T[keys, q] for the whole tile. A operand via
-    // transpose reads: lane r16 of group g points at row 16u + 4hf + r16/4
-    // (and +8), column 32dt + 16(g%2) + 4(r16%4), and receives column
-    // 32dt + 16(g%2) + r16 of four consecutive key rows.
-    auto pv_tile = [&](const uint32_t* pk, const uint16_t* Vt) __attribute__((always_inline)) {
-        const uint32_t vf = opaque(vfrag);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const s16x8 pb = __builtin_bit_cast(s16x8, make_uint4(pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]));
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const char* vb = (const char*)Vt + (vf ^ (64u * dt));
-                const s16x4 lo = lds_read_tr16((const uint16_t*)(vb + 2 * D * (16 * u)));
-                const s16x4 hi4 = lds_read_tr16((const uint16_t*)(vb + 2 * D * (16 * u + 8)));
-                o[dt] = mfma32x32x16<BF16>(concat4(lo, hi4), pb, o[dt]);
-            }
-        }
-    };
 
     // Software pipeline over key tiles, two tiles of scores in registers:
-    // step j runs the QK MFMAs of tile j+1 while the VALU turns the scores of
-    // tile j into probabilities (with the m settled at the end of step j-1),
-    // then the P V MFMAs of tile j, and finally takes the row max of tile j+1
-    // and settles m for it (rescaling O, which by then includes tile j). K(j+1) and V(j) are read in step j; K(j+2) and V(j+1)
-    // are loaded meanwhile into the buffers that held K(j) and V(j-1).
+    // step j runs the QK MFMAs of tile j+1 while the VALU turns three quarters
+    // of the scores of tile j into probabilities (with the m settled at the
+    // end of step j-1), then the P V MFMAs of tile j, ordered by key chunk,
+    // while the VALU finishes the last quarter (used by the last chunk's
+    // MFMAs) and takes the raw row max of tile j+1; then it sums P(j) and
+    // settles m for tile j+1 (rescaling O, which by then includes tile j).
+    // The split keeps the VALU work of each half within what runs beside
+    // its MFMAs, whichever half the other wave of the SIMD is in.
     //
     // Every step runs the same code. A tile that is not fully visible to all
     // rows of the wave gets its hidden scores replaced by the mask value, whose
     // probability is exactly 0 and which never moves m (the host keeps
     // p.c >= 1e-8, so mask * c lies far below the initial m); this covers the
     // diagonal and window-edge tiles, the ragged end of K, tiles past the
-    // wave's last visible key, and the tile after the last one (read from a
-    // stale or unfilled buffer and never used).
+    // wave's last visible key, and the tile after the last one (a repeat of
+    // the last tile, never used).
     // The step body is laid out by hand in stages separated by scheduling
     // fences: stage s of the QK part issues the two MFMAs of K chunk s, the
-    // LDS reads of chunk s+2 and 1/NS of the probabilities; stage i of the
-    // P V part issues MFMA i, the transpose reads of MFMA i+4, one row-sum
-    // dot2 and part of the raw row max of tile j+1. LDS reads thus run two
-    // stages (at least 128 MFMA cycles) ahead of their use.
+    // LDS reads of chunk s+2 and its share of the probabilities; stage i of
+    // the P V part issues MFMA i, the transpose reads of MFMA i+4 and its
+    // share of the remaining probabilities and of the raw row max of tile
+    // j+1. LDS reads thus run two stages (at least 128 MFMA cycles) ahead of
+    // their use. The row sums of P(j) (v_dot2c, which stalls when mixed with
+    // MFMAs) come after the last MFMA, in two independent chains.
     //
     // Loads and barriers: step j issues V(j+1) at its start (into the buffer
     // of V(j-1)) and K(j+3) after a mid-step barrier that follows the QK part
     // (into the buffer of K(j+1), which that part has just read). The
     // mid-step barrier also publishes V(j), the end-of-step barrier K(j+2):
-    // every tile has about one and a half steps to arrive. Loads complete in
-    // issue order (V(j), K(j+2), V(j+1), K(j+3), ...), so each barrier waits
-    // with vmcnt = the loads issued after the one it needs.
-    constexpr int NS = D / 16;          // K chunks of 16 along d
+    // every tile has about one and a half steps to arrive. Tile indices past
+    // the last tile are clamped to it, so every step issues the same loads
+    // and each wait is a fixed count: loads complete in issue order (V(j),
+    // K(j+2), V(j+1), K(j+3), ...), and each barrier waits with vmcnt = the
+    // loads issued after the one it needs.
     constexpr int NPV = 4 * NDT;        // P V MFMAs per tile
     constexpr int VPRE = 4;             // P V MFMAs whose fragments are in flight
+    constexpr int PQ = 12;              // probability pairs (of 16) made in the QK part
+    constexpr int NPV_EARLY = NPV - NDT;  // P V MFMAs before the last key chunk's
     static_assert(NS >= 4, "the V prefetch is issued in the last two QK stages");
-    auto wait_tiles = [&](int n_after) __attribute__((always_inline)) {
-        if (n_after >= 2) wait_vmcnt<2 * LPW>();
-        else if (n_after == 1) wait_vmcnt<LPW>();
-        else wait_vmcnt<0>();
-    };
+    const int j_last = j_end - 1;
     auto step = [&](int j, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1, uint16_t* Kn, uint16_t* Vc,
                     uint16_t* Vl) __attribute__((always_inline)) {
-        if (j + 1 < j_end) load_v_tile(Vl, j + 1);
-        const uint32_t kf = opaque(kfrag);
-        const uint32_t vf = opaque(vfrag);
+        const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(vbase, p.vs.seq, min(j + 1, j_last));
+        const uint32_t kf = PRE ? 0u : opaque(kfrag);
+        const uint32_t vf = PRE ? 0u : opaque(vfrag);
         s16x8 ka[NS][2];
         s16x8 vb[NPV];
         uint32_t pk[16];
         auto kread = [&](int s) __attribute__((always_inline)) {
-            ka[s][0] = lds_frag8(Kn, kf ^ (32u * s));
-            ka[s][1] = lds_frag8(Kn + 32 * D, kf ^ (32u * s));
+            uint32_t off;
+            if constexpr (PRE) off = koff[s]; else off = kf ^ (32u * s);
+            ka[s][0] = lds_frag8(Kn, off);
+            ka[s][1] = lds_frag8(Kn + 32 * D, off);
         };
         auto vread = [&](int i) __attribute__((always_inline)) {
             const int u = i / NDT, dt = i % NDT;
-            const char* vb0 = (const char*)Vc + (vf ^ (64u * dt));
+            uint32_t off;
+            if constexpr (PRE) off = voff[dt]; else off = vf ^ (64u * dt);
+            const char* vb0 = (const char*)Vc + off;
             vb[i] = concat4(lds_read_tr16((const uint16_t*)(vb0 + 2 * D * (16 * u))),
                             lds_read_tr16((const uint16_t*)(vb0 + 2 * D * (16 * u + 8))));
         };
@@ -367,7 +381,7 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
             const f32x16& sc = i < 8 ? c0 : c1;
             const int r = 2 * (i % 8);
             pk[i] = pack2_16<BF16>(fast_exp2(fmaf(sc[r], p.c, neg_m)), fast_exp2(fmaf(sc[r + 1], p.c, neg_m)));
-            asm volatile("" ::"v"(pk[i]));  // computed here, not sunk below the mid-step barrier
+            asm volatile("" ::"v"(pk[i]));  // computed here, not sunk into a later stage
         };
         kread(0);
         kread(1);
@@ -378,33 +392,42 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
         for (int s = 0; s < NS; ++s) {
             n0 = mfma32x32x16<BF16>(ka[s][0], qf[s], n0);
             n1 = mfma32x32x16<BF16>(ka[s][1], qf[s], n1);
+            if (s % (NS / LPW) == 0) load_part(Vl, vrs, vvo[s / (NS / LPW)], s / (NS / LPW));
             if (s + 2 < NS) kread(s + 2);
 #pragma unroll
-            for (int i = s * 16 / NS; i < (s + 1) * 16 / NS; ++i) prob_pair(i);
+            for (int i = s * PQ / NS; i < (s + 1) * PQ / NS; ++i) prob_pair(i);
             sched_fence();
         }
         // V(j) in; every wave is past its reads of K(j+1).
-        wait_tiles((j + 2 < j_end) + (j + 1 < j_end));
-        __syncthreads();
-        if (j + 3 < j_end) load_k_tile(Kn, j + 3);
+        wait_vmcnt<2 * LPW>();
+        barrier_lds();
+        const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kbase, p.ks.seq, min(j + 3, j_last));
 #pragma unroll
         for (int i = 0; i < VPRE; ++i) vread(i);
         sched_fence();
-        float ps = 0.f, mx = kMaskedScore;
+        float mx = kMaskedScore;
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
             const int u = i / NDT, dt = i % NDT;
             const s16x8 pb = __builtin_bit_cast(s16x8, make_uint4(pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]));
             o[dt] = mfma32x32x16<BF16>(vb[i], pb, o[dt]);
+            if (i % (NPV / LPW) == 0) load_part(Kn, krs, kvo[i / (NPV / LPW)], i / (NPV / LPW));
             if (i + VPRE < NPV) vread(i + VPRE);
+            if (i < NPV_EARLY) {
 #pragma unroll
-            for (int e = i * 16 / NPV; e < (i + 1) * 16 / NPV; ++e) {
-                ps = dot2_16<BF16>(pk[e], one2, ps);
-                mx = fmaxf(mx, fmaxf(n0[e], n1[e]));
+                for (int e = PQ + i * (16 - PQ) / NPV_EARLY; e < PQ + (i + 1) * (16 - PQ) / NPV_EARLY; ++e) prob_pair(e);
             }
+#pragma unroll
+            for (int e = i * 16 / NPV; e < (i + 1) * 16 / NPV; ++e) mx = max3f(mx, n0[e], n1[e]);
             sched_fence();
         }
-        l_i += ps;
+        float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+            ps0 = dot2_16<BF16>(pk[e], one2, ps0);
+            ps1 = dot2_16<BF16>(pk[e + 1], one2, ps1);
+        }
+        l_i += ps0 + ps1;
         mx = max_with_other_half(mx);
         if (!(wave_live && tile_full(j + 1))) {
             mask_half(n0, (j + 1) * PF_BN, 0);
@@ -413,8 +436,8 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
         }
         rescale(mx);
         // K(j+2) in; every wave is past its reads of V(j).
-        wait_tiles((j + 1 < j_end) + (j + 3 < j_end));
-        __syncthreads();
+        wait_vmcnt<2 * LPW>();
+        barrier_lds();
     };
 
     // Prologue: K(j_begin), V(j_begin), K(j_begin + 1) in, S(j_begin) and its
@@ -422,9 +445,12 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
     f32x16 sa0, sa1, sb0, sb1;
     const int nt = j_end - j_begin;
     if (nt > 0) {
+        // The first refill of Vs1 may be range-limited: start it from zeros.
+#pragma unroll
+        for (int c = tid; c < TILE / 8; c += PF_THREADS) *(uint4*)(Vs1 + 8 * c) = make_uint4(0, 0, 0, 0);
         load_k_tile(Ks0, j_begin);
         load_v_tile(Vs0, j_begin);
-        if (nt > 1) load_k_tile(Ks1, j_begin + 1);
+        load_k_tile(Ks1, min(j_begin + 1, j_last));
         wait_vmcnt<0>();
         __syncthreads();
         qk_tile(sa0, sa1, Ks0);
@@ -434,7 +460,7 @@ __global__ __launch_bounds__(PF_THREADS, (D >= 256 ? 1 : 2)) void prefill_mfma(P
         }
         rescale(max_tile(sa0, sa1));
         __syncthreads();  // every wave is past its reads of K(j_begin)
-        if (nt > 2) load_k_tile(Ks0, j_begin + 2);
+        load_k_tile(Ks0, min(j_begin + 2, j_last));
     }
     // Step r = j - j_begin: K(j+1) sits in buffer (r+1)%2, V(j) in buffer r%2.
     // Unrolled by two so that every LDS access names its buffer (the compiler
@@ -565,16 +591,31 @@ __global__ __launch_bounds__(256) void prefill_f32(PrefillParams p) {
 }
 
 // ---------------------------------------------------------------------------- dispatch
-template <bool BF16, int D>
-static hipError_t launch_mfma_mask(PrefillParams p, int mask, hipStream_t s) {
-    p.n_q_tiles = (p.seqlen_q + PF_BM - 1) / PF_BM;
-    const dim3 grid((unsigned)p.n_q_tiles * p.batch * p.n_q_heads);
+template <bool BF16, int D, int NW>
+static hipError_t launch_mfma_nw(PrefillParams p, int mask, hipStream_t s) {
+    p.n_q_tiles = (p.seqlen_q + PF_ROWS_PER_WAVE * NW - 1) / (PF_ROWS_PER_WAVE * NW);
+    const dim3 grid((unsigned)p.n_q_tiles * p.batch * p.n_q_heads), block(64 * NW);
     switch (mask) {
-        case kMaskNone: hipLaunchKernelGGL((prefill_mfma<BF16, D, kMaskNone>), grid, dim3(PF_THREADS), 0, s, p); break;
-        case kMaskCausal: hipLaunchKernelGGL((prefill_mfma<BF16, D, kMaskCausal>), grid, dim3(PF_THREADS), 0, s, p); break;
-        default: hipLaunchKernelGGL((prefill_mfma<BF16, D, kMaskCausalWindow>), grid, dim3(PF_THREADS), 0, s, p); break;
+        case kMaskNone: hipLaunchKernelGGL((prefill_mfma<BF16, D, kMaskNone, NW>), grid, block, 0, s, p); break;
+        case kMaskCausal: hipLaunchKernelGGL((prefill_mfma<BF16, D, kMaskCausal, NW>), grid, block, 0, s, p); break;
+        default: hipLaunchKernelGGL((prefill_mfma<BF16, D, kMaskCausalWindow, NW>), grid, block, 0, s, p); break;
     }
     return hipGetLastError();
+}
+
+// Eight-wave workgroups halve the K/V traffic per FLOP but hold a whole CU
+// each; they are used for D <= 128 when there are enough of them to fill the
+// chip at least twice over (D = 256 needs more than half a SIMD's registers
+// per wave, so it stays at four waves).
+constexpr int kPrefillWideMinWorkgroups = 512;
+
+template <bool BF16, int D>
+static hipError_t launch_mfma_mask(PrefillParams p, int mask, hipStream_t s) {
+    if constexpr (D <= 128) {
+        const long wide = (long)((p.seqlen_q + 255) / 256) * p.batch * p.n_q_heads;
+        if (wide >= kPrefillWideMinWorkgroups) return launch_mfma_nw<BF16, D, 8>(p, mask, s);
+    }
+    return launch_mfma_nw<BF16, D, 4>(p, mask, s);
 }
 
 template <int D>

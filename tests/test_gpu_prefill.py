@@ -29,6 +29,11 @@ SMALL = {
     "bf16_window1": W.PrefillSpec(1, 2, 1, 140, 140, 64, "bf16", causal=True, window=1),
     "bf16_single_row": W.PrefillSpec(1, 8, 1, 1, 1, 128, "bf16", causal=True),
     "f16_mqa_long_window": W.PrefillSpec(1, 8, 1, 520, 520, 128, "f16", causal=True, window=512),
+    # enough 256-row query tiles (>= 512 workgroups) for the eight-wave launch
+    "wide_bf16_causal_ragged": W.PrefillSpec(32, 8, 2, 300, 300, 128, "bf16", causal=True),
+    "wide_f16_d64_window": W.PrefillSpec(32, 8, 4, 290, 290, 64, "f16", causal=True, window=100),
+    "wide_bf16_nocausal_sq_lt_skv": W.PrefillSpec(128, 4, 1, 200, 330, 128, "bf16", causal=False),
+    "wide_bf16_sq_lt_skv_window": W.PrefillSpec(64, 8, 8, 130, 400, 128, "bf16", causal=True, window=90),
 }
 
 
