@@ -34,6 +34,7 @@ PREFILL = "c3_bf16_causal_32k"
 DECODE = "c5_paged_decode"
 CONTEXT = "c2_f16_gqa_causal_2k"  # the 7B-shaped 2K prefill the minfer page times
 PAGES_CONTEXT_MS_PER_LAYER = 8.5   # minfer 8n page, results: 7B @2K prefill attention, on its own (NVIDIA) GPU
+DEFAULT_SPLIT_LEN = 1024  # decode keys per split (timed sweep: 512 and 2048 are slower on the paged workload)
 
 
 def visible_pairs(spec) -> int:
@@ -138,7 +139,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--split-len", type=int, default=512)
+    ap.add_argument("--split-len", type=int, default=DEFAULT_SPLIT_LEN)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()

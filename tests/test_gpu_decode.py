@@ -74,7 +74,9 @@ def test_decode_full_size_sampled():
     name = "c5_paged_decode"
     inp = W.make_decode(C5, W.WORKLOAD_SEEDS[name])
     say("decode full size", int(inp.cache_len.sum()))
-    got = gpu_decode(inp, split_len=512)
+    import bench
+
+    got = gpu_decode(inp, split_len=bench.DEFAULT_SPLIT_LEN)
     order = np.argsort(inp.cache_len)
     batches = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 3, 17})
     ref = oracle_decode(inp, batches=batches)
