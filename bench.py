@@ -184,6 +184,17 @@ def main():
     ws = F.DecodeWorkspace(dspec.batch, dspec.s_active, dspec.n_q_heads, dspec.head_dim, ms, dev)
     do = torch.empty_like(dq)
 
+    # the same caches read by four query tokens per sequence (speculative decode),
+    # and through a flat [batch, max_len, Hkv, D] copy instead of the page table
+    rng = np.random.default_rng(W.WORKLOAD_SEEDS[DECODE] + 100)
+    dq4 = W.to_torch(W.round_to(rng.standard_normal((dspec.batch, 4, dspec.n_q_heads, dspec.head_dim),
+                                                    dtype=np.float32), dspec.dtype), dspec.dtype, dev)
+    ws4 = F.DecodeWorkspace(dspec.batch, 4, dspec.n_q_heads, dspec.head_dim, ms, dev)
+    do4 = torch.empty_like(dq4)
+    btl = bt.long()
+    kflat = kc[btl].reshape(dspec.batch, max_len, dspec.n_kv_heads, dspec.head_dim)
+    vflat = vc[btl].reshape(dspec.batch, max_len, dspec.n_kv_heads, dspec.head_dim)
+
     cspec = W.WORKLOADS[CONTEXT]
     cin = W.make_prefill(cspec, W.WORKLOAD_SEEDS[CONTEXT])
     cq, ck, cv = (W.to_torch(a, cspec.dtype, dev) for a in (cin.q, cin.k, cin.v))
@@ -235,6 +246,22 @@ def main():
         e[1].record(stream)
     torch.cuda.synchronize()
     ctx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in cev]))
+
+    def time_decode(qq, kk, vv, table, w, out, reps=20):
+        for _ in range(3):
+            F.attn_decode_fwd(qq, kk, vv, cl, w.part_o, w.part_lse, args.split_len, ms, dspec.scale_f32, table)
+            F.attn_decode_combine(w.part_o, w.part_lse, cl, args.split_len, ms, out)
+        evv = [[ev(), ev()] for _ in range(reps)]
+        for e in evv:
+            e[0].record(stream)
+            F.attn_decode_fwd(qq, kk, vv, cl, w.part_o, w.part_lse, args.split_len, ms, dspec.scale_f32, table)
+            F.attn_decode_combine(w.part_o, w.part_lse, cl, args.split_len, ms, out)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in evv]))
+
+    spec_us = time_decode(dq4, kc, vc, bt, ws4, do4) * 1e3
+    flat_us = time_decode(dq, kflat, vflat, None, ws, torch.empty_like(dq)) * 1e3
 
     flops = prefill_flops(pspec)
     kv_bytes = decode_kv_bytes(din)
@@ -292,6 +319,13 @@ def main():
             "tflops": round(prefill_flops(cspec) / (ctx_ms * 1e-3) / 1e12, 2),
             "pages_ms_per_layer": PAGES_CONTEXT_MS_PER_LAYER,
             "pages_hardware": "unnamed NVIDIA GPU (minfer 8n page); context only",
+        },
+        "decode_variants": {
+            "speculative_s_active4_us": round(spec_us, 2),
+            "speculative_s_active4_gbps": round(kv_bytes / (spec_us * 1e-6) / 1e9, 1),
+            "flat_cache_us": round(flat_us, 2),
+            "flat_cache_gbps": round(kv_bytes / (flat_us * 1e-6) / 1e9, 1),
+            "note": "split + combine over the same caches: 4 query tokens per sequence, and a flat cache copy",
         },
         "kernel_source_digest": kernel_source_digest(),
     }

@@ -53,7 +53,7 @@ def _load():
         p = ctypes.c_void_p
         i64 = ctypes.c_int64
         lib.oracle_attention_rows.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64,
-                                              ctypes.c_double, ctypes.c_int, i64, p, i64, p, p]
+                                              ctypes.c_double, ctypes.c_int, i64, p, p, i64, p, p]
         lib.oracle_attention_rows.restype = ctypes.c_int
         lib.oracle_visible_mask.argtypes = [i64, i64, ctypes.c_int, i64, p]
         lib.oracle_visible_mask.restype = None
@@ -81,11 +81,12 @@ def visible_mask(Sq: int, Skv: int, causal: bool, window: int = 0) -> np.ndarray
     return m.astype(bool)
 
 
-def attention_rows(q, k, v, scale: float, causal: bool, window: int, rows):
+def attention_rows(q, k, v, scale: float, causal: bool, window: int, rows, sinks=None):
     """Oracle output for selected rows.
 
     q: float64 [B, Sq, Hq, D]; k, v: float64 [B, Skv, Hkv, D] (views allowed,
-    head_dim contiguous). rows: int array [n, 3] of (b, i, h).
+    head_dim contiguous). rows: int array [n, 3] of (b, i, h). sinks: None or
+    [Hq] sink logits (scaled-score units; see attn_oracle.c).
     Returns (o [n, D] float64, lse [n] float64, natural log).
     """
     lib = _load()
@@ -97,9 +98,13 @@ def attention_rows(q, k, v, scale: float, causal: bool, window: int, rows):
     o = np.zeros((n, D), dtype=np.float64)
     lse = np.zeros(n, dtype=np.float64)
     qs, ks, vs = _strides3(q), _strides3(k), _strides3(v)
+    sk = None
+    if sinks is not None:
+        sk = np.ascontiguousarray(sinks, dtype=np.float64).reshape(-1)
+        assert sk.shape[0] == Hq
     rc = lib.oracle_attention_rows(_ptr(q), _ptr(qs), _ptr(k), _ptr(ks), _ptr(v), _ptr(vs),
                                    Hq, Hkv, Sq, Skv, D, float(scale), int(bool(causal)), int(window),
-                                   _ptr(rows), n, _ptr(o), _ptr(lse))
+                                   _ptr(sk) if sk is not None else None, _ptr(rows), n, _ptr(o), _ptr(lse))
     if rc != 0:
         raise ValueError("oracle_attention_rows rejected its arguments")
     return o, lse
@@ -110,10 +115,11 @@ def all_rows(B: int, Sq: int, Hq: int) -> np.ndarray:
     return np.stack([b.ravel(), i.ravel(), h.ravel()], axis=1)
 
 
-def attention(q, k, v, scale: float, causal: bool = False, window: int = 0, return_lse: bool = False):
+def attention(q, k, v, scale: float, causal: bool = False, window: int = 0, return_lse: bool = False,
+              sinks=None):
     """Full oracle output [B, Sq, Hq, D] (and lse [B, Sq, Hq])."""
     B, Sq, Hq, D = q.shape
-    o, lse = attention_rows(q, k, v, scale, causal, window, all_rows(B, Sq, Hq))
+    o, lse = attention_rows(q, k, v, scale, causal, window, all_rows(B, Sq, Hq), sinks)
     o = o.reshape(B, Sq, Hq, D)
     lse = lse.reshape(B, Sq, Hq)
     return (o, lse) if return_lse else o
@@ -128,13 +134,14 @@ def gather_paged(pool: np.ndarray, block_table_row: np.ndarray, length: int) -> 
 
 
 def decode(q, k_pool, v_pool, block_table, cache_len, scale: float, window: int = 0,
-           batches=None, to_f64=None, return_lse: bool = False):
+           batches=None, to_f64=None, return_lse: bool = False, sinks=None):
     """Oracle paged decode.
 
     q: float64 [B, s_active, Hq, D]; pools: [num_pages, page_size, Hkv, D]
     (float64, or any storage array with ``to_f64`` converting a gathered
     slice exactly); block_table: uint32 [B, max_pages]; cache_len: int [B]
-    (counts the s_active current tokens). Returns o [len(batches), s_active, Hq, D].
+    (counts the s_active current tokens); sinks: None or [Hq] sink logits.
+    Returns o [len(batches), s_active, Hq, D] (and lse [len(batches), s_active, Hq]).
     """
     B, sa, Hq, D = q.shape
     batches = range(B) if batches is None else batches
@@ -145,7 +152,8 @@ def decode(q, k_pool, v_pool, block_table, cache_len, scale: float, window: int 
         kb = conv(gather_paged(k_pool, block_table[b], L))[None]
         vb = conv(gather_paged(v_pool, block_table[b], L))[None]
         o, lse = attention(np.ascontiguousarray(q[b : b + 1]), np.ascontiguousarray(kb),
-                           np.ascontiguousarray(vb), scale, causal=True, window=window, return_lse=True)
+                           np.ascontiguousarray(vb), scale, causal=True, window=window, return_lse=True,
+                           sinks=sinks)
         outs.append(o[0])
         lses.append(lse[0])
     o = np.stack(outs) if outs else np.zeros((0, sa, Hq, D))

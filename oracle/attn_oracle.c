@@ -27,9 +27,21 @@
  *            "The single-query decode attention"; scale applied to the
  *            scores: CTE page, section "Scale")
  *
- * A row with no visible key gets o = 0 and lse = -inf (the convention of
- * the minfer "8n" page, section 3.2, epilogue: an all-masked row is zero). Masked keys are
- * skipped, never multiplied by zero, so NaN in masked K/V cannot leak.
+ * Attention sink (optional, one logit sink[h] per q-head, in the units of the
+ * scaled scores): it joins the softmax as one more logit that has no value
+ * row, so it enters the max and the sum but not the weighted sum of V
+ * ("Flash-Attention: Context (CTE)": the sink logit appended as an extra
+ * column of the section max and its exp appended to the sums; one sink per
+ * q-head, broadcast over the batch, on the decode page):
+ *   m   = max(max_j s_j, sink[h])
+ *   l   = sum_j exp(s_j - m) + exp(sink[h] - m)
+ *   o   = sum_j exp(s_j - m) v_j / l,   lse = m + log(l)
+ * A sink of -inf is no sink.
+ *
+ * A row with no visible key gets o = 0 and lse = -inf, or lse = sink[h] with
+ * a sink (the convention of the minfer "8n" page, section 3.2, epilogue: an
+ * all-masked row is zero). Masked keys are skipped, never multiplied by zero,
+ * so NaN in masked K/V cannot leak.
  *
  * Layouts: q is [B, Sq, Hq, D], k and v are [B, Skv, Hkv, D], addressed with
  * element strides (batch, seq, head); the head_dim stride is 1.
@@ -58,7 +70,8 @@ void oracle_visible_mask(int64_t Sq, int64_t Skv, int causal, int64_t window, ui
 static double attention_row(const double* qrow, const double* k, const int64_t* k_st,
                             const double* v, const int64_t* v_st, int64_t b, int64_t hk,
                             int64_t i, int64_t Sq, int64_t Skv, int64_t D, double scale,
-                            int causal, int64_t window, double* s, double* orow)
+                            int causal, int64_t window, int has_sink, double sink, double* s,
+                            double* orow)
 {
     double m = -INFINITY;
     int64_t nvis = 0;
@@ -72,9 +85,11 @@ static double attention_row(const double* qrow, const double* k, const int64_t* 
         ++nvis;
     }
     for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
-    if (nvis == 0) return -INFINITY;
+    if (has_sink && sink == -INFINITY) has_sink = 0;
+    if (has_sink && sink > m) m = sink;
+    if (nvis == 0 && !has_sink) return -INFINITY;
 
-    double l = 0.0;
+    double l = has_sink ? exp(sink - m) : 0.0;
     for (int64_t j = 0; j < Skv; ++j) {
         if (!visible(i, j, Sq, Skv, causal, window)) continue;
         double p = exp(s[j] - m);
@@ -88,14 +103,16 @@ static double attention_row(const double* qrow, const double* k, const int64_t* 
 
 /*
  * Attention for a list of output rows.
- *   rows: nrows triples (b, i, h)
- *   o:    [nrows, D] output; lse: [nrows] output (may be NULL)
+ *   rows:  nrows triples (b, i, h)
+ *   sinks: [Hq] sink logits, or NULL for none
+ *   o:     [nrows, D] output; lse: [nrows] output (may be NULL)
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
 int oracle_attention_rows(const double* q, const int64_t* q_st, const double* k, const int64_t* k_st,
                           const double* v, const int64_t* v_st, int64_t Hq, int64_t Hkv,
                           int64_t Sq, int64_t Skv, int64_t D, double scale, int causal,
-                          int64_t window, const int64_t* rows, int64_t nrows, double* o, double* lse)
+                          int64_t window, const double* sinks, const int64_t* rows, int64_t nrows,
+                          double* o, double* lse)
 {
     if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || Sq < 0 || Skv < 0) return -1;
     const int64_t group = Hq / Hkv;
@@ -110,7 +127,8 @@ int oracle_attention_rows(const double* q, const int64_t* q_st, const double* k,
             const int64_t b = rows[3 * r], i = rows[3 * r + 1], h = rows[3 * r + 2];
             const double* qrow = q + b * q_st[0] + i * q_st[1] + h * q_st[2];
             double L = attention_row(qrow, k, k_st, v, v_st, b, h / group, i, Sq, Skv, D, scale,
-                                     causal, window, s, o + r * D);
+                                     causal, window, sinks != NULL, sinks ? sinks[h] : 0.0, s,
+                                     o + r * D);
             if (lse) lse[r] = L;
         }
         free(s);

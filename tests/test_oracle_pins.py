@@ -418,3 +418,71 @@ def test_generators_are_seeded_and_round_to_nearest_even():
         ours = W.as_f32(W.round_to(x, dt), dt)
         ref = torch.from_numpy(x).to(tdt).float().numpy()
         assert np.array_equal(ours, ref)
+
+
+# ----------------------------------------------------------------------------- attention sinks
+def brute_row_sink(q, k, v, b, i, h, scale, causal, window, sink):
+    """mpmath, 50 digits: the sink is one more exponential in the normaliser, with no value row."""
+    o, logz = brute_row(q, k, v, b, i, h, scale, causal, window)
+    z = mpmath.exp(logz) if logz != -mpmath.inf else mpmath.mpf(0)
+    zs = z + mpmath.exp(mpmath.mpf(sink))
+    return [x * z / zs for x in o], mpmath.log(zs)
+
+
+SINK_CASES = [
+    # B, Hq, Hkv, Sq, Skv, D, causal, window
+    (1, 2, 1, 6, 6, 3, True, 0),
+    (2, 4, 2, 5, 9, 4, True, 3),  # Sq < Skv, window
+    (1, 3, 3, 7, 7, 2, False, 0),
+    (1, 2, 1, 9, 4, 3, True, 0),  # Sq > Skv: the first rows see no key, only the sink
+]
+
+
+@pytest.mark.parametrize("case", SINK_CASES)
+def test_sinks_bruteforce_mpmath(case):
+    B, Hq, Hkv, Sq, Skv, D, causal, window = case
+    seed = 71 + sum(case[:6])
+    q, k, v = rand((B, Sq, Hq, D), seed), rand((B, Skv, Hkv, D), seed + 1), rand((B, Skv, Hkv, D), seed + 2)
+    sinks = np.linspace(-2.0, 3.0, Hq)
+    o, lse = oracle.attention(q, k, v, 0.8, causal, window, return_lse=True, sinks=sinks)
+    for b in range(B):
+        for i in range(Sq):
+            for h in range(Hq):
+                ref, ref_lse = brute_row_sink(q, k, v, b, i, h, 0.8, causal, window, sinks[h])
+                assert np.allclose(o[b, i, h], [float(x) for x in ref], rtol=1e-13, atol=1e-13)
+                assert abs(lse[b, i, h] - float(ref_lse)) <= 1e-13 * max(1.0, abs(float(ref_lse)))
+
+
+def test_sinks_zero_query_closed_form():
+    """All visible scores are 0: o = (sum of visible V) / (n + e^sink), lse = log(n + e^sink)."""
+    Sq = Skv = 11
+    D = 4
+    q = np.zeros((1, Sq, 2, D))
+    k, v = rand((1, Skv, 1, D), 81), rand((1, Skv, 1, D), 82)
+    sinks = np.array([1.5, -0.75])
+    o, lse = oracle.attention(q, k, v, 0.5, True, 4, return_lse=True, sinks=sinks)
+    for i in range(Sq):
+        lo, hi = max(0, i - 3), i + 1
+        for h in range(2):
+            den = (hi - lo) + math.exp(sinks[h])
+            np.testing.assert_allclose(o[0, i, h], v[0, lo:hi, 0].sum(0) / den, rtol=1e-13, atol=1e-15)
+            assert abs(lse[0, i, h] - math.log(den)) <= 1e-13
+
+
+def test_sinks_rescale_the_plain_result():
+    """With a sink, o = o_plain * sigmoid(lse_plain - sink) and lse = logaddexp(lse_plain, sink);
+    rows without keys give o = 0 and lse = sink. A sink of -inf changes nothing, bit for bit."""
+    q, k, v = rand((2, 10, 4, 8), 91), rand((2, 6, 2, 8), 92), rand((2, 6, 2, 8), 93)
+    sinks = np.array([0.3, -4.0, 2.5, 9.0])
+    o0, l0 = oracle.attention(q, k, v, 0.6, True, 0, return_lse=True)
+    o1, l1 = oracle.attention(q, k, v, 0.6, True, 0, return_lse=True, sinks=sinks)
+    for h in range(4):
+        seen = np.isfinite(l0[:, :, h])
+        sig = 1.0 / (1.0 + np.exp(sinks[h] - l0[:, :, h][seen]))
+        np.testing.assert_allclose(o1[:, :, h][seen], o0[:, :, h][seen] * sig[:, None], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(l1[:, :, h][seen], np.logaddexp(l0[:, :, h][seen], sinks[h]), rtol=1e-13)
+        assert (o1[:, :, h][~seen] == 0).all() and (l1[:, :, h][~seen] == sinks[h]).all()
+    assert (~np.isfinite(l0)).any()  # Sq > Skv: some rows see no key
+    o2, l2 = oracle.attention(q, k, v, 0.6, True, 0, return_lse=True, sinks=np.full(4, -np.inf))
+    np.testing.assert_array_equal(o2, o0)
+    np.testing.assert_array_equal(l2, l0)
