@@ -8,8 +8,10 @@ from .attn import (  # noqa: F401
     AttnError,
     DecodeWorkspace,
     attn_decode_combine,
+    attn_decode_combine_ex,
     attn_decode_fwd,
     attn_prefill_fwd,
+    attn_prefill_fwd_ex,
     decode,
     lib,
     prefill,

@@ -21,8 +21,8 @@ LIB_PATH = os.path.join(HERE, "libattn.so")
 
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "kernel launch failed"}
-SYMBOLS = ("attn_prefill_fwd", "attn_decode_fwd", "attn_decode_combine", "attn_decode_workspace_size",
-           "attn_status_string")
+SYMBOLS = ("attn_prefill_fwd", "attn_prefill_fwd_ex", "attn_decode_fwd", "attn_decode_combine",
+           "attn_decode_combine_ex", "attn_decode_workspace_size", "attn_status_string")
 
 
 class AttnError(RuntimeError):
@@ -50,11 +50,16 @@ def lib() -> ctypes.CDLL:
     L.attn_prefill_fwd.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, i32, i32, i32, i32, i32,
                                    i32, i32, f32, i32, i32, vp]
     L.attn_prefill_fwd.restype = i32
+    L.attn_prefill_fwd_ex.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, i32, i32, i32, i32, i32,
+                                      i32, i32, f32, i32, i32, vp, vp, vp]
+    L.attn_prefill_fwd_ex.restype = i32
     L.attn_decode_fwd.argtypes = [vp, Strides, vp, vp, Strides, vp, i32, i32, vp, i32, i32, i32, i32, i32, i32,
                                   f32, i32, vp, vp, i32, i32, vp]
     L.attn_decode_fwd.restype = i32
     L.attn_decode_combine.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, Strides, i32, vp]
     L.attn_decode_combine.restype = i32
+    L.attn_decode_combine_ex.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, Strides, i32, vp, vp, vp]
+    L.attn_decode_combine_ex.restype = i32
     L.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t),
                                              ctypes.POINTER(ctypes.c_size_t)]
     L.attn_decode_workspace_size.restype = i32
@@ -103,8 +108,26 @@ def _check(fn: str, rc: int):
 
 
 # ----------------------------------------------------------------------------- entry points
+def _f32_vec(t, name: str, n: int):
+    """An optional contiguous float32 GPU tensor with n elements (None passes through)."""
+    import torch
+
+    if t is None:
+        return None
+    _gpu(t, name)
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n:
+        raise ValueError(f"{name} must be a contiguous float32 tensor of {n} elements")
+    return t
+
+
 def attn_prefill_fwd(q, k, v, o, scale: float, causal: bool, window: int = 0, stream=None) -> None:
     """O <- attention(q, k, v). q, o: [B, Sq, Hq, D]; k, v: [B, Skv, Hkv, D]; same dtype."""
+    attn_prefill_fwd_ex(q, k, v, o, scale, causal, window, None, None, stream, _name="attn_prefill_fwd")
+
+
+def attn_prefill_fwd_ex(q, k, v, o, scale: float, causal: bool, window: int = 0, lse=None, sinks=None,
+                        stream=None, _name: str = "attn_prefill_fwd_ex") -> None:
+    """attn_prefill_fwd plus lse (float32 [B, Sq, Hq] out) and sinks (float32 [Hq] in), each optional."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
         _gpu(t, n)
     B, Sq, Hq, D = q.shape
@@ -114,10 +137,16 @@ def attn_prefill_fwd(q, k, v, o, scale: float, causal: bool, window: int = 0, st
     dt = _dtype_code(q)
     if not (k.dtype == v.dtype == o.dtype == q.dtype):
         raise TypeError("q, k, v, o must share one dtype")
-    rc = lib().attn_prefill_fwd(_ptr(q), _strides4(q, "q"), _ptr(k), _strides4(k, "k"), _ptr(v), _strides4(v, "v"),
-                                _ptr(o), _strides4(o, "o"), dt, B, Hq, Hkv, Sq, Skv, D, float(scale), int(bool(causal)),
-                                int(window), _stream(stream))
-    _check("attn_prefill_fwd", rc)
+    lse = _f32_vec(lse, "lse", B * Sq * Hq)
+    sinks = _f32_vec(sinks, "sinks", Hq)
+    L = lib()
+    args = (_ptr(q), _strides4(q, "q"), _ptr(k), _strides4(k, "k"), _ptr(v), _strides4(v, "v"), _ptr(o),
+            _strides4(o, "o"), dt, B, Hq, Hkv, Sq, Skv, D, float(scale), int(bool(causal)), int(window))
+    if _name == "attn_prefill_fwd":
+        rc = L.attn_prefill_fwd(*args, _stream(stream))
+    else:
+        rc = L.attn_prefill_fwd_ex(*args, _ptr(lse), _ptr(sinks), _stream(stream))
+    _check(_name, rc)
 
 
 def attn_decode_fwd(q, k_cache, v_cache, cache_len, part_o, part_lse, split_len: int, max_splits: int,
@@ -150,12 +179,26 @@ def attn_decode_fwd(q, k_cache, v_cache, cache_len, part_o, part_lse, split_len:
 
 def attn_decode_combine(part_o, part_lse, cache_len, split_len: int, max_splits: int, o, stream=None) -> None:
     """o [B, s_active, Hq, D] <- LSE merge of the partials."""
+    attn_decode_combine_ex(part_o, part_lse, cache_len, split_len, max_splits, o, None, None, stream,
+                           _name="attn_decode_combine")
+
+
+def attn_decode_combine_ex(part_o, part_lse, cache_len, split_len: int, max_splits: int, o, lse=None, sinks=None,
+                           stream=None, _name: str = "attn_decode_combine_ex") -> None:
+    """attn_decode_combine plus lse (float32 [B, s_active, Hq] out) and sinks (float32 [Hq] in), each optional."""
     for t, n in ((part_o, "part_o"), (part_lse, "part_lse"), (cache_len, "cache_len"), (o, "o")):
         _gpu(t, n)
     B, sa, Hq, D = o.shape
-    rc = lib().attn_decode_combine(_ptr(part_o), _ptr(part_lse), _ptr(cache_len), int(split_len), int(max_splits),
-                                   B, sa, Hq, D, _ptr(o), _strides4(o, "o"), _dtype_code(o), _stream(stream))
-    _check("attn_decode_combine", rc)
+    lse = _f32_vec(lse, "lse", B * sa * Hq)
+    sinks = _f32_vec(sinks, "sinks", Hq)
+    L = lib()
+    args = (_ptr(part_o), _ptr(part_lse), _ptr(cache_len), int(split_len), int(max_splits), B, sa, Hq, D, _ptr(o),
+            _strides4(o, "o"), _dtype_code(o))
+    if _name == "attn_decode_combine":
+        rc = L.attn_decode_combine(*args, _stream(stream))
+    else:
+        rc = L.attn_decode_combine_ex(*args, _ptr(lse), _ptr(sinks), _stream(stream))
+    _check(_name, rc)
 
 
 # ----------------------------------------------------------------------------- conveniences
@@ -163,12 +206,19 @@ def default_scale(head_dim: int) -> float:
     return 1.0 / math.sqrt(head_dim)
 
 
-def prefill(q, k, v, scale: float | None = None, causal: bool = False, window: int = 0, out=None, stream=None):
+def prefill(q, k, v, scale: float | None = None, causal: bool = False, window: int = 0, out=None, stream=None,
+            sinks=None, return_lse: bool = False):
+    """Output (and, with return_lse, the float32 [B, Sq, Hq] log-sum-exp); sinks: float32 [Hq] or None."""
     import torch
 
     o = torch.empty_like(q) if out is None else out
-    attn_prefill_fwd(q, k, v, o, default_scale(q.shape[-1]) if scale is None else scale, causal, window, stream)
-    return o
+    sc = default_scale(q.shape[-1]) if scale is None else scale
+    if sinks is None and not return_lse:
+        attn_prefill_fwd(q, k, v, o, sc, causal, window, stream)
+        return o
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    attn_prefill_fwd_ex(q, k, v, o, sc, causal, window, lse, sinks, stream)
+    return (o, lse) if return_lse else o
 
 
 class DecodeWorkspace:
@@ -187,9 +237,10 @@ def max_splits_for(max_len: int, split_len: int) -> int:
 
 
 def decode(q, k_cache, v_cache, cache_len, block_table=None, scale: float | None = None, window: int = 0,
-           split_len: int = 512, max_len: int | None = None, workspace: DecodeWorkspace | None = None, out=None,
-           stream=None):
-    """Split-KV decode followed by the combine, both on the current stream."""
+           split_len: int = 1024, max_len: int | None = None, workspace: DecodeWorkspace | None = None, out=None,
+           stream=None, sinks=None, return_lse: bool = False):
+    """Split-KV decode followed by the combine, both on the current stream (optionally with
+    attention sinks, float32 [Hq], and returning the float32 [B, s_active, Hq] log-sum-exp)."""
     import torch
 
     B, sa, Hq, D = q.shape
@@ -203,5 +254,9 @@ def decode(q, k_cache, v_cache, cache_len, block_table=None, scale: float | None
     sc = default_scale(D) if scale is None else scale
     attn_decode_fwd(q, k_cache, v_cache, cache_len, ws.part_o, ws.part_lse, split_len, ws.max_splits, sc,
                     block_table, window, stream)
-    attn_decode_combine(ws.part_o, ws.part_lse, cache_len, split_len, ws.max_splits, o, stream)
-    return o
+    if sinks is None and not return_lse:
+        attn_decode_combine(ws.part_o, ws.part_lse, cache_len, split_len, ws.max_splits, o, stream)
+        return o
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    attn_decode_combine_ex(ws.part_o, ws.part_lse, cache_len, split_len, ws.max_splits, o, lse, sinks, stream)
+    return (o, lse) if return_lse else o

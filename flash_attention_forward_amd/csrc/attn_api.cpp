@@ -18,6 +18,9 @@ int elem_bytes(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
+// Optional float arrays (NULL allowed) must be 4-byte aligned.
+bool aligned4(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 3u) == 0; }
+
 bool strides_ok(const attn_strides& s, int eb) {
     return s.batch >= 0 && s.seq >= 0 && s.head >= 0 && (s.batch * eb) % 16 == 0 && (s.seq * eb) % 16 == 0 &&
            (s.head * eb) % 16 == 0;
@@ -31,10 +34,6 @@ uint32_t q_flip_mask(float scale, int dtype) {
     return dtype == ATTN_F32 ? 0x80000000u : 0x80008000u;
 }
 
-// |scale| * log2(e), kept >= 1e-30 so that the float32-min stand-in of a
-// masked score always maps to probability exactly 0. A zero scale becomes
-// 1e-30: every visible score is then a tiny number whose exp2 rounds to 1, the
-// same uniform weights.
 // |scale| * log2(e), kept at or above `floor` so that a masked score (float32
 // min) times it stays far below every real scaled score and below the kernels'
 // initial running max (-1e30): its exp2 is then exactly 0 and it never moves
@@ -63,10 +62,10 @@ const char* attn_status_string(int status) {
     }
 }
 
-int attn_prefill_fwd(const void* q, attn_strides q_st, const void* k, attn_strides k_st, const void* v,
-                     attn_strides v_st, void* o, attn_strides o_st, attn_dtype dtype, int batch, int n_q_heads,
-                     int n_kv_heads, int seqlen_q, int seqlen_kv, int head_dim, float scale, int causal, int window,
-                     void* hip_stream) {
+int attn_prefill_fwd_ex(const void* q, attn_strides q_st, const void* k, attn_strides k_st, const void* v,
+                        attn_strides v_st, void* o, attn_strides o_st, attn_dtype dtype, int batch, int n_q_heads,
+                        int n_kv_heads, int seqlen_q, int seqlen_kv, int head_dim, float scale, int causal,
+                        int window, float* lse, const float* sinks, void* hip_stream) {
     if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
     if (batch < 0 || n_q_heads < 0 || n_kv_heads < 0 || seqlen_q < 0 || seqlen_kv < 0 || head_dim <= 0)
         return ATTN_ERR_INVALID;
@@ -80,6 +79,7 @@ int attn_prefill_fwd(const void* q, attn_strides q_st, const void* k, attn_strid
     if (seqlen_kv > 0 && (!k || !v || !aligned16(k) || !aligned16(v))) return ATTN_ERR_INVALID;
     if (!strides_ok(q_st, eb) || !strides_ok(k_st, eb) || !strides_ok(v_st, eb) || !strides_ok(o_st, eb))
         return ATTN_ERR_INVALID;
+    if (!aligned4(lse) || !aligned4(sinks)) return ATTN_ERR_INVALID;
     // lane offsets inside one 64-row K/V tile are kept in 32 bits
     if (k_st.seq * 64 + head_dim >= ((int64_t)1 << 31) || v_st.seq * 64 + head_dim >= ((int64_t)1 << 31))
         return ATTN_ERR_UNSUPPORTED;
@@ -94,8 +94,18 @@ int attn_prefill_fwd(const void* q, attn_strides q_st, const void* k, attn_strid
     p.window = window > 0 ? window : 0;
     p.c = scaled_log2e(scale, dtype == ATTN_F32 ? 1e-30 : 1e-8);
     p.qflip = q_flip_mask(scale, dtype);
+    p.lse = lse;
+    p.sinks = sinks;
     const int mask = !causal ? attn::kMaskNone : (p.window > 0 ? attn::kMaskCausalWindow : attn::kMaskCausal);
     return status_of(attn::launch_prefill(p, (int)dtype, head_dim, mask, (hipStream_t)hip_stream));
+}
+
+int attn_prefill_fwd(const void* q, attn_strides q_st, const void* k, attn_strides k_st, const void* v,
+                     attn_strides v_st, void* o, attn_strides o_st, attn_dtype dtype, int batch, int n_q_heads,
+                     int n_kv_heads, int seqlen_q, int seqlen_kv, int head_dim, float scale, int causal, int window,
+                     void* hip_stream) {
+    return attn_prefill_fwd_ex(q, q_st, k, k_st, v, v_st, o, o_st, dtype, batch, n_q_heads, n_kv_heads, seqlen_q,
+                               seqlen_kv, head_dim, scale, causal, window, nullptr, nullptr, hip_stream);
 }
 
 int attn_decode_workspace_size(int batch, int s_active, int n_q_heads, int head_dim, int max_splits,
@@ -151,9 +161,9 @@ int attn_decode_fwd(const void* q, attn_strides q_st, const void* k_cache, const
     return status_of(attn::launch_decode(p, (int)dtype, head_dim, (hipStream_t)hip_stream));
 }
 
-int attn_decode_combine(const float* part_o, const float* part_lse, const int32_t* cache_len, int split_len,
-                        int max_splits, int batch, int s_active, int n_q_heads, int head_dim, void* o,
-                        attn_strides o_st, attn_dtype dtype, void* hip_stream) {
+int attn_decode_combine_ex(const float* part_o, const float* part_lse, const int32_t* cache_len, int split_len,
+                           int max_splits, int batch, int s_active, int n_q_heads, int head_dim, void* o,
+                           attn_strides o_st, attn_dtype dtype, float* lse, const float* sinks, void* hip_stream) {
     if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
     if (batch < 0 || s_active < 0 || n_q_heads < 0 || head_dim <= 0) return ATTN_ERR_INVALID;
     if (batch == 0 || s_active == 0 || n_q_heads == 0) return ATTN_OK;
@@ -163,12 +173,21 @@ int attn_decode_combine(const float* part_o, const float* part_lse, const int32_
     if ((int64_t)batch * s_active * n_q_heads >= (int64_t)1 << 31) return ATTN_ERR_UNSUPPORTED;
     if (!part_o || !part_lse || !cache_len || !o || !aligned16(o)) return ATTN_ERR_INVALID;
     if (!strides_ok(o_st, elem_bytes(dtype))) return ATTN_ERR_INVALID;
+    if (!aligned4(lse) || !aligned4(sinks)) return ATTN_ERR_INVALID;
 
     attn::CombineParams p{};
     p.part_o = part_o; p.part_lse = part_lse; p.cache_len = cache_len; p.o = o; p.os = conv(o_st);
     p.batch = batch; p.s_active = s_active; p.n_q_heads = n_q_heads;
     p.split_len = split_len; p.max_splits = max_splits;
+    p.lse = lse; p.sinks = sinks;
     return status_of(attn::launch_combine(p, (int)dtype, head_dim, (hipStream_t)hip_stream));
+}
+
+int attn_decode_combine(const float* part_o, const float* part_lse, const int32_t* cache_len, int split_len,
+                        int max_splits, int batch, int s_active, int n_q_heads, int head_dim, void* o,
+                        attn_strides o_st, attn_dtype dtype, void* hip_stream) {
+    return attn_decode_combine_ex(part_o, part_lse, cache_len, split_len, max_splits, batch, s_active, n_q_heads,
+                                  head_dim, o, o_st, dtype, nullptr, nullptr, hip_stream);
 }
 
 }  // extern "C"

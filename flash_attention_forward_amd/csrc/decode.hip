@@ -378,7 +378,21 @@ __global__ __launch_bounds__(64) void decode_combine(CombineParams p) {
         acc.z = add_other(acc.z, true); acc.w = add_other(acc.w, true);
         wsum = add_other(wsum, true);
     }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    // Attention sink: one more logit of the row, with no value (the decode
+    // page's per-q-head sink), merged like a split with O = 0. The partial
+    // LSEs are natural-log, so the sink enters in the same units.
+    float osc = 1.f;
+    if (p.sinks) {
+        const float sk = p.sinks[h];
+        if (sk > -__builtin_inff()) {
+            const float mn = fmaxf(M, sk);
+            osc = fast_exp2((M - mn) * kLog2e);  // 0 when no split was visible (M = -inf)
+            wsum = wsum * osc + fast_exp2((sk - mn) * kLog2e);
+            M = mn;
+        }
+    }
+    const float inv = wsum > 0.f ? osc / wsum : 0.f;
+    if (p.lse && lane == 0) p.lse[row] = wsum > 0.f ? M + __logf(wsum) : -__builtin_inff();
     if (r == 0) {
         uint16_t* orow = (uint16_t*)p.o + (int64_t)b * p.os.batch + (int64_t)i * p.os.seq + (int64_t)h * p.os.head;
         uint2 pk;

@@ -89,6 +89,22 @@ __device__ __forceinline__ float sum_with_other_half(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Attention sink (one extra logit without a value row, in scaled log2 units
+// s2 = sink * log2 e) folded into a finished row with running max m and sum
+// l (also log2 units): the max becomes max(m, s2), O and l are rescaled once
+// to it and the sink's exponential joins the sum. Returns the factor for O
+// and updates m and l. A sink of -inf (or none) leaves everything as it is.
+// A row that saw no key (l = 0, m at its finite initial value) ends with
+// l = 1, O = 0 and m = s2.
+__device__ __forceinline__ float fold_sink(float s2, float& m, float& l) {
+    if (!(s2 > -__builtin_inff())) return 1.f;
+    const float mn = fmaxf(m, s2);
+    const float a = __builtin_amdgcn_exp2f(m - mn);
+    l = l * a + __builtin_amdgcn_exp2f(s2 - mn);
+    m = mn;
+    return a;
+}
+
 // Round-to-nearest-even conversions of f32 to 16-bit floats, returned as raw bits.
 template <bool BF16>
 __device__ __forceinline__ uint16_t f32_to_16(float x) {

@@ -22,6 +22,8 @@ struct PrefillParams {
     int n_q_tiles;
     float c;          // |scale| * log2(e): scores are kept in scaled log2 units
     uint32_t qflip;   // 0x80008000 (16-bit) / 0x80000000 (f32) flips Q's sign when scale < 0
+    float* lse;           // NULL, or [batch, seqlen_q, n_q_heads] natural-log log-sum-exp per row
+    const float* sinks;   // NULL, or [n_q_heads] sink logits (scaled-score units)
 };
 
 struct DecodeParams {
@@ -47,6 +49,8 @@ struct CombineParams {
     void* o;
     Strides3 os;
     int batch, s_active, n_q_heads, split_len, max_splits;
+    float* lse;           // NULL, or [batch, s_active, n_q_heads] natural-log log-sum-exp per row
+    const float* sinks;   // NULL, or [n_q_heads] sink logits (scaled-score units)
 };
 
 // Largest number of pages one decode split may span (split_len / page_size).

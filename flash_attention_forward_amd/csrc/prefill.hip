@@ -471,9 +471,15 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     }
     wait_vmcnt<0>();  // nothing is left in flight when the wave ends
 
-    // Epilogue: O * (1/l); rows that saw no key are written as zeros.
-    const float l_tot = sum_with_other_half(l_i);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    // Epilogue: O * (1/l), with the sink folded in first; rows that saw no
+    // key are written as zeros. The log-sum-exp (natural log) goes to lse.
+    float l_tot = sum_with_other_half(l_i);
+    float m_fin = m_i;
+    const float osc = p.sinks ? fold_sink(p.sinks[h] * kLog2e, m_fin, l_tot) : 1.f;
+    const float inv = l_tot > 0.f ? osc / l_tot : 0.f;
+    if (p.lse && hf == 0 && wave_live && my_q < p.seqlen_q)
+        p.lse[((int64_t)b * p.seqlen_q + my_q) * p.n_q_heads + h] =
+            l_tot > 0.f ? (m_fin + __log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
     if (wave_live && my_q < p.seqlen_q) {
         uint16_t* orow = (uint16_t*)p.o + (int64_t)b * p.os.batch + (int64_t)my_q * p.os.seq +
                          (int64_t)h * p.os.head;
@@ -581,7 +587,12 @@ __global__ __launch_bounds__(256) void prefill_f32(PrefillParams p) {
         }
     }
     if (live) {
-        const float inv = l_i > 0.f ? 1.f / l_i : 0.f;
+        float m_fin = m_i;
+        const float osc = p.sinks ? fold_sink(p.sinks[h] * kLog2e, m_fin, l_i) : 1.f;
+        const float inv = l_i > 0.f ? osc / l_i : 0.f;
+        if (p.lse && qd == 0)
+            p.lse[((int64_t)b * p.seqlen_q + my_q) * p.n_q_heads + h] =
+                l_i > 0.f ? (m_fin + __log2f(l_i)) * 0.69314718055994531f : -__builtin_inff();
         float* orow = (float*)p.o + (int64_t)b * p.os.batch + (int64_t)my_q * p.os.seq + (int64_t)h * p.os.head +
                       qd * DQ;
 #pragma unroll

@@ -98,6 +98,31 @@ int attn_prefill_fwd(const void* q, attn_strides q_st, const void* k, attn_strid
                      float scale, int causal, int window, void* hip_stream);
 
 /*
+ * attn_prefill_fwd with two optional extras (NULL = not used):
+ *   lse    device float [batch, seqlen_q, n_q_heads] (contiguous): for every
+ *          row, the natural-log log-sum-exp of its scaled visible scores
+ *          (and of the sink), m + log(l) — the softmax statistics the CTE
+ *          page writes out for a backward pass ("cache_softmax": the row max
+ *          and the reciprocal of the sum) and what a sequence-parallel merge
+ *          needs. -inf for a row that sees no key and has no sink.
+ *   sinks  device float [n_q_heads]: an attention sink per q-head — one more
+ *          logit of every row of that head, in the units of the scaled
+ *          scores, that joins the row max and the softmax sum but has no
+ *          value row (CTE page: the sink logit appended to the section max
+ *          and its exponential to the sums; decode page: one sink per q-head,
+ *          broadcast over the batch). O becomes sum_j p_j v_j / (sum_j p_j +
+ *          exp(sink - m)). A sink of -inf is no sink; NaN or +inf sinks give
+ *          NaN rows. A row that sees no key outputs zeros and lse = sink.
+ * Both pointers must be 4-byte aligned.
+ */
+int attn_prefill_fwd_ex(const void* q, attn_strides q_st, const void* k, attn_strides k_st,
+                        const void* v, attn_strides v_st, void* o, attn_strides o_st,
+                        attn_dtype dtype, int batch, int n_q_heads, int n_kv_heads,
+                        int seqlen_q, int seqlen_kv, int head_dim,
+                        float scale, int causal, int window,
+                        float* lse, const float* sinks, void* hip_stream);
+
+/*
  * Decode attention against a KV cache, split along the cache (split-KV).
  *   q       [batch, s_active, n_q_heads, head_dim] device, `dtype`.
  *   Paged cache (block_table != NULL): k_cache, v_cache are
@@ -154,6 +179,21 @@ int attn_decode_combine(const float* part_o, const float* part_lse, const int32_
                         int split_len, int max_splits, int batch, int s_active, int n_q_heads,
                         int head_dim, void* o, attn_strides o_st, attn_dtype dtype,
                         void* hip_stream);
+
+/*
+ * attn_decode_combine with the same two optional extras as
+ * attn_prefill_fwd_ex (NULL = not used):
+ *   lse    device float [batch, s_active, n_q_heads]: natural-log
+ *          log-sum-exp of each merged row (over all its splits and the sink);
+ *   sinks  device float [n_q_heads]: attention sink per q-head, merged as
+ *          one more partial whose output is zero and whose log-sum-exp is the
+ *          sink.
+ * The split kernel is unchanged: the sink enters once per row, here.
+ */
+int attn_decode_combine_ex(const float* part_o, const float* part_lse, const int32_t* cache_len,
+                           int split_len, int max_splits, int batch, int s_active, int n_q_heads,
+                           int head_dim, void* o, attn_strides o_st, attn_dtype dtype,
+                           float* lse, const float* sinks, void* hip_stream);
 
 /* Bytes of part_o and part_lse that attn_decode_fwd needs. Returns ATTN_OK or ATTN_ERR_INVALID. */
 int attn_decode_workspace_size(int batch, int s_active, int n_q_heads, int head_dim, int max_splits,

@@ -151,3 +151,33 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 4, 1, 64)
     with pytest.raises(ValueError, match="GPU"):
         A.attn_prefill_fwd(x, x, x, x, 1.0, False)
+
+
+def prefill_ex(lse=None, sinks=None, **kw):
+    a = dict(q=FAKE, qs=st(2048 * 8 * 128, 8 * 128, 128), k=FAKE, ks=st(2048 * 128, 128, 128), v=FAKE,
+             vs=st(2048 * 128, 128, 128), o=FAKE, os=st(2048 * 8 * 128, 8 * 128, 128), dtype=A.ATTN_BF16, batch=1,
+             hq=8, hkv=1, sq=2048, skv=2048, d=128, scale=0.088, causal=1, window=0)
+    a.update(kw)
+    return A.lib().attn_prefill_fwd_ex(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["o"], a["os"],
+                                       a["dtype"], a["batch"], a["hq"], a["hkv"], a["sq"], a["skv"], a["d"],
+                                       a["scale"], a["causal"], a["window"], lse, sinks, None)
+
+
+def combine_ex(lse=None, sinks=None, **kw):
+    a = dict(po=FAKE, pl=FAKE, cl=FAKE, split=512, ms=64, batch=32, sa=1, hq=32, d=128, o=FAKE,
+             os=st(32 * 128, 32 * 128, 128), dtype=A.ATTN_BF16)
+    a.update(kw)
+    return A.lib().attn_decode_combine_ex(a["po"], a["pl"], a["cl"], a["split"], a["ms"], a["batch"], a["sa"],
+                                          a["hq"], a["d"], a["o"], a["os"], a["dtype"], lse, sinks, None)
+
+
+@pytest.mark.parametrize("lse,sinks", [(FAKE + 2, None), (None, FAKE + 1), (FAKE + 6, FAKE)])
+def test_ex_entry_points_reject_misaligned_extras(lse, sinks):
+    assert prefill_ex(lse=lse, sinks=sinks) == INVALID
+    assert combine_ex(lse=lse, sinks=sinks) == INVALID
+
+
+def test_ex_entry_points_check_like_the_plain_ones():
+    assert prefill_ex(d=96, lse=FAKE) == UNSUPPORTED
+    assert prefill_ex(batch=0, lse=FAKE + 2) == 0  # empty: nothing is checked or enqueued
+    assert combine_ex(ms=0, sinks=FAKE) == INVALID
