@@ -262,6 +262,48 @@ def main():
 
     spec_us = time_decode(dq4, kc, vc, bt, ws4, do4) * 1e3
     flat_us = time_decode(dq, kflat, vflat, None, ws, torch.empty_like(dq)) * 1e3
+    del kflat, vflat
+
+    # the same caches stored as FP8 E4M3 (attn_decode_fwd_fp8kv + combine): the values rounded on the GPU
+    kc8, vc8 = kc.to(torch.float8_e4m3fn), vc.to(torch.float8_e4m3fn)
+    for _ in range(3):
+        F.attn_decode_fwd_fp8kv(dq, kc8, vc8, cl, ws.part_o, ws.part_lse, args.split_len, ms, dspec.scale_f32,
+                                block_table=bt)
+    fev = [[ev(), ev(), ev()] for _ in range(20)]
+    for e in fev:
+        e[0].record(stream)
+        F.attn_decode_fwd_fp8kv(dq, kc8, vc8, cl, ws.part_o, ws.part_lse, args.split_len, ms, dspec.scale_f32,
+                                block_table=bt)
+        e[1].record(stream)
+        F.attn_decode_combine(ws.part_o, ws.part_lse, cl, args.split_len, ms, do)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    fp8_split_us = float(np.mean([e[0].elapsed_time(e[1]) for e in fev])) * 1e3
+    fp8_us = float(np.mean([e[0].elapsed_time(e[2]) for e in fev])) * 1e3
+    del kc8, vc8
+
+    # the same prefill and decode with an attention sink per q-head and the
+    # per-row log-sum-exp written out (attn_prefill_fwd_ex, attn_decode_combine_ex)
+    psinks = torch.linspace(-1.0, 2.0, pspec.n_q_heads, device=dev)
+    plse = torch.empty((pspec.batch, pspec.seqlen_q, pspec.n_q_heads), dtype=torch.float32, device=dev)
+    dsinks = torch.linspace(-1.0, 2.0, dspec.n_q_heads, device=dev)
+    dlse = torch.empty((dspec.batch, dspec.s_active, dspec.n_q_heads), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        F.attn_prefill_fwd_ex(q, k, v, o, pspec.scale_f32, True, 0, plse, psinks)
+    pev = [[ev(), ev()] for _ in range(8)]
+    for e in pev:
+        e[0].record(stream)
+        F.attn_prefill_fwd_ex(q, k, v, o, pspec.scale_f32, True, 0, plse, psinks)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    pre_ex_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in pev]))
+    cev = [[ev(), ev()] for _ in range(20)]
+    for e in cev:
+        e[0].record(stream)
+        F.attn_decode_combine_ex(ws.part_o, ws.part_lse, cl, args.split_len, ms, do, dlse, dsinks)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    comb_ex_us = float(np.mean([e[0].elapsed_time(e[1]) for e in cev])) * 1e3
 
     flops = prefill_flops(pspec)
     kv_bytes = decode_kv_bytes(din)
@@ -320,12 +362,24 @@ def main():
             "pages_ms_per_layer": PAGES_CONTEXT_MS_PER_LAYER,
             "pages_hardware": "unnamed NVIDIA GPU (minfer 8n page); context only",
         },
+        "sinks_and_lse": {
+            "prefill_ex_ms": round(pre_ex_ms, 4),
+            "prefill_ex_tflops": round(prefill_flops(pspec) / (pre_ex_ms * 1e-3) / 1e12, 2),
+            "decode_combine_ex_us": round(comb_ex_us, 2),
+            "note": "attn_prefill_fwd_ex / attn_decode_combine_ex with one sink per q-head and the lse output",
+        },
         "decode_variants": {
             "speculative_s_active4_us": round(spec_us, 2),
             "speculative_s_active4_gbps": round(kv_bytes / (spec_us * 1e-6) / 1e9, 1),
             "flat_cache_us": round(flat_us, 2),
             "flat_cache_gbps": round(kv_bytes / (flat_us * 1e-6) / 1e9, 1),
-            "note": "split + combine over the same caches: 4 query tokens per sequence, and a flat cache copy",
+            "fp8_kv_split_us": round(fp8_split_us, 2),
+            "fp8_kv_us": round(fp8_us, 2),
+            "fp8_kv_split_gbps": round(kv_bytes / 2 / (fp8_split_us * 1e-6) / 1e9, 1),
+            "fp8_kv_split_frac_of_peak": round(kv_bytes / 2 / (fp8_split_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+            "fp8_kv_speedup_vs_bf16": round(float(dec_ms.mean()) * 1e3 / fp8_us, 3),
+            "note": "split + combine over the same caches: 4 query tokens per sequence, a flat cache copy, and the "
+                    "cache stored as FP8 E4M3 (half the bytes)",
         },
         "kernel_source_digest": kernel_source_digest(),
     }

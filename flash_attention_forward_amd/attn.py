@@ -21,8 +21,8 @@ LIB_PATH = os.path.join(HERE, "libattn.so")
 
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "kernel launch failed"}
-SYMBOLS = ("attn_prefill_fwd", "attn_prefill_fwd_ex", "attn_decode_fwd", "attn_decode_combine",
-           "attn_decode_combine_ex", "attn_decode_workspace_size", "attn_status_string")
+SYMBOLS = ("attn_prefill_fwd", "attn_prefill_fwd_ex", "attn_decode_fwd", "attn_decode_fwd_fp8kv",
+           "attn_decode_combine", "attn_decode_combine_ex", "attn_decode_workspace_size", "attn_status_string")
 
 
 class AttnError(RuntimeError):
@@ -56,6 +56,9 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_fwd.argtypes = [vp, Strides, vp, vp, Strides, vp, i32, i32, vp, i32, i32, i32, i32, i32, i32,
                                   f32, i32, vp, vp, i32, i32, vp]
     L.attn_decode_fwd.restype = i32
+    L.attn_decode_fwd_fp8kv.argtypes = [vp, Strides, vp, vp, Strides, vp, i32, i32, vp, i32, i32, i32, i32, i32, i32,
+                                        f32, f32, f32, i32, vp, vp, i32, i32, vp]
+    L.attn_decode_fwd_fp8kv.restype = i32
     L.attn_decode_combine.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, Strides, i32, vp]
     L.attn_decode_combine.restype = i32
     L.attn_decode_combine_ex.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, Strides, i32, vp, vp, vp]
@@ -152,6 +155,20 @@ def attn_prefill_fwd_ex(q, k, v, o, scale: float, causal: bool, window: int = 0,
 def attn_decode_fwd(q, k_cache, v_cache, cache_len, part_o, part_lse, split_len: int, max_splits: int,
                     scale: float, block_table=None, window: int = 0, stream=None) -> None:
     """Split-KV partials. Paged if block_table is given ([B, max_pages] uint32 stored as int32)."""
+    _decode_fwd(q, k_cache, v_cache, cache_len, part_o, part_lse, split_len, max_splits, scale, block_table, window,
+                stream, None)
+
+
+def attn_decode_fwd_fp8kv(q, k_cache, v_cache, cache_len, part_o, part_lse, split_len: int, max_splits: int,
+                          scale: float, k_scale: float = 1.0, v_scale: float = 1.0, block_table=None, window: int = 0,
+                          stream=None) -> None:
+    """attn_decode_fwd for an FP8 E4M3 cache (torch.float8_e4m3fn or uint8 codes); q stays f16/bf16."""
+    _decode_fwd(q, k_cache, v_cache, cache_len, part_o, part_lse, split_len, max_splits, scale, block_table, window,
+                stream, (float(k_scale), float(v_scale)))
+
+
+def _decode_fwd(q, k_cache, v_cache, cache_len, part_o, part_lse, split_len, max_splits, scale, block_table, window,
+                stream, fp8_scales):
     import torch
 
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (cache_len, "cache_len"),
@@ -170,11 +187,17 @@ def attn_decode_fwd(q, k_cache, v_cache, cache_len, part_o, part_lse, split_len:
         maxp, ps = block_table.shape[1], k_cache.shape[1]
     else:
         maxp, ps = 0, 0
-    rc = lib().attn_decode_fwd(_ptr(q), _strides4(q, "q"), _ptr(k_cache), _ptr(v_cache), _strides4(k_cache, "k_cache"),
-                               _ptr(block_table), maxp, ps, _ptr(cache_len), _dtype_code(q), B, sa, Hq, Hkv, D,
-                               float(scale), int(window), _ptr(part_o), _ptr(part_lse), int(split_len),
-                               int(max_splits), _stream(stream))
-    _check("attn_decode_fwd", rc)
+    head = (_ptr(q), _strides4(q, "q"), _ptr(k_cache), _ptr(v_cache), _strides4(k_cache, "k_cache"),
+            _ptr(block_table), maxp, ps, _ptr(cache_len), _dtype_code(q), B, sa, Hq, Hkv, D, float(scale))
+    tail = (int(window), _ptr(part_o), _ptr(part_lse), int(split_len), int(max_splits), _stream(stream))
+    if fp8_scales is None:
+        if k_cache.dtype != q.dtype:
+            raise TypeError("k_cache and v_cache must have q's dtype (use attn_decode_fwd_fp8kv for FP8 caches)")
+        _check("attn_decode_fwd", lib().attn_decode_fwd(*head, *tail))
+    else:
+        if k_cache.dtype not in (torch.float8_e4m3fn, torch.uint8) or v_cache.dtype != k_cache.dtype:
+            raise TypeError("FP8 caches must be torch.float8_e4m3fn (or uint8 codes)")
+        _check("attn_decode_fwd_fp8kv", lib().attn_decode_fwd_fp8kv(*head, *fp8_scales, *tail))
 
 
 def attn_decode_combine(part_o, part_lse, cache_len, split_len: int, max_splits: int, o, stream=None) -> None:
@@ -238,7 +261,7 @@ def max_splits_for(max_len: int, split_len: int) -> int:
 
 def decode(q, k_cache, v_cache, cache_len, block_table=None, scale: float | None = None, window: int = 0,
            split_len: int = 1024, max_len: int | None = None, workspace: DecodeWorkspace | None = None, out=None,
-           stream=None, sinks=None, return_lse: bool = False):
+           stream=None, sinks=None, return_lse: bool = False, k_scale: float = 1.0, v_scale: float = 1.0):
     """Split-KV decode followed by the combine, both on the current stream (optionally with
     attention sinks, float32 [Hq], and returning the float32 [B, s_active, Hq] log-sum-exp)."""
     import torch
@@ -252,8 +275,12 @@ def decode(q, k_cache, v_cache, cache_len, block_table=None, scale: float | None
         raise ValueError("workspace has too few splits")
     o = torch.empty_like(q) if out is None else out
     sc = default_scale(D) if scale is None else scale
-    attn_decode_fwd(q, k_cache, v_cache, cache_len, ws.part_o, ws.part_lse, split_len, ws.max_splits, sc,
-                    block_table, window, stream)
+    if k_cache.dtype in (torch.float8_e4m3fn, torch.uint8):
+        attn_decode_fwd_fp8kv(q, k_cache, v_cache, cache_len, ws.part_o, ws.part_lse, split_len, ws.max_splits, sc,
+                              k_scale, v_scale, block_table, window, stream)
+    else:
+        attn_decode_fwd(q, k_cache, v_cache, cache_len, ws.part_o, ws.part_lse, split_len, ws.max_splits, sc,
+                        block_table, window, stream)
     if sinks is None and not return_lse:
         attn_decode_combine(ws.part_o, ws.part_lse, cache_len, split_len, ws.max_splits, o, stream)
         return o

@@ -117,11 +117,13 @@ int attn_decode_workspace_size(int batch, int s_active, int n_q_heads, int head_
     return ATTN_OK;
 }
 
-int attn_decode_fwd(const void* q, attn_strides q_st, const void* k_cache, const void* v_cache, attn_strides kv_st,
+namespace {
+// Shared by attn_decode_fwd and attn_decode_fwd_fp8kv: kv_bytes is the cache's element size.
+int decode_fwd_impl(const void* q, attn_strides q_st, const void* k_cache, const void* v_cache, attn_strides kv_st,
                     const uint32_t* block_table, int max_pages_per_seq, int page_size, const int32_t* cache_len,
                     attn_dtype dtype, int batch, int s_active, int n_q_heads, int n_kv_heads, int head_dim,
                     float scale, int window, float* part_o, float* part_lse, int split_len, int max_splits,
-                    void* hip_stream) {
+                    int kv_bytes, float v_scale, void* hip_stream) {
     if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
     if (batch < 0 || s_active < 0 || n_q_heads < 0 || n_kv_heads < 0 || head_dim <= 0) return ATTN_ERR_INVALID;
     if (!std::isfinite(scale)) return ATTN_ERR_INVALID;
@@ -140,7 +142,7 @@ int attn_decode_fwd(const void* q, attn_strides q_st, const void* k_cache, const
     const int eb = elem_bytes(dtype);
     if (!q || !k_cache || !v_cache || !cache_len || !part_o || !part_lse) return ATTN_ERR_INVALID;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(part_o)) return ATTN_ERR_INVALID;
-    if (!strides_ok(q_st, eb) || !strides_ok(kv_st, eb)) return ATTN_ERR_INVALID;
+    if (!strides_ok(q_st, eb) || !strides_ok(kv_st, kv_bytes)) return ATTN_ERR_INVALID;
 
     attn::DecodeParams p{};
     p.q = q; p.k = k_cache; p.v = v_cache;
@@ -158,7 +160,32 @@ int attn_decode_fwd(const void* q, attn_strides q_st, const void* k_cache, const
     p.split_len = split_len; p.max_splits = max_splits;
     p.c = scaled_log2e(scale, 1e-30);
     p.qflip = q_flip_mask(scale, dtype);
+    p.kv_fp8 = kv_bytes == 1;
+    p.v_scale = v_scale;
     return status_of(attn::launch_decode(p, (int)dtype, head_dim, (hipStream_t)hip_stream));
+}
+}  // namespace
+
+int attn_decode_fwd(const void* q, attn_strides q_st, const void* k_cache, const void* v_cache, attn_strides kv_st,
+                    const uint32_t* block_table, int max_pages_per_seq, int page_size, const int32_t* cache_len,
+                    attn_dtype dtype, int batch, int s_active, int n_q_heads, int n_kv_heads, int head_dim,
+                    float scale, int window, float* part_o, float* part_lse, int split_len, int max_splits,
+                    void* hip_stream) {
+    return decode_fwd_impl(q, q_st, k_cache, v_cache, kv_st, block_table, max_pages_per_seq, page_size, cache_len,
+                           dtype, batch, s_active, n_q_heads, n_kv_heads, head_dim, scale, window, part_o, part_lse,
+                           split_len, max_splits, elem_bytes(dtype), 1.f, hip_stream);
+}
+
+int attn_decode_fwd_fp8kv(const void* q, attn_strides q_st, const uint8_t* k_cache, const uint8_t* v_cache,
+                          attn_strides kv_st, const uint32_t* block_table, int max_pages_per_seq, int page_size,
+                          const int32_t* cache_len, attn_dtype dtype, int batch, int s_active, int n_q_heads,
+                          int n_kv_heads, int head_dim, float scale, float k_scale, float v_scale, int window,
+                          float* part_o, float* part_lse, int split_len, int max_splits, void* hip_stream) {
+    if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !std::isfinite(scale * k_scale))
+        return ATTN_ERR_INVALID;
+    return decode_fwd_impl(q, q_st, k_cache, v_cache, kv_st, block_table, max_pages_per_seq, page_size, cache_len,
+                           dtype, batch, s_active, n_q_heads, n_kv_heads, head_dim, scale * k_scale, window, part_o,
+                           part_lse, split_len, max_splits, 1, v_scale, hip_stream);
 }
 
 int attn_decode_combine_ex(const float* part_o, const float* part_lse, const int32_t* cache_len, int split_len,

@@ -308,6 +308,261 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
     }
 }
 
+// decode_split_f8: decode_split for a K/V cache stored in FP8 E4M3 (the OCP
+// "fn" encoding; the decode page's FP8-e4m3 KV cache), with q, the partials
+// and the output as in decode_split. A stored code stands for k_scale (or
+// v_scale) times its value; k_scale is folded into the softmax scale on the
+// host and v_scale multiplies each split's output. The codes are widened
+// exactly to bf16 (gfx950's v_cvt_scalef32_pk_bf16_fp8, scale 1) and the
+// products run on the same bf16/f16 MFMAs, so the only rounding beyond the
+// 16-bit path is the cache's own.
+//
+// All cache reads are plain 16-byte register loads (non-temporal), so the
+// compiler's own wait counting covers them exactly. K is loaded straight in
+// the MFMA A-operand layout: lane (n, g) takes row n of a 16-key group and
+// the D/4 contiguous bytes [g D/4, (g+1) D/4) of it, and k-step ks of the
+// product uses d = g D/4 + 8 ks .. +8; Q's B operand uses the same d order,
+// so the sum over d is unchanged. V is loaded the same way, widened and
+// written as bf16 rows into the wave's LDS tile (decode_split's layout and
+// swizzle), from which the transpose reads build V^T. Two register sets
+// alternate: a set is refilled with block i+2 as soon as block i's K has
+// been multiplied and its V written to LDS, so two blocks are in flight
+// while block i's softmax and P V run.
+template <bool BF16, int D, int MODE, int HW>
+__global__ __launch_bounds__(64 * HW) void decode_split_f8(DecodeParams p) {
+    constexpr int NKS = D / 32;   // k-steps of S^T = K Q^T
+    constexpr int NDT = D / 16;   // 16-row d tiles of O^T
+    constexpr int SEG = D / 4;    // bytes (= codes) of a row per lane group
+    constexpr int NLD = SEG / 16; // 16-byte loads per row segment
+    static_assert(NLD >= 1, "D >= 64");
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[HW][DC_KB * D];
+    __shared__ uint32_t pages[kDecodeMaxSplitPages];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const int hk = blockIdx.x * HW + w, split = blockIdx.y, b = blockIdx.z;
+
+    const int t0 = split * p.split_len;
+    const int nrows = p.group * p.s_active;
+    const bool row_real = n < nrows;
+    const int qi = row_real ? n / p.group : 0;
+    const int qh = hk * p.group + (row_real ? n % p.group : 0);
+
+    constexpr int PPT = (kDecodeMaxSplitPages + 64 * HW - 1) / (64 * HW);
+    uint32_t pe[PPT];
+    const int spp = MODE == kDecodeFlat ? 0 : p.split_len / p.page_size;
+    if constexpr (MODE != kDecodeFlat) {
+        const uint32_t* trow = p.block_table + (int64_t)b * p.max_pages_per_seq;
+        const int first = t0 / p.page_size, last = p.max_pages_per_seq - 1;
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int i = (int)threadIdx.x + k * 64 * HW;
+            pe[k] = i < spp && last >= 0 ? trow[min(first + i, last)] : 0u;
+        }
+    }
+    // Q fragments in the permuted d order: lane (n, g), k-step ks holds d = g D/4 + 8 ks .. +8.
+    s16x8 qf[NKS];
+    {
+        const uint16_t* qrow = (const uint16_t*)p.q + (int64_t)b * p.qs.batch + (int64_t)qi * p.qs.seq +
+                               (int64_t)qh * p.qs.head + SEG * g;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            uint4 x = make_uint4(0, 0, 0, 0);
+            if (row_real) x = *(const uint4*)(qrow + 8 * ks);
+            x.x ^= p.qflip; x.y ^= p.qflip; x.z ^= p.qflip; x.w ^= p.qflip;
+            qf[ks] = __builtin_bit_cast(s16x8, x);
+        }
+    }
+    const int len = p.cache_len[b];
+    if (t0 >= len) return;
+    const int t1 = min(len, t0 + p.split_len);
+    const int qpos = len - p.s_active + qi;
+    const int64_t prow = (((int64_t)b * p.s_active + qi) * p.n_q_heads + qh) * p.max_splits + split;
+
+    int tlo = t0;
+    if (p.window > 0) tlo = max(tlo, (len - p.s_active) - p.window + 1);
+    if (tlo >= t1) {
+        if (row_real) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+                *(float4*)(p.part_o + prow * D + 16 * dt + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (g == 0) p.part_lse[prow] = -__builtin_inff();
+        }
+        return;
+    }
+    const int tb0 = t0 + ((tlo - t0) / DC_KB) * DC_KB;
+    const int nblk = (t1 - tb0 + DC_KB - 1) / DC_KB;
+    if constexpr (MODE != kDecodeFlat) {
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int i = (int)threadIdx.x + k * 64 * HW;
+            if (i < spp) pages[i] = pe[k];
+        }
+        __syncthreads();
+    }
+    // Q, cache_len and the page table are in: from here on the only loads in
+    // flight are cache blocks, so the compiler's wait counts in the loop are exact.
+    wait_vmcnt<0>();
+
+    const uint8_t* kbase = (const uint8_t*)p.k + (int64_t)hk * p.kvs.head + SEG * g;
+    const uint8_t* vbase = (const uint8_t*)p.v + (int64_t)hk * p.kvs.head + SEG * g;
+    const int64_t seq = p.kvs.seq;
+    auto row_off = [&](int t) -> int64_t {
+        if constexpr (MODE == kDecodeFlat) {
+            return (int64_t)b * p.kvs.batch + (int64_t)t * seq;
+        } else {
+            const int rel = t - t0;
+            int pi, slot;
+            if constexpr (MODE == kDecodeFast) {
+                pi = rel >> p.page_shift;
+                slot = rel & (p.page_size - 1);
+            } else {
+                pi = rel / p.page_size;
+                slot = rel - pi * p.page_size;
+            }
+            return (int64_t)pages[pi] * p.kvs.batch + (int64_t)slot * seq;
+        }
+    };
+    // Rows are clamped to the last valid token (see decode_split): rows past
+    // the end re-read finite cache data and get probability exactly 0.
+    const int tlast = t1 - 1;
+    auto tok_off = [&](int t) -> int64_t {
+        const int tc = min(t, tlast);
+        if constexpr (MODE == kDecodeFast) {
+            const int tg = tc & ~15;
+            return row_off(tg) + (int64_t)(tc - tg) * seq;
+        } else {
+            return row_off(tc);
+        }
+    };
+    // One block's raw codes: [gi][j] = 16 bytes j of this lane's segment of key row 16 gi + n.
+    auto load_block = [&](uint4 (&kr)[2][NLD], uint4 (&vr)[2][NLD], int tb) {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+            const int64_t off = tok_off(tb + 16 * gi + n);
+#pragma unroll
+            for (int j = 0; j < NLD; ++j) {
+                kr[gi][j] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(kbase + off) + j));
+                vr[gi][j] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(vbase + off) + j));
+            }
+        }
+    };
+    // 8 codes (two dwords, low byte first) -> 8 values of the product's 16-bit type as one MFMA
+    // operand (exact: every E4M3 value is a bf16 and an f16 value).
+    auto operand8 = [](uint32_t lo, uint32_t hi) __attribute__((always_inline)) {
+        uint32_t w[4];
+        if constexpr (BF16) {
+            w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+            w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+            w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+            w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+        } else {
+            w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false));
+            w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true));
+            w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false));
+            w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true));
+        }
+        return __builtin_bit_cast(s16x8, make_uint4(w[0], w[1], w[2], w[3]));
+    };
+
+    float m_i = kMaxInit, l_i = 0.f;
+    f32x4 o[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{};
+    const uint32_t one2 = BF16 ? 0x3F803F80u : 0x3C003C00u;
+    uint16_t* V = Vs[w];
+
+    auto step = [&](uint4 (&kr)[2][NLD], uint4 (&vr)[2][NLD], int it) {
+        const int tb = tb0 + it * DC_KB;
+        // (the fence keeps the scheduler from hoisting this block's code,
+        // whose loads were issued one step ago, into the previous step)
+        sched_fence();
+        // S^T = K Q^T from the registers of this block
+        f32x4 sacc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int gi = 0; gi < 2; ++gi) {
+                const uint4 c4 = kr[gi][ks / 2];
+                const s16x8 a = (ks & 1) ? operand8(c4.z, c4.w) : operand8(c4.x, c4.y);
+                sacc[gi] = mfma16x16x32<BF16>(a, qf[ks], sacc[gi]);
+            }
+        // V rows widened into the LDS tile: 16-byte chunk (SEG g / 8 + c) of row 16 gi + n
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+            const int row = 16 * gi + n;
+#pragma unroll
+            for (int j = 0; j < NLD; ++j) {
+                const uint4 c4 = vr[gi][j];
+                const s16x8 lo8 = operand8(c4.x, c4.y), hi8 = operand8(c4.z, c4.w);
+                const int c0 = SEG * g / 8 + 2 * j;
+                *(s16x8*)&V[row * D + 8 * (c0 ^ dc_vswz<D>(row))] = lo8;
+                *(s16x8*)&V[row * D + 8 * ((c0 + 1) ^ dc_vswz<D>(row))] = hi8;
+            }
+        }
+        load_block(kr, vr, tb + 2 * DC_KB);  // this set now carries block it+2 (clamped past the end)
+
+        float mx = kMaskedScore;
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = tb + 16 * gi + 4 * g + r;
+                bool keep = t < t1 && t <= qpos;
+                if (p.window > 0) keep &= t >= qpos - p.window + 1;
+                sacc[gi][r] = keep ? sacc[gi][r] : kMaskedScore;
+                mx = fmaxf(mx, sacc[gi][r]);
+            }
+        mx = max_over_groups(mx);
+        const float m_new = fmaxf(m_i, mx * p.c);
+        const float alpha = fast_exp2(m_i - m_new);
+        m_i = m_new;
+        uint32_t pk[4];
+        float psum = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 8; jj += 2) {
+            const float s0 = sacc[jj >> 2][jj & 3], s1 = sacc[jj >> 2][(jj & 3) + 1];
+            const float p0 = s0 == kMaskedScore ? 0.f : fast_exp2(fmaf(s0, p.c, -m_new));
+            const float p1 = s1 == kMaskedScore ? 0.f : fast_exp2(fmaf(s1, p.c, -m_new));
+            pk[jj / 2] = pack2_16<BF16>(p0, p1);
+            psum = dot2_16<BF16>(pk[jj / 2], one2, psum);
+        }
+        const s16x8 pb = __builtin_bit_cast(s16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+        l_i = l_i * alpha + psum;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int c = 2 * dt + ((n & 3) >> 1), half = 4 * (n & 1);
+            const int r0 = 4 * g + (n >> 2), r1 = r0 + 16;
+            const s16x4 lo = lds_read_tr16(&V[r0 * D + 8 * (c ^ dc_vswz<D>(r0)) + half]);
+            const s16x4 hi4 = lds_read_tr16(&V[r1 * D + 8 * (c ^ dc_vswz<D>(r1)) + half]);
+            o[dt] = mfma16x16x32<BF16>(concat4(lo, hi4), pb, o[dt]);
+        }
+    };
+
+    uint4 kA[2][NLD], vA[2][NLD], kB[2][NLD], vB[2][NLD];
+    load_block(kA, vA, tb0);
+    load_block(kB, vB, tb0 + DC_KB);
+    for (int it = 0; it < nblk; it += 2) {
+        step(kA, vA, it);
+        step(kB, vB, it + 1);
+    }
+    wait_vmcnt<0>();
+
+    const float l_tot = sum_over_groups(l_i);
+    const float inv = l_tot > 0.f ? p.v_scale / l_tot : 0.f;
+    if (row_real) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            *(float4*)(p.part_o + prow * D + 16 * dt + 4 * g) =
+                make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+        if (g == 0) p.part_lse[prow] = l_tot > 0.f ? (m_i + __log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
+    }
+}
+
 // One wave per output row. A split's partial row is read as float4s by
 // D / 4 lanes, so one load instruction covers 64 / (D / 4) splits; up to 32
 // instructions per lane are issued together with the matching log-sum-exps,
@@ -405,6 +660,12 @@ __global__ __launch_bounds__(64) void decode_combine(CombineParams p) {
 template <bool BF16, int D, int HW>
 static void launch_decode_hw(const DecodeParams& p, hipStream_t s) {
     const dim3 grid((unsigned)(p.n_kv_heads / HW), (unsigned)p.max_splits, (unsigned)p.batch), block(64 * HW);
+    if (p.kv_fp8) {
+        if (!p.block_table) hipLaunchKernelGGL((decode_split_f8<BF16, D, kDecodeFlat, HW>), grid, block, 0, s, p);
+        else if (p.page_shift >= 4) hipLaunchKernelGGL((decode_split_f8<BF16, D, kDecodeFast, HW>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((decode_split_f8<BF16, D, kDecodeGeneric, HW>), grid, block, 0, s, p);
+        return;
+    }
     if (!p.block_table) hipLaunchKernelGGL((decode_split<BF16, D, kDecodeFlat, HW>), grid, block, 0, s, p);
     else if (p.page_shift >= 4) hipLaunchKernelGGL((decode_split<BF16, D, kDecodeFast, HW>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((decode_split<BF16, D, kDecodeGeneric, HW>), grid, block, 0, s, p);

@@ -40,6 +40,8 @@ struct DecodeParams {
     int window, split_len, max_splits;
     float c;
     uint32_t qflip;
+    int kv_fp8;       // the cache holds FP8 E4M3 codes (decode_split_f8)
+    float v_scale;    // FP8 caches: V row = v_scale * its codes (K's scale is folded into c)
 };
 
 struct CombineParams {

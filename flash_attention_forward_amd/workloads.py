@@ -12,8 +12,11 @@ normals; the draw order is fixed per workload kind:
 * prefill: q, k, v (each ``[B, S, H, D]``), then the key "spike" positions;
 * decode:  cache_len, the page permutation, the K pool, the V pool, then q.
 
-Storage arrays are numpy: ``uint16`` bit patterns for bf16/f16 and ``float32``
-for fp32. ``as_f64`` widens a storage array exactly to float64.
+Storage arrays are numpy: ``uint16`` bit patterns for bf16/f16, ``uint8``
+bit patterns for fp8 (OCP FP8 E4M3, "e4m3fn": 1 sign, 4 exponent bits with
+bias 7, 3 mantissa bits, subnormals, no infinities, NaN = S.1111.111, largest
+finite value 448) and ``float32`` for fp32. ``as_f64`` widens a storage array
+exactly to float64.
 """
 from __future__ import annotations
 
@@ -22,8 +25,63 @@ from dataclasses import dataclass, field, replace
 
 import numpy as np
 
-DTYPES = ("f32", "f16", "bf16")
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+DTYPES = ("f32", "f16", "bf16", "fp8")
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+
+
+# --------------------------------------------------------------------------- fp8 (E4M3, OCP "fn" variant)
+def _e4m3_values() -> np.ndarray:
+    """float64 value of each of the 256 codes (NaN for the two NaN codes), from the format definition."""
+    c = np.arange(256)
+    e, m = (c >> 3) & 15, (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e.astype(np.float64) - 7.0))
+    val = np.where(c & 0x80, -mag, mag)
+    val[(c & 0x7F) == 0x7F] = np.nan
+    return val
+
+
+E4M3_VALUES = _e4m3_values()
+E4M3_MAX = 448.0
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to E4M3 (round-to-nearest-even), saturating at +-448; NaN -> 0x7F.
+    Large arrays go through torch's CPU conversion after clamping to +-448 (the same rounding:
+    the two are compared value by value in the tests); the rest follow the definition below."""
+    if np.size(x) >= 1 << 20:
+        import torch
+
+        xc = np.clip(np.ascontiguousarray(x, dtype=np.float32), -E4M3_MAX, E4M3_MAX)
+        code = torch.from_numpy(xc).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        nan = np.isnan(xc)
+        if nan.any():
+            code[nan] = 0x7F
+        return code
+    return f32_to_e4m3_bits_by_definition(x)
+
+
+def f32_to_e4m3_bits_by_definition(x: np.ndarray) -> np.ndarray:
+    """Round float32 to E4M3 (round-to-nearest-even), saturating at +-448; NaN -> 0x7F.
+    Returns the 8-bit patterns. Normal results (|x| >= 2^-6) keep 3 of the 23 float32 mantissa
+    bits with the usual add-and-shift RNE (a carry moves into the exponent), rebiased from 127 to
+    7; smaller magnitudes are multiples of 2^-9, rounded with np.rint (ties to even)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32)
+    a = np.minimum(bits & np.uint32(0x7FFFFFFF), np.uint32(0x43E00000))  # |x|, saturated at 448
+    r = (a >> np.uint32(20)) & np.uint32(1)
+    r += np.uint32(0x7FFFF)
+    r += a
+    r >>= np.uint32(20)
+    r -= np.uint32(120 << 3)  # exponent bias 127 -> 7: now the [exp:mant] code (wraps below 2^-6; unused there)
+    sub = a < np.uint32(0x3C800000)
+    if sub.any():  # multiples of 2^-9
+        r[sub] = np.rint(a[sub].view(np.float32) * np.float32(512.0)).astype(np.uint32)
+    code = r.astype(np.uint8)
+    code |= (bits >> np.uint32(24)).astype(np.uint8) & np.uint8(0x80)
+    nan = np.isnan(x)
+    if nan.any():
+        code[nan] = 0x7F
+    return code
 
 
 # --------------------------------------------------------------------------- rounding
@@ -51,6 +109,8 @@ def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
         return f32_to_f16_bits(x)
     if dtype == "f32":
         return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "fp8":
+        return f32_to_e4m3_bits(x)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -60,6 +120,8 @@ def as_f32(a: np.ndarray, dtype: str) -> np.ndarray:
         return bf16_bits_to_f32(a)
     if dtype == "f16":
         return np.ascontiguousarray(a, dtype=np.uint16).view(np.float16).astype(np.float32)
+    if dtype == "fp8":
+        return E4M3_VALUES[np.asarray(a, dtype=np.uint8)].astype(np.float32)
     return np.asarray(a, dtype=np.float32)
 
 
@@ -74,6 +136,8 @@ def to_torch(a: np.ndarray, dtype: str, device=None):
 
     if dtype == "f32":
         t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    elif dtype == "fp8":
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).view(torch.float8_e4m3fn)
     else:
         t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16))
         t = t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
@@ -87,6 +151,8 @@ def from_torch(t, dtype: str) -> np.ndarray:
     t = t.detach().to("cpu").contiguous()
     if dtype == "f32":
         return t.numpy().astype(np.float32, copy=False)
+    if dtype == "fp8":
+        return t.view(torch.uint8).numpy()
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
@@ -100,13 +166,18 @@ def normal_f32(rng: np.random.Generator, shape, chunk: int = 1 << 26) -> np.ndar
     return out.reshape(shape)
 
 
-def normal_rounded(rng: np.random.Generator, shape, dtype: str, chunk: int = 1 << 26) -> np.ndarray:
-    """N(0,1) draws rounded to ``dtype``, chunked so no full float32 copy is held."""
+def normal_rounded(rng: np.random.Generator, shape, dtype: str, chunk: int = 1 << 24,
+                   divide_by: float = 1.0) -> np.ndarray:
+    """N(0,1) draws (divided by ``divide_by``) rounded to ``dtype``, chunked so no full float32 copy
+    is held."""
     n = int(np.prod(shape))
-    out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
+    out = np.empty(n, dtype={"f32": np.float32, "fp8": np.uint8}.get(dtype, np.uint16))
     for s in range(0, n, chunk):
         e = min(n, s + chunk)
-        out[s:e] = round_to(rng.standard_normal(e - s, dtype=np.float32), dtype)
+        x = rng.standard_normal(e - s, dtype=np.float32)
+        if divide_by != 1.0:
+            x /= np.float32(divide_by)
+        out[s:e] = round_to(x, dtype)
     return out.reshape(shape)
 
 
@@ -175,6 +246,13 @@ class DecodeSpec:
     len_hi: int
     scale: float | None = None
     extra_pages: int = 0  # physical pages no sequence references
+    kv_dtype: str = ""  # storage of the K/V pools; "" = dtype (q and the output are always dtype)
+    k_scale: float = 1.0  # fp8 caches: the K row a code stands for is k_scale * its value
+    v_scale: float = 1.0
+
+    @property
+    def cache_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
 
     @property
     def scale_f32(self) -> float:
@@ -210,8 +288,12 @@ def make_decode(spec: DecodeSpec, seed: int, unused_entry: int = 0) -> DecodeInp
         table[b, : npages[b]] = perm[off : off + npages[b]]
         off += int(npages[b])
     shape = (total, ps, spec.n_kv_heads, spec.head_dim)
-    k_pool = normal_rounded(rng, shape, spec.dtype)
-    v_pool = normal_rounded(rng, shape, spec.dtype)
+    if spec.cache_dtype == "fp8":  # N(0,1) in the units the cache represents, stored as x / scale
+        k_pool = normal_rounded(rng, shape, "fp8", divide_by=spec.k_scale)
+        v_pool = normal_rounded(rng, shape, "fp8", divide_by=spec.v_scale)
+    else:
+        k_pool = normal_rounded(rng, shape, spec.cache_dtype)
+        v_pool = normal_rounded(rng, shape, spec.cache_dtype)
     q = normal_rounded(rng, (B, spec.s_active, spec.n_q_heads, spec.head_dim), spec.dtype)
     return DecodeInputs(spec, cache_len, table, k_pool, v_pool, q)
 
@@ -229,6 +311,9 @@ WORKLOADS = {
     # paged decode: 32 sequences, 1 query token, 32 q over 8 kv heads, 16-token pages
     "c5_paged_decode": DecodeSpec(32, 1, 32, 8, 128, "bf16", page_size=16, len_lo=1024, len_hi=32768),
 }
+
+# The paged-decode workload with its K/V cache in FP8 E4M3 (q and the output stay bf16).
+FP8_DECODE = replace(WORKLOADS["c5_paged_decode"], kv_dtype="fp8")
 
 WORKLOAD_SEEDS = {name: 1001 + i for i, name in enumerate(WORKLOADS)}
 

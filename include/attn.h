@@ -166,6 +166,29 @@ int attn_decode_fwd(const void* q, attn_strides q_st,
                     void* hip_stream);
 
 /*
+ * attn_decode_fwd for a K/V cache stored in FP8 E4M3 (the OCP "e4m3fn"
+ * encoding: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, NaN = S.1111.111, largest value 448) — the decode page's
+ * FP8-e4m3 KV cache ("Flash-Attention: Decode (TKG)", section "KV-cache
+ * layouts and access", flat cache: the FP8 K path). k_cache and v_cache hold one byte per element with the same
+ * layouts and strides (in elements, i.e. bytes) as for attn_decode_fwd; a
+ * stored code x stands for k_scale * value(x) (K) or v_scale * value(x) (V).
+ * q (`dtype`, f16 or bf16), the workspace and the partials are as for
+ * attn_decode_fwd, and attn_decode_combine merges them as usual. The codes
+ * are widened exactly to the 16-bit type of q before the products, so the
+ * only rounding beyond attn_decode_fwd is the cache's own. k_scale and
+ * v_scale must be finite (else ATTN_ERR_INVALID); NaN codes give NaN rows.
+ */
+int attn_decode_fwd_fp8kv(const void* q, attn_strides q_st,
+                          const uint8_t* k_cache, const uint8_t* v_cache, attn_strides kv_st,
+                          const uint32_t* block_table, int max_pages_per_seq, int page_size,
+                          const int32_t* cache_len, attn_dtype dtype, int batch, int s_active,
+                          int n_q_heads, int n_kv_heads, int head_dim, float scale,
+                          float k_scale, float v_scale, int window,
+                          float* part_o, float* part_lse, int split_len, int max_splits,
+                          void* hip_stream);
+
+/*
  * Merge of the split partials written by attn_decode_fwd with the same
  * (cache_len, split_len, max_splits, batch, s_active, n_q_heads, head_dim):
  *   M = max_s lse_s,  w_s = exp(lse_s - M),  O = sum_s w_s O_s / sum_s w_s

@@ -181,3 +181,29 @@ def test_ex_entry_points_check_like_the_plain_ones():
     assert prefill_ex(d=96, lse=FAKE) == UNSUPPORTED
     assert prefill_ex(batch=0, lse=FAKE + 2) == 0  # empty: nothing is checked or enqueued
     assert combine_ex(ms=0, sinks=FAKE) == INVALID
+
+
+def decode_fp8(**kw):
+    a = dict(q=FAKE, qs=st(32 * 128, 32 * 128, 128), k=FAKE, v=FAKE, kvs=st(16 * 8 * 128, 8 * 128, 128), bt=FAKE,
+             maxp=2048, ps=16, cl=FAKE, dtype=A.ATTN_BF16, batch=32, sa=1, hq=32, hkv=8, d=128, scale=0.088,
+             ks=1.0, vs=1.0, window=0, po=FAKE, pl=FAKE, split=512, ms=64)
+    a.update(kw)
+    return A.lib().attn_decode_fwd_fp8kv(a["q"], a["qs"], a["k"], a["v"], a["kvs"], a["bt"], a["maxp"], a["ps"],
+                                         a["cl"], a["dtype"], a["batch"], a["sa"], a["hq"], a["hkv"], a["d"],
+                                         a["scale"], a["ks"], a["vs"], a["window"], a["po"], a["pl"], a["split"],
+                                         a["ms"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=float("inf")), INVALID), (dict(vs=float("nan")), INVALID), (dict(ks=1e30, scale=1e30), INVALID),
+    (dict(kvs=st(16 * 8 * 128, 8 * 128, 8)), INVALID),  # 8-byte head stride: rows not 16-byte aligned
+    (dict(dtype=A.ATTN_F32), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(split=500), INVALID),
+    (dict(k=FAKE + 8), INVALID),
+])
+def test_decode_fp8_rejects(kw, status):
+    assert decode_fp8(**kw) == status
+
+
+def test_decode_fp8_accepts_byte_strides():
+    # 16-byte-aligned byte strides are fine for one-byte codes; an empty batch enqueues nothing
+    assert decode_fp8(batch=0) == 0

@@ -486,3 +486,38 @@ def test_sinks_rescale_the_plain_result():
     o2, l2 = oracle.attention(q, k, v, 0.6, True, 0, return_lse=True, sinks=np.full(4, -np.inf))
     np.testing.assert_array_equal(o2, o0)
     np.testing.assert_array_equal(l2, l0)
+
+
+# ----------------------------------------------------------------------------- FP8 E4M3 storage of the inputs
+def test_e4m3_decode_table_matches_torch():
+    """The generator's value of every code equals torch's float8_e4m3fn widening (a library routine)."""
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = W.E4M3_VALUES
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    assert np.array_equal(mine[~np.isnan(ref)], ref[~np.isnan(ref)])
+    assert mine[0x7E] == 448.0 and mine[1] == 2.0 ** -9 and mine[0x38] == 1.0
+
+
+def test_e4m3_rounding_is_nearest_even_and_saturating():
+    rng = np.random.default_rng(17)
+    x = np.concatenate([rng.standard_normal(200000) * s for s in (0.004, 1.0, 60.0)]).astype(np.float32)
+    mids = (W.E4M3_VALUES[1:127] + W.E4M3_VALUES[0:126]) / 2  # exact ties between neighbours
+    x = np.concatenate([x, mids.astype(np.float32), -mids.astype(np.float32), [0.0, -0.0, 448.0, 449.0, 464.0, 1e20]])
+    x = x.astype(np.float32)
+    mine = W.f32_to_e4m3_bits_by_definition(x)
+    # torch's conversion (ties to even; it turns values past the top into NaN, so compare within range)
+    within = np.abs(x) <= 448.0
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(mine[within], ref[within])
+    assert (mine[np.abs(x) > 448.0] & 0x7F == 0x7E).all()  # saturated at +-448
+    # nearest value by search over the decoded table, ties to the even code
+    small = x[:20000]
+    a = np.minimum(np.abs(small).astype(np.float64), 448.0)
+    d = np.abs(a[:, None] - W.E4M3_VALUES[None, :127])
+    cand = np.where(d == d.min(1, keepdims=True), np.arange(127)[None, :], 999)
+    even = np.where(cand % 2 == 0, cand, 999).min(1)
+    code = np.where(even < 999, even, cand.min(1)).astype(np.uint8) | np.where(np.signbit(small), 0x80, 0).astype(np.uint8)
+    np.testing.assert_array_equal(mine[:20000], code)
+    # the bulk path of the generator is the same rounding
+    big = np.tile(x, 3)
+    np.testing.assert_array_equal(W.f32_to_e4m3_bits(big), W.f32_to_e4m3_bits_by_definition(big))
