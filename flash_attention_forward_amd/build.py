@@ -18,10 +18,14 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattn.so")
 SOURCES = ["prefill.hip", "decode.hip", "attn_api.cpp"]
-# Per-source extra flags. The prefill kernels never rely on NaN propagation
-# (masked scores are a finite sentinel); without it the row maxima of MFMA
-# results compile to v_max3_f32 with no NaN-quieting copies.
-EXTRA = {"prefill.hip": ["-fno-honor-nans"]}
+# Per-source extra flags. The kernels never rely on NaN propagation (masked
+# scores are a finite sentinel); without it the row maxima of MFMA results
+# compile to v_max3_f32 with no NaN-quieting copies. The decode kernels keep
+# their MFMA accumulators in VGPRs (the VGPR form), so the occasional rescale
+# of O reads and writes them in place instead of copying them out of and
+# back into AGPRs.
+EXTRA = {"prefill.hip": ["-fno-honor-nans"],
+         "decode.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -162,6 +162,7 @@ int decode_fwd_impl(const void* q, attn_strides q_st, const void* k_cache, const
     p.qflip = q_flip_mask(scale, dtype);
     p.kv_fp8 = kv_bytes == 1;
     p.v_scale = v_scale;
+    p.lane_addr32 = (int64_t)16 * (kv_st.seq + head_dim) * kv_bytes < ((int64_t)1 << 31);
     return status_of(attn::launch_decode(p, (int)dtype, head_dim, (hipStream_t)hip_stream));
 }
 }  // namespace

@@ -46,6 +46,65 @@ __device__ __forceinline__ float sum_over_groups(float x) {
     return sum_with_other_half(x);
 }
 
+// Running max in scaled log2 units. It only moves when a row's block max
+// exceeds it by more than kDecodeLazyRescale, so O and l are rescaled rarely
+// (a wave-uniform branch); in between, probabilities are at most
+// 2^kDecodeLazyRescale, and the normalised result is the same softmax.
+constexpr float kDecodeLazyRescale = 8.0f;
+
+// Online-softmax update for one 32-key block of S^T (lane (n, g) holds keys
+// tb + 16 gi + 4 g + r of query row n, raw scores): moves m_i (rescaling l_i
+// and O when it moves) and returns this lane's P^T as the B operand of
+// O^T += V^T P^T (slot j of group g is key 4g + j for j < 4, else 16 + 4g + j - 4).
+// MASKED applies the visibility cut t < t1, t <= qpos (and the window); a
+// block that every row of the wave sees in full skips it. Hidden scores get
+// probability exactly 0 and never move m.
+template <bool BF16, bool MASKED, int NDT>
+__device__ __forceinline__ s16x8 dc_block_probs(f32x4 (&sacc)[2], f32x4 (&o)[NDT], float& m_i, float& l_i, float c,
+                                                int tb, int g, int t1, int qpos, int window) {
+    float mx = kMaskedScore;
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if constexpr (MASKED) {
+                const int t = tb + 16 * gi + 4 * g + r;
+                bool keep = t < t1 && t <= qpos;
+                if (window > 0) keep &= t >= qpos - window + 1;
+                sacc[gi][r] = keep ? sacc[gi][r] : kMaskedScore;
+            }
+            mx = fmaxf(mx, sacc[gi][r]);
+        }
+    mx = max_over_groups(mx);
+    const float m_cand = mx * c;
+    const bool grow = m_cand > m_i + kDecodeLazyRescale;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? m_cand : m_i;
+        const float alpha = fast_exp2(m_i - m_new);
+        m_i = m_new;
+        l_i *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+    }
+    const uint32_t one2 = BF16 ? 0x3F803F80u : 0x3C003C00u;  // two 16-bit 1.0s for the row-sum dot2
+    uint32_t pk[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 8; jj += 2) {
+        const float s0 = sacc[jj >> 2][jj & 3], s1 = sacc[jj >> 2][(jj & 3) + 1];
+        float p0 = fast_exp2(fmaf(s0, c, -m_i)), p1 = fast_exp2(fmaf(s1, c, -m_i));
+        if constexpr (MASKED) {
+            // (with the smallest scales, mask * c need not underflow to 0)
+            p0 = s0 == kMaskedScore ? 0.f : p0;
+            p1 = s1 == kMaskedScore ? 0.f : p1;
+        }
+        pk[jj / 2] = pack2_16<BF16>(p0, p1);
+        psum = dot2_16<BF16>(pk[jj / 2], one2, psum);
+    }
+    l_i += psum;
+    return __builtin_bit_cast(s16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+}
+
 // 16-byte chunk swizzle of a V row in LDS: chunk c of row r lives at c ^ f(r).
 // With it the 32 lanes of a transpose read (8 rows x two adjacent chunks) hit
 // 16 distinct bank groups, while each direct-to-LDS load still fills whole rows.
@@ -65,6 +124,10 @@ enum DecodeMode { kDecodeFlat = 0, kDecodeFast = 1, kDecodeGeneric = 2 };
 template <int D>
 constexpr int dc_max_heads() {
     return D >= 256 ? 1 : (D >= 128 ? 2 : 4);
+}
+template <int D>
+constexpr int dc_max_heads_f8() {
+    return D >= 256 ? 2 : 4;
 }
 
 // 16-byte chunk swizzle of a K row in LDS: the 16 lanes of a fragment read hit
@@ -190,11 +253,24 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
     // no conditional loads, each lane has exactly 2 * VLD loads per block in
     // flight and the wait counts below hold on every path.
     const int tlast = t1 - 1;
+    // Keys in [t_from, t_full) are visible to every query row of the wave.
+    const int t_full = min(t1, len - p.s_active + 1);
+    const int t_from = p.window > 0 ? len - p.window : 0;
     // FAST: offset of the 16-aligned group holding token t, plus the row within it
     auto fast_off = [&](int t) -> int64_t {
         const int tc = min(t, tlast);
         const int tg = tc & ~15;
         return row_off(tg) + (int64_t)(tc - tg) * seq;
+    };
+    // Element offset of the first row of the 16-key group at tg (FLAT, FAST), as a wave-uniform value.
+    auto group_off = [&](int tg) -> int64_t {
+        if constexpr (MODE == kDecodeFlat) {
+            return (int64_t)b * p.kvs.batch + (int64_t)tg * seq;
+        } else {
+            const int rel = tg - t0;
+            const uint32_t page = __builtin_amdgcn_readfirstlane(pages[rel >> p.page_shift]);
+            return (int64_t)page * p.kvs.batch + (int64_t)(rel & (p.page_size - 1)) * seq;
+        }
     };
     // A K or V block straight into LDS: load i writes LDS bytes [1 KB * i,
     // 1 KB * (i + 1)), lane L landing at row i * RPL + L / CPR, swizzled chunk L % CPR.
@@ -203,7 +279,29 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
     // of L2, and measured 4-6% faster than default-policy loads.
     constexpr int kStreamPolicy = 2;  // nt
     const int cs = lane % CPR;
+    // A block that ends before t1 (in FLAT and FAST mode) is addressed as a
+    // wave-uniform base per 16-key group (page entry, slot: scalar
+    // arithmetic) plus a per-lane byte offset fixed for the whole loop (row
+    // within the group, swizzled chunk), so its loads cost no vector ALU work.
+    const bool lane_addr = MODE != kDecodeGeneric && p.lane_addr32;
     auto load_rows = [&](uint16_t* dst, const uint16_t* base, int tb, bool is_k) {
+        if (lane_addr && tb + DC_KB <= t1) {
+            int64_t gofs[2];
+#pragma unroll
+            for (int gi = 0; gi < 2; ++gi) gofs[gi] = group_off(tb + 16 * gi);
+#pragma unroll
+            for (int i = 0; i < VLD; ++i) {
+                // (loop-invariant: computed once, outside the key loop)
+                const int row = i * RPL + lane / CPR;
+                const int c = cs ^ (is_k ? dc_kswz<D>(row) : dc_vswz<D>(row));
+                const uint32_t lane_off = (uint32_t)(((row & 15) * seq + 8 * c) * 2);
+                const char* gb = (const char*)(base + gofs[(i * RPL) / 16]);
+                __builtin_amdgcn_global_load_lds(gb + lane_off,
+                                                 (__attribute__((address_space(3))) void*)(dst + 512 * i), 16, 0,
+                                                 kStreamPolicy);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
             const int row = i * RPL + lane / CPR;
@@ -218,7 +316,6 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
     f32x4 o[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{};
-    const uint32_t one2 = BF16 ? 0x3F803F80u : 0x3C003C00u;
 
     // One block: wait for its loads, S^T = K Q^T, refill these K registers with
     // block it+2, online softmax, O^T += V^T P^T, refill this V tile with block it+2.
@@ -239,38 +336,10 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // K fragment reads done before the tile is refilled
         load_rows(K, kbase, tb + 2 * DC_KB, true);  // block it+2 (clamped rows when past the end)
 
-        // rows at or beyond t1 hold another row's keys: masked here
-        float mx = kMaskedScore;
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = tb + 16 * gi + 4 * g + r;
-                bool keep = t < t1 && t <= qpos;
-                if (p.window > 0) keep &= t >= qpos - p.window + 1;
-                sacc[gi][r] = keep ? sacc[gi][r] : kMaskedScore;
-                mx = fmaxf(mx, sacc[gi][r]);
-            }
-        mx = max_over_groups(mx);
-        const float m_new = fmaxf(m_i, mx * p.c);
-        const float alpha = fast_exp2(m_i - m_new);
-        m_i = m_new;
-
-        // P^T as the B operand: slot j of group g is key 4g + j (j < 4) or 16 + 4g + j - 4.
-        uint32_t pk[4];
-        float psum = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < 8; jj += 2) {
-            const float s0 = sacc[jj >> 2][jj & 3], s1 = sacc[jj >> 2][(jj & 3) + 1];
-            const float p0 = s0 == kMaskedScore ? 0.f : fast_exp2(fmaf(s0, p.c, -m_new));
-            const float p1 = s1 == kMaskedScore ? 0.f : fast_exp2(fmaf(s1, p.c, -m_new));
-            pk[jj / 2] = pack2_16<BF16>(p0, p1);
-            psum = dot2_16<BF16>(pk[jj / 2], one2, psum);
-        }
-        const s16x8 pb = __builtin_bit_cast(s16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-        l_i = l_i * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        // rows at or beyond t1 hold another row's keys: masked in the edge blocks
+        const s16x8 pb = tb + DC_KB <= t_full && tb >= t_from
+                             ? dc_block_probs<BF16, false>(sacc, o, m_i, l_i, p.c, tb, g, t1, qpos, p.window)
+                             : dc_block_probs<BF16, true>(sacc, o, m_i, l_i, p.c, tb, g, t1, qpos, p.window);
 
         // O^T[d, q] += V^T[d, keys] P^T[keys, q]; lane n of group g reads rows
         // 4g + n/4 (and 16 + ...), column 16dt + 4(n%4), receiving column 16dt + n.
@@ -317,27 +386,39 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
 // products run on the same bf16/f16 MFMAs, so the only rounding beyond the
 // 16-bit path is the cache's own.
 //
-// All cache reads are plain 16-byte register loads (non-temporal), so the
-// compiler's own wait counting covers them exactly. K is loaded straight in
-// the MFMA A-operand layout: lane (n, g) takes row n of a 16-key group and
-// the D/4 contiguous bytes [g D/4, (g+1) D/4) of it, and k-step ks of the
-// product uses d = g D/4 + 8 ks .. +8; Q's B operand uses the same d order,
-// so the sum over d is unchanged. V is loaded the same way, widened and
-// written as bf16 rows into the wave's LDS tile (decode_split's layout and
-// swizzle), from which the transpose reads build V^T. Two register sets
-// alternate: a set is refilled with block i+2 as soon as block i's K has
-// been multiplied and its V written to LDS, so two blocks are in flight
-// while block i's softmax and P V run.
+// Cache reads are plain 16-byte register loads (non-temporal), so the
+// compiler's own wait counting covers them exactly. Each load instruction
+// reads whole rows: D/16 consecutive lanes cover one row, so a 128-byte row
+// is one full-line request (a CU keeps a bounded number of requests in
+// flight, so half-line requests would halve the bytes in flight). Two
+// register sets alternate: a set is refilled with block i+2 as soon as block
+// i's codes have gone to LDS, so two blocks are in flight while block i is
+// multiplied. K's codes go to a per-wave byte tile, read back in the MFMA
+// A-operand layout with a permuted d order: lane (n, g) takes row n of a
+// 16-key group and bytes [64 j + 16 g, +16) of it, so k-step ks of the
+// product uses d = 64 (ks/2) + 16 g + 8 (ks%2) .. +8; Q's B operand uses the
+// same order, so the sum over d is unchanged. V is widened in registers and
+// written as bf16 rows into the wave's V tile (decode_split's layout and
+// swizzle), from which the transpose reads build V^T.
+template <int D>
+__device__ __forceinline__ int dc_kcswz(int row) {
+    // 16-byte chunk swizzle of the K code tile: the 16 lanes of an operand
+    // read (rows r..r+15, one chunk) hit distinct bank groups.
+    return D == 64 ? ((row >> 1) & 3) : (row & 7);
+}
+
 template <bool BF16, int D, int MODE, int HW>
 __global__ __launch_bounds__(64 * HW) void decode_split_f8(DecodeParams p) {
     constexpr int NKS = D / 32;   // k-steps of S^T = K Q^T
     constexpr int NDT = D / 16;   // 16-row d tiles of O^T
-    constexpr int SEG = D / 4;    // bytes (= codes) of a row per lane group
-    constexpr int NLD = SEG / 16; // 16-byte loads per row segment
-    static_assert(NLD >= 1, "D >= 64");
+    constexpr int NLD = D / 64;   // 16-byte operand reads per lane and 16-key group
+    constexpr int CPR = D / 16;   // 16-byte code chunks per row (= lanes per row in a load)
+    constexpr int RPI = 64 / CPR; // rows per load instruction
+    constexpr int NI = DC_KB / RPI;  // load instructions per block and tensor
+    static_assert(NLD >= 1 && RPI <= 16, "D in 64..256");
     __shared__ __attribute__((aligned(16))) uint16_t Vs[HW][DC_KB * D];
+    __shared__ __attribute__((aligned(16))) uint8_t Kc[HW][DC_KB * D];
     __shared__ uint32_t pages[kDecodeMaxSplitPages];
-
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int n = lane & 15;
@@ -362,15 +443,15 @@ __global__ __launch_bounds__(64 * HW) void decode_split_f8(DecodeParams p) {
             pe[k] = i < spp && last >= 0 ? trow[min(first + i, last)] : 0u;
         }
     }
-    // Q fragments in the permuted d order: lane (n, g), k-step ks holds d = g D/4 + 8 ks .. +8.
+    // Q fragments in the permuted d order: lane (n, g), k-step ks holds d = 64 (ks/2) + 16 g + 8 (ks%2) .. +8.
     s16x8 qf[NKS];
     {
         const uint16_t* qrow = (const uint16_t*)p.q + (int64_t)b * p.qs.batch + (int64_t)qi * p.qs.seq +
-                               (int64_t)qh * p.qs.head + SEG * g;
+                               (int64_t)qh * p.qs.head + 16 * g;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             uint4 x = make_uint4(0, 0, 0, 0);
-            if (row_real) x = *(const uint4*)(qrow + 8 * ks);
+            if (row_real) x = *(const uint4*)(qrow + 64 * (ks / 2) + 8 * (ks % 2));
             x.x ^= p.qflip; x.y ^= p.qflip; x.z ^= p.qflip; x.w ^= p.qflip;
             qf[ks] = __builtin_bit_cast(s16x8, x);
         }
@@ -406,8 +487,8 @@ __global__ __launch_bounds__(64 * HW) void decode_split_f8(DecodeParams p) {
     // flight are cache blocks, so the compiler's wait counts in the loop are exact.
     wait_vmcnt<0>();
 
-    const uint8_t* kbase = (const uint8_t*)p.k + (int64_t)hk * p.kvs.head + SEG * g;
-    const uint8_t* vbase = (const uint8_t*)p.v + (int64_t)hk * p.kvs.head + SEG * g;
+    const uint8_t* kbase = (const uint8_t*)p.k + (int64_t)hk * p.kvs.head;
+    const uint8_t* vbase = (const uint8_t*)p.v + (int64_t)hk * p.kvs.head;
     const int64_t seq = p.kvs.seq;
     auto row_off = [&](int t) -> int64_t {
         if constexpr (MODE == kDecodeFlat) {
@@ -428,6 +509,9 @@ __global__ __launch_bounds__(64 * HW) void decode_split_f8(DecodeParams p) {
     // Rows are clamped to the last valid token (see decode_split): rows past
     // the end re-read finite cache data and get probability exactly 0.
     const int tlast = t1 - 1;
+    // Keys in [t_from, t_full) are visible to every query row of the wave.
+    const int t_full = min(t1, len - p.s_active + 1);
+    const int t_from = p.window > 0 ? len - p.window : 0;
     auto tok_off = [&](int t) -> int64_t {
         const int tc = min(t, tlast);
         if constexpr (MODE == kDecodeFast) {
@@ -437,16 +521,38 @@ __global__ __launch_bounds__(64 * HW) void decode_split_f8(DecodeParams p) {
             return row_off(tc);
         }
     };
-    // One block's raw codes: [gi][j] = 16 bytes j of this lane's segment of key row 16 gi + n.
-    auto load_block = [&](uint4 (&kr)[2][NLD], uint4 (&vr)[2][NLD], int tb) {
+    // Byte offset of the first row of the 16-key group at tg (FLAT, FAST), as a wave-uniform value.
+    auto group_off = [&](int tg) -> int64_t {
+        if constexpr (MODE == kDecodeFlat) {
+            return (int64_t)b * p.kvs.batch + (int64_t)tg * seq;
+        } else {
+            const int rel = tg - t0;
+            const uint32_t page = __builtin_amdgcn_readfirstlane(pages[rel >> p.page_shift]);
+            return (int64_t)page * p.kvs.batch + (int64_t)(rel & (p.page_size - 1)) * seq;
+        }
+    };
+    // Load i of a block: lane L takes row RPI i + L / CPR, bytes [16 (L % CPR), +16).
+    const int lrow = lane / CPR, lchunk = lane % CPR;
+    // A block that ends before t1 (FLAT, FAST) is addressed as that uniform
+    // base plus this lane's fixed offset, so its loads cost no vector ALU
+    // work; other blocks clamp row by row.
+    const bool lane_addr = MODE != kDecodeGeneric && p.lane_addr32;
+    auto load_block = [&](uint4 (&kr)[NI], uint4 (&vr)[NI], int tb) {
+        if (lane_addr && tb + DC_KB <= t1) {
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-            const int64_t off = tok_off(tb + 16 * gi + n);
-#pragma unroll
-            for (int j = 0; j < NLD; ++j) {
-                kr[gi][j] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(kbase + off) + j));
-                vr[gi][j] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(vbase + off) + j));
+            for (int i = 0; i < NI; ++i) {
+                const int64_t go = group_off(tb + ((RPI * i) & ~15));
+                const uint32_t lo = (uint32_t)(((RPI * i) % 16 + lrow) * seq + 16 * lchunk);
+                kr[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(kbase + go + lo)));
+                vr[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(vbase + go + lo)));
             }
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int64_t off = tok_off(tb + RPI * i + lrow) + 16 * lchunk;
+            kr[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(kbase + off)));
+            vr[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(vbase + off)));
         }
     };
     // 8 codes (two dwords, low byte first) -> 8 values of the product's 16-bit type as one MFMA
@@ -471,68 +577,39 @@ __global__ __launch_bounds__(64 * HW) void decode_split_f8(DecodeParams p) {
     f32x4 o[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{};
-    const uint32_t one2 = BF16 ? 0x3F803F80u : 0x3C003C00u;
     uint16_t* V = Vs[w];
+    uint8_t* K = Kc[w];
 
-    auto step = [&](uint4 (&kr)[2][NLD], uint4 (&vr)[2][NLD], int it) {
+    auto step = [&](uint4 (&kr)[NI], uint4 (&vr)[NI], int it) {
         const int tb = tb0 + it * DC_KB;
         // (the fence keeps the scheduler from hoisting this block's code,
         // whose loads were issued one step ago, into the previous step)
         sched_fence();
-        // S^T = K Q^T from the registers of this block
-        f32x4 sacc[2] = {f32x4{}, f32x4{}};
+        // K codes to the byte tile, V rows widened into the bf16 tile (chunks 2c, 2c + 1)
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-            for (int gi = 0; gi < 2; ++gi) {
-                const uint4 c4 = kr[gi][ks / 2];
-                const s16x8 a = (ks & 1) ? operand8(c4.z, c4.w) : operand8(c4.x, c4.y);
-                sacc[gi] = mfma16x16x32<BF16>(a, qf[ks], sacc[gi]);
-            }
-        // V rows widened into the LDS tile: 16-byte chunk (SEG g / 8 + c) of row 16 gi + n
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-            const int row = 16 * gi + n;
-#pragma unroll
-            for (int j = 0; j < NLD; ++j) {
-                const uint4 c4 = vr[gi][j];
-                const s16x8 lo8 = operand8(c4.x, c4.y), hi8 = operand8(c4.z, c4.w);
-                const int c0 = SEG * g / 8 + 2 * j;
-                *(s16x8*)&V[row * D + 8 * (c0 ^ dc_vswz<D>(row))] = lo8;
-                *(s16x8*)&V[row * D + 8 * ((c0 + 1) ^ dc_vswz<D>(row))] = hi8;
-            }
+        for (int i = 0; i < NI; ++i) {
+            const int row = RPI * i + lrow;
+            *(uint4*)&K[row * D + 16 * (lchunk ^ dc_kcswz<D>(row))] = kr[i];
+            const s16x8 lo8 = operand8(vr[i].x, vr[i].y), hi8 = operand8(vr[i].z, vr[i].w);
+            *(s16x8*)&V[row * D + 8 * ((2 * lchunk) ^ dc_vswz<D>(row))] = lo8;
+            *(s16x8*)&V[row * D + 8 * ((2 * lchunk + 1) ^ dc_vswz<D>(row))] = hi8;
         }
         load_block(kr, vr, tb + 2 * DC_KB);  // this set now carries block it+2 (clamped past the end)
 
-        float mx = kMaskedScore;
+        // S^T = K Q^T from the code tile (one wave's own LDS writes are seen by its later reads)
+        f32x4 sacc[2] = {f32x4{}, f32x4{}};
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi)
+        for (int j = 0; j < NLD; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = tb + 16 * gi + 4 * g + r;
-                bool keep = t < t1 && t <= qpos;
-                if (p.window > 0) keep &= t >= qpos - p.window + 1;
-                sacc[gi][r] = keep ? sacc[gi][r] : kMaskedScore;
-                mx = fmaxf(mx, sacc[gi][r]);
+            for (int gi = 0; gi < 2; ++gi) {
+                const int row = 16 * gi + n;
+                const uint4 c4 = *(const uint4*)&K[row * D + 16 * ((4 * j + g) ^ dc_kcswz<D>(row))];
+                sacc[gi] = mfma16x16x32<BF16>(operand8(c4.x, c4.y), qf[2 * j], sacc[gi]);
+                sacc[gi] = mfma16x16x32<BF16>(operand8(c4.z, c4.w), qf[2 * j + 1], sacc[gi]);
             }
-        mx = max_over_groups(mx);
-        const float m_new = fmaxf(m_i, mx * p.c);
-        const float alpha = fast_exp2(m_i - m_new);
-        m_i = m_new;
-        uint32_t pk[4];
-        float psum = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < 8; jj += 2) {
-            const float s0 = sacc[jj >> 2][jj & 3], s1 = sacc[jj >> 2][(jj & 3) + 1];
-            const float p0 = s0 == kMaskedScore ? 0.f : fast_exp2(fmaf(s0, p.c, -m_new));
-            const float p1 = s1 == kMaskedScore ? 0.f : fast_exp2(fmaf(s1, p.c, -m_new));
-            pk[jj / 2] = pack2_16<BF16>(p0, p1);
-            psum = dot2_16<BF16>(pk[jj / 2], one2, psum);
-        }
-        const s16x8 pb = __builtin_bit_cast(s16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-        l_i = l_i * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        const s16x8 pb = tb + DC_KB <= t_full && tb >= t_from
+                             ? dc_block_probs<BF16, false>(sacc, o, m_i, l_i, p.c, tb, g, t1, qpos, p.window)
+                             : dc_block_probs<BF16, true>(sacc, o, m_i, l_i, p.c, tb, g, t1, qpos, p.window);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
             const int c = 2 * dt + ((n & 3) >> 1), half = 4 * (n & 1);
@@ -543,7 +620,7 @@ __global__ __launch_bounds__(64 * HW) void decode_split_f8(DecodeParams p) {
         }
     };
 
-    uint4 kA[2][NLD], vA[2][NLD], kB[2][NLD], vB[2][NLD];
+    uint4 kA[NI], vA[NI], kB[NI], vB[NI];
     load_block(kA, vA, tb0);
     load_block(kB, vB, tb0 + DC_KB);
     for (int it = 0; it < nblk; it += 2) {
@@ -660,20 +737,31 @@ __global__ __launch_bounds__(64) void decode_combine(CombineParams p) {
 template <bool BF16, int D, int HW>
 static void launch_decode_hw(const DecodeParams& p, hipStream_t s) {
     const dim3 grid((unsigned)(p.n_kv_heads / HW), (unsigned)p.max_splits, (unsigned)p.batch), block(64 * HW);
-    if (p.kv_fp8) {
-        if (!p.block_table) hipLaunchKernelGGL((decode_split_f8<BF16, D, kDecodeFlat, HW>), grid, block, 0, s, p);
-        else if (p.page_shift >= 4) hipLaunchKernelGGL((decode_split_f8<BF16, D, kDecodeFast, HW>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((decode_split_f8<BF16, D, kDecodeGeneric, HW>), grid, block, 0, s, p);
-        return;
-    }
     if (!p.block_table) hipLaunchKernelGGL((decode_split<BF16, D, kDecodeFlat, HW>), grid, block, 0, s, p);
     else if (p.page_shift >= 4) hipLaunchKernelGGL((decode_split<BF16, D, kDecodeFast, HW>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((decode_split<BF16, D, kDecodeGeneric, HW>), grid, block, 0, s, p);
 }
 
-// Waves per workgroup: the largest power of two up to dc_max_heads that divides n_kv_heads.
+template <bool BF16, int D, int HW>
+static void launch_decode_f8_hw(const DecodeParams& p, hipStream_t s) {
+    const dim3 grid((unsigned)(p.n_kv_heads / HW), (unsigned)p.max_splits, (unsigned)p.batch), block(64 * HW);
+    if (!p.block_table) hipLaunchKernelGGL((decode_split_f8<BF16, D, kDecodeFlat, HW>), grid, block, 0, s, p);
+    else if (p.page_shift >= 4) hipLaunchKernelGGL((decode_split_f8<BF16, D, kDecodeFast, HW>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((decode_split_f8<BF16, D, kDecodeGeneric, HW>), grid, block, 0, s, p);
+}
+
+// Waves per workgroup: the largest power of two up to the LDS-bound maximum
+// that divides n_kv_heads (decode_split_f8 holds one V tile per wave, decode_split four).
 template <bool BF16, int D>
 static void launch_decode_d(const DecodeParams& p, hipStream_t s) {
+    if (p.kv_fp8) {
+        constexpr int MH = dc_max_heads_f8<D>();
+        if (MH >= 8 && p.n_kv_heads % 8 == 0) launch_decode_f8_hw<BF16, D, (MH >= 8 ? 8 : 1)>(p, s);
+        else if (MH >= 4 && p.n_kv_heads % 4 == 0) launch_decode_f8_hw<BF16, D, (MH >= 4 ? 4 : 1)>(p, s);
+        else if (MH >= 2 && p.n_kv_heads % 2 == 0) launch_decode_f8_hw<BF16, D, (MH >= 2 ? 2 : 1)>(p, s);
+        else launch_decode_f8_hw<BF16, D, 1>(p, s);
+        return;
+    }
     constexpr int MH = dc_max_heads<D>();
     if (MH >= 4 && p.n_kv_heads % 4 == 0) launch_decode_hw<BF16, D, (MH >= 4 ? 4 : 1)>(p, s);
     else if (MH >= 2 && p.n_kv_heads % 2 == 0) launch_decode_hw<BF16, D, (MH >= 2 ? 2 : 1)>(p, s);

@@ -42,6 +42,7 @@ struct DecodeParams {
     uint32_t qflip;
     int kv_fp8;       // the cache holds FP8 E4M3 codes (decode_split_f8)
     float v_scale;    // FP8 caches: V row = v_scale * its codes (K's scale is folded into c)
+    int lane_addr32;  // the byte offset of row 15 of a 16-row group, plus a head row, fits 31 bits
 };
 
 struct CombineParams {
