@@ -30,9 +30,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E, published
-PREFILL = "c3_bf16_causal_32k"
-DECODE = "c5_paged_decode"
-CONTEXT = "c2_f16_gqa_causal_2k"  # the 7B-shaped 2K prefill the minfer page times
+PREFILL = "bf16_causal_32k"
+DECODE = "paged_decode_b32_d128"
+CONTEXT = "f16_gqa7_causal_2k"  # the 7B-shaped 2K prefill the minfer page times
 PAGES_CONTEXT_MS_PER_LAYER = 8.5   # minfer 8n page, results: 7B @2K prefill attention, on its own (NVIDIA) GPU
 DEFAULT_SPLIT_LEN = 1024  # decode keys per split (timed sweep: 512 and 2048 are slower on the paged workload)
 
@@ -290,20 +290,28 @@ def main():
     dlse = torch.empty((dspec.batch, dspec.s_active, dspec.n_q_heads), dtype=torch.float32, device=dev)
     for _ in range(2):
         F.attn_prefill_fwd_ex(q, k, v, o, pspec.scale_f32, True, 0, plse, psinks)
-    pev = [[ev(), ev()] for _ in range(8)]
-    for e in pev:
-        e[0].record(stream)
+    # back-to-back launches between two events (the host stays ahead of the GPU)
+    n_ex = 8
+    pev = [ev(), ev()]
+    pev[0].record(stream)
+    for _ in range(n_ex):
         F.attn_prefill_fwd_ex(q, k, v, o, pspec.scale_f32, True, 0, plse, psinks)
-        e[1].record(stream)
+    pev[1].record(stream)
     torch.cuda.synchronize()
-    pre_ex_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in pev]))
-    cev = [[ev(), ev()] for _ in range(20)]
-    for e in cev:
-        e[0].record(stream)
-        F.attn_decode_combine_ex(ws.part_o, ws.part_lse, cl, args.split_len, ms, do, dlse, dsinks)
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    comb_ex_us = float(np.mean([e[0].elapsed_time(e[1]) for e in cev])) * 1e3
+    pre_ex_ms = pev[0].elapsed_time(pev[1]) / n_ex
+    # the combine takes a few microseconds, less than one host call: each timed
+    # group of combines is queued behind a split, so the GPU never waits for the host
+    comb_ex = []
+    for _ in range(5):
+        cev = [ev(), ev()]
+        F.attn_decode_fwd(dq, kc, vc, cl, ws.part_o, ws.part_lse, args.split_len, ms, dspec.scale_f32, bt)
+        cev[0].record(stream)
+        for _ in range(n_ex):
+            F.attn_decode_combine_ex(ws.part_o, ws.part_lse, cl, args.split_len, ms, do, dlse, dsinks)
+        cev[1].record(stream)
+        torch.cuda.synchronize()
+        comb_ex.append(cev[0].elapsed_time(cev[1]) / n_ex)
+    comb_ex_us = float(np.median(comb_ex)) * 1e3
 
     flops = prefill_flops(pspec)
     kv_bytes = decode_kv_bytes(din)
@@ -344,7 +352,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic_from_profiles("prefill_c3"),
+            "traffic": traffic_from_profiles("prefill_causal_32k"),
         },
         "roofline_decode": {
             "kernel": "decode_split<bf16, D128>",
@@ -353,7 +361,16 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(split_gbps / PEAK_HBM_GBPS, 4),
-            "traffic": traffic_from_profiles("decode_c5"),
+            "traffic": traffic_from_profiles("decode_paged_b32"),
+        },
+        "roofline_decode_fp8": {
+            "kernel": "decode_split_f8<bf16 q, D128>",
+            "bound": "hbm",
+            "achieved": round(kv_bytes / 2 / (fp8_split_us * 1e-6) / 1e9, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(kv_bytes / 2 / (fp8_split_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+            "traffic": traffic_from_profiles("decode_paged_b32_fp8"),
         },
         "context": {
             "workload": CONTEXT,

@@ -301,19 +301,19 @@ def make_decode(spec: DecodeSpec, seed: int, unused_entry: int = 0) -> DecodeInp
 # --------------------------------------------------------------------------- the five workloads
 WORKLOADS = {
     # 1 head, 256 x 256, D=64, fp32, full (non-causal) softmax
-    "c1_fp32_d64": PrefillSpec(1, 1, 1, 256, 256, 64, "f32", causal=False, scale=1.0 / 8.0),
+    "fp32_d64_s256": PrefillSpec(1, 1, 1, 256, 256, 64, "f32", causal=False, scale=1.0 / 8.0),
     # 7B-shaped causal GQA prefill: 28 q-heads over 4 kv-heads, 2048 tokens, D=128, f16
-    "c2_f16_gqa_causal_2k": PrefillSpec(1, 28, 4, 2048, 2048, 128, "f16", causal=True),
+    "f16_gqa7_causal_2k": PrefillSpec(1, 28, 4, 2048, 2048, 128, "f16", causal=True),
     # long-context causal prefill: 8 q-heads over 1 kv-head, 32768 tokens, bf16, 1% K spikes x2
-    "c3_bf16_causal_32k": PrefillSpec(1, 8, 1, 32768, 32768, 128, "bf16", causal=True, spike_frac=0.01),
+    "bf16_causal_32k": PrefillSpec(1, 8, 1, 32768, 32768, 128, "bf16", causal=True, spike_frac=0.01),
     # head_dim 256 with a 1024-token sliding window on top of causal, B=2, 16 q over 8 kv heads
-    "c4_bf16_swa1024_d256": PrefillSpec(2, 16, 8, 8192, 8192, 256, "bf16", causal=True, window=1024),
+    "bf16_swa1024_d256_8k": PrefillSpec(2, 16, 8, 8192, 8192, 256, "bf16", causal=True, window=1024),
     # paged decode: 32 sequences, 1 query token, 32 q over 8 kv heads, 16-token pages
-    "c5_paged_decode": DecodeSpec(32, 1, 32, 8, 128, "bf16", page_size=16, len_lo=1024, len_hi=32768),
+    "paged_decode_b32_d128": DecodeSpec(32, 1, 32, 8, 128, "bf16", page_size=16, len_lo=1024, len_hi=32768),
 }
 
 # The paged-decode workload with its K/V cache in FP8 E4M3 (q and the output stay bf16).
-FP8_DECODE = replace(WORKLOADS["c5_paged_decode"], kv_dtype="fp8")
+FP8_DECODE = replace(WORKLOADS["paged_decode_b32_d128"], kv_dtype="fp8")
 
 WORKLOAD_SEEDS = {name: 1001 + i for i, name in enumerate(WORKLOADS)}
 

@@ -9,7 +9,7 @@ from gpu_common import check, decode_tensors, gpu_decode, oracle_decode, say, to
 
 pytestmark = pytest.mark.gpu
 
-C5 = W.WORKLOADS["c5_paged_decode"]
+C5 = W.WORKLOADS["paged_decode_b32_d128"]
 
 
 def small(seed=0, **kw):
@@ -71,7 +71,7 @@ def test_decode_flat_cache():
 
 def test_decode_full_size_sampled():
     """The full paged-decode workload, launched as the benchmark does; oracle on sampled sequences."""
-    name = "c5_paged_decode"
+    name = "paged_decode_b32_d128"
     inp = W.make_decode(C5, W.WORKLOAD_SEEDS[name])
     say("decode full size", int(inp.cache_len.sum()))
     import bench

@@ -94,7 +94,7 @@ def test_fp8_decode_full_size_sampled():
     import bench
 
     say("fp8 decode full size: generating the cache")
-    inp = W.make_decode(W.FP8_DECODE, W.WORKLOAD_SEEDS["c5_paged_decode"])
+    inp = W.make_decode(W.FP8_DECODE, W.WORKLOAD_SEEDS["paged_decode_b32_d128"])
     say("fp8 decode full size", int(inp.cache_len.sum()))
     got = gpu_fp8(inp, bench.DEFAULT_SPLIT_LEN)
     order = np.argsort(inp.cache_len)

@@ -13,13 +13,13 @@ WL = W.WORKLOADS
 # Same structure as the five workloads, at sizes the oracle finishes in seconds,
 # spanning several tiles with a ragged tail.
 SMALL = {
-    "c1_full": WL["c1_fp32_d64"],
-    "c1_ragged_causal": W.shrink(WL["c1_fp32_d64"], seqlen_q=200, seqlen_kv=200, causal=True),
-    "c1_d128_gqa_window": W.PrefillSpec(1, 4, 2, 150, 150, 128, "f32", causal=True, window=40),
-    "c1_d256": W.PrefillSpec(2, 2, 1, 97, 97, 256, "f32", causal=False),
-    "c2_ragged": W.shrink(WL["c2_f16_gqa_causal_2k"], seqlen_q=333, seqlen_kv=333),
-    "c3_ragged_spikes": W.shrink(WL["c3_bf16_causal_32k"], seqlen_q=700, seqlen_kv=700),
-    "c4_ragged": W.shrink(WL["c4_bf16_swa1024_d256"], n_q_heads=4, n_kv_heads=2, seqlen_q=600, seqlen_kv=600,
+    "fp32_full": WL["fp32_d64_s256"],
+    "fp32_ragged_causal": W.shrink(WL["fp32_d64_s256"], seqlen_q=200, seqlen_kv=200, causal=True),
+    "fp32_d128_gqa_window": W.PrefillSpec(1, 4, 2, 150, 150, 128, "f32", causal=True, window=40),
+    "fp32_d256": W.PrefillSpec(2, 2, 1, 97, 97, 256, "f32", causal=False),
+    "f16_gqa7_ragged": W.shrink(WL["f16_gqa7_causal_2k"], seqlen_q=333, seqlen_kv=333),
+    "bf16_ragged_spikes": W.shrink(WL["bf16_causal_32k"], seqlen_q=700, seqlen_kv=700),
+    "bf16_swa_d256_ragged": W.shrink(WL["bf16_swa1024_d256_8k"], n_q_heads=4, n_kv_heads=2, seqlen_q=600, seqlen_kv=600,
                           window=150),
     "bf16_d64_nocausal": W.PrefillSpec(2, 3, 3, 190, 190, 64, "bf16", causal=False),
     "f16_d256_nocausal": W.PrefillSpec(1, 2, 1, 130, 130, 256, "f16", causal=False),
@@ -47,7 +47,7 @@ def test_prefill_parity_small(name):
     check(got, ref, spec.dtype, name)
 
 
-@pytest.mark.parametrize("name", ["c2_f16_gqa_causal_2k", "c3_bf16_causal_32k", "c4_bf16_swa1024_d256"])
+@pytest.mark.parametrize("name", ["f16_gqa7_causal_2k", "bf16_causal_32k", "bf16_swa1024_d256_8k"])
 def test_prefill_parity_full_size_sampled(name):
     """Full-size workloads, launched as the benchmark launches them; oracle on sampled rows."""
     spec = WL[name]
@@ -61,12 +61,12 @@ def test_prefill_parity_full_size_sampled(name):
     assert np.isfinite(got).all()
 
 
-def test_prefill_c1_full_fp32():
-    spec = WL["c1_fp32_d64"]
-    inp = W.make_prefill(spec, seed=W.WORKLOAD_SEEDS["c1_fp32_d64"])
-    say("prefill c1 full")
-    rel = check(gpu_prefill(inp), oracle_prefill(inp), "f32", "c1")
-    say("c1 normwise rel err", rel)
+def test_prefill_fp32_full():
+    spec = WL["fp32_d64_s256"]
+    inp = W.make_prefill(spec, seed=W.WORKLOAD_SEEDS["fp32_d64_s256"])
+    say("prefill fp32 d64 full")
+    rel = check(gpu_prefill(inp), oracle_prefill(inp), "f32", "fp32_full")
+    say("fp32 full normwise rel err", rel)
 
 
 def test_empty_kv_gives_zeros():
@@ -206,7 +206,7 @@ def test_repeated_runs_bit_identical():
     torch = torch_cuda()
     import flash_attention_forward_amd as F
 
-    spec = W.shrink(WL["c3_bf16_causal_32k"], seqlen_q=4096, seqlen_kv=4096)
+    spec = W.shrink(WL["bf16_causal_32k"], seqlen_q=4096, seqlen_kv=4096)
     inp = W.make_prefill(spec, seed=10)
     q, k, v = (W.to_torch(a, "bf16", "cuda") for a in (inp.q, inp.k, inp.v))
     say("repeated runs")

@@ -70,7 +70,7 @@ def test_prefill_full_size_with_sinks_and_lse():
     from gpu_common import sample_rows
 
     torch = torch_cuda()
-    name = "c3_bf16_causal_32k"
+    name = "bf16_causal_32k"
     s = W.WORKLOADS[name]
     inp = W.make_prefill(s, seed=W.WORKLOAD_SEEDS[name])
     sinks = sinks_for(s.n_q_heads, 8)
@@ -112,7 +112,7 @@ def test_decode_lse_and_sinks(kw, split_len):
     import flash_attention_forward_amd as F
 
     torch = torch_cuda()
-    spec = W.shrink(W.WORKLOADS["c5_paged_decode"], batch=6, len_lo=kw.get("len_lo", 1), len_hi=2500,
+    spec = W.shrink(W.WORKLOADS["paged_decode_b32_d128"], batch=6, len_lo=kw.get("len_lo", 1), len_hi=2500,
                     **{k: v for k, v in kw.items() if k != "len_lo"})
     inp = W.make_decode(spec, seed=11)
     sinks = sinks_for(spec.n_q_heads, 9)
@@ -133,7 +133,7 @@ def test_decode_without_sinks_lse_matches_oracle_and_neg_inf_is_none():
     import flash_attention_forward_amd as F
 
     torch = torch_cuda()
-    spec = W.shrink(W.WORKLOADS["c5_paged_decode"], batch=5, len_lo=1, len_hi=3000)
+    spec = W.shrink(W.WORKLOADS["paged_decode_b32_d128"], batch=5, len_lo=1, len_hi=3000)
     inp = W.make_decode(spec, seed=12)
     t = decode_tensors(inp)
     say("decode lse without sinks")

@@ -409,7 +409,7 @@ def test_decode_needles_follow_page_table():
 
 # ----------------------------------------------------------------------------- input generators
 def test_generators_are_seeded_and_round_to_nearest_even():
-    spec = W.shrink(W.WORKLOADS["c3_bf16_causal_32k"], seqlen_q=300, seqlen_kv=300)
+    spec = W.shrink(W.WORKLOADS["bf16_causal_32k"], seqlen_q=300, seqlen_kv=300)
     a, b = W.make_prefill(spec, 7), W.make_prefill(spec, 7)
     assert all(np.array_equal(x, y) for x, y in [(a.q, b.q), (a.k, b.k), (a.v, b.v)])
     assert a.spike_positions.shape == (1, 3) and len(set(a.spike_positions[0])) == 3
