@@ -247,6 +247,26 @@ def main():
     torch.cuda.synchronize()
     ctx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in cev]))
 
+    # packed prompts of different lengths (attn_prefill_varlen_fwd): 10 back-to-back launches
+    vspec = W.VARLEN_SPEC
+    vin = W.make_varlen(vspec, W.VARLEN_SEED)
+    vq, vk, vv = (W.to_torch(a, vspec.dtype, dev) for a in (vin.q, vin.k, vin.v))
+    vo = torch.empty_like(vq)
+    vcq = torch.from_numpy(vin.cu_q.astype(np.int32)).to(dev)
+    vck = torch.from_numpy(vin.cu_kv.astype(np.int32)).to(dev)
+    vmq, vmk = int(vin.lens_q.max()), int(vin.lens_kv.max())
+    for _ in range(3):
+        F.attn_prefill_varlen_fwd(vq, vk, vv, vo, vcq, vck, vmq, vmk, vspec.scale_f32, True)
+    vev = [ev(), ev()]
+    vev[0].record(stream)
+    for _ in range(10):
+        F.attn_prefill_varlen_fwd(vq, vk, vv, vo, vcq, vck, vmq, vmk, vspec.scale_f32, True)
+    vev[1].record(stream)
+    torch.cuda.synchronize()
+    varlen_ms = vev[0].elapsed_time(vev[1]) / 10
+    varlen_flops = 4.0 * vspec.head_dim * vspec.n_q_heads * W.varlen_visible_pairs(vin)
+    del vq, vk, vv, vo
+
     def time_decode(qq, kk, vv, table, w, out, reps=20):
         for _ in range(3):
             F.attn_decode_fwd(qq, kk, vv, cl, w.part_o, w.part_lse, args.split_len, ms, dspec.scale_f32, table)
@@ -378,6 +398,16 @@ def main():
             "tflops": round(prefill_flops(cspec) / (ctx_ms * 1e-3) / 1e12, 2),
             "pages_ms_per_layer": PAGES_CONTEXT_MS_PER_LAYER,
             "pages_hardware": "unnamed NVIDIA GPU (minfer 8n page); context only",
+        },
+        "varlen": {
+            "workload": W.VARLEN,
+            "sequences": vspec.batch,
+            "total_tokens": int(vin.cu_q[-1]),
+            "flops": varlen_flops,
+            "ms": round(varlen_ms, 4),
+            "tflops": round(varlen_flops / (varlen_ms * 1e-3) / 1e12, 2),
+            "frac_of_peak": round(varlen_flops / (varlen_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "note": "packed causal prompts, 28/4 heads, D128, bf16, lengths uniform in [256, 4096]",
         },
         "sinks_and_lse": {
             "prefill_ex_ms": round(pre_ex_ms, 4),

@@ -13,7 +13,9 @@ from .attn import (  # noqa: F401
     attn_decode_fwd_fp8kv,
     attn_prefill_fwd,
     attn_prefill_fwd_ex,
+    attn_prefill_varlen_fwd,
     decode,
     lib,
     prefill,
+    prefill_varlen,
 )

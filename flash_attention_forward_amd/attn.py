@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libattn.so")
 
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "kernel launch failed"}
-SYMBOLS = ("attn_prefill_fwd", "attn_prefill_fwd_ex", "attn_decode_fwd", "attn_decode_fwd_fp8kv",
+SYMBOLS = ("attn_prefill_fwd", "attn_prefill_fwd_ex", "attn_prefill_varlen_fwd", "attn_decode_fwd", "attn_decode_fwd_fp8kv",
            "attn_decode_combine", "attn_decode_combine_ex", "attn_decode_workspace_size", "attn_status_string")
 
 
@@ -53,6 +53,9 @@ def lib() -> ctypes.CDLL:
     L.attn_prefill_fwd_ex.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, i32, i32, i32, i32, i32,
                                       i32, i32, f32, i32, i32, vp, vp, vp]
     L.attn_prefill_fwd_ex.restype = i32
+    L.attn_prefill_varlen_fwd.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, i32, i32, i32, i32, vp,
+                                          vp, i32, i32, i32, f32, i32, i32, vp, vp, vp]
+    L.attn_prefill_varlen_fwd.restype = i32
     L.attn_decode_fwd.argtypes = [vp, Strides, vp, vp, Strides, vp, i32, i32, vp, i32, i32, i32, i32, i32, i32,
                                   f32, i32, vp, vp, i32, i32, vp]
     L.attn_decode_fwd.restype = i32
@@ -152,6 +155,44 @@ def attn_prefill_fwd_ex(q, k, v, o, scale: float, causal: bool, window: int = 0,
     _check(_name, rc)
 
 
+def _strides3(t, name: str) -> Strides:
+    """Strides of a packed [tokens, heads, head_dim] tensor (the batch stride is unused)."""
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError(f"{name} must be 3-D [tokens, heads, head_dim] with a contiguous last dim")
+    return Strides(0, t.stride(0), t.stride(1))
+
+
+def attn_prefill_varlen_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int, max_seqlen_kv: int,
+                            scale: float, causal: bool, window: int = 0, lse=None, sinks=None, stream=None) -> None:
+    """Packed sequences: q, o [total_q, Hq, D]; k, v [total_kv, Hkv, D]; cu_seqlens_* int32 [B + 1] on the GPU.
+    lse: float32 [total_q, Hq] out; sinks: float32 [Hq] in; both optional."""
+    import torch
+
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (cu_seqlens_q, "cu_seqlens_q"),
+                 (cu_seqlens_kv, "cu_seqlens_kv")):
+        _gpu(t, n)
+    Tq, Hq, D = q.shape
+    Tk, Hkv, Dk = k.shape
+    if v.shape != k.shape or o.shape != q.shape or Dk != D:
+        raise ValueError("shape mismatch between q, k, v, o")
+    if not (k.dtype == v.dtype == o.dtype == q.dtype):
+        raise TypeError("q, k, v, o must share one dtype")
+    for c, n in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_kv, "cu_seqlens_kv")):
+        if c.dtype != torch.int32 or c.dim() != 1 or not c.is_contiguous():
+            raise TypeError(f"{n} must be a contiguous int32 vector")
+    if cu_seqlens_q.numel() != cu_seqlens_kv.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_kv must both hold batch + 1 offsets")
+    B = cu_seqlens_q.numel() - 1
+    lse = _f32_vec(lse, "lse", Tq * Hq)
+    sinks = _f32_vec(sinks, "sinks", Hq)
+    rc = lib().attn_prefill_varlen_fwd(_ptr(q), _strides3(q, "q"), _ptr(k), _strides3(k, "k"), _ptr(v),
+                                       _strides3(v, "v"), _ptr(o), _strides3(o, "o"), _dtype_code(q), B, Hq, Hkv,
+                                       _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), int(max_seqlen_q), int(max_seqlen_kv),
+                                       D, float(scale), int(bool(causal)), int(window), _ptr(lse), _ptr(sinks),
+                                       _stream(stream))
+    _check("attn_prefill_varlen_fwd", rc)
+
+
 def attn_decode_fwd(q, k_cache, v_cache, cache_len, part_o, part_lse, split_len: int, max_splits: int,
                     scale: float, block_table=None, window: int = 0, stream=None) -> None:
     """Split-KV partials. Paged if block_table is given ([B, max_pages] uint32 stored as int32)."""
@@ -242,6 +283,31 @@ def prefill(q, k, v, scale: float | None = None, causal: bool = False, window: i
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
     attn_prefill_fwd_ex(q, k, v, o, sc, causal, window, lse, sinks, stream)
     return (o, lse) if return_lse else o
+
+
+def prefill_varlen(q, k, v, seqlens_q, seqlens_kv=None, scale: float | None = None, causal: bool = False,
+                   window: int = 0, out=None, stream=None, sinks=None, return_lse: bool = False):
+    """Packed-sequence prefill from per-sequence lengths (host ints); the offsets go to the GPU as int32."""
+    import torch
+
+    seqlens_kv = seqlens_q if seqlens_kv is None else seqlens_kv
+    if len(seqlens_q) != len(seqlens_kv):
+        raise ValueError("one q length and one k/v length per sequence")
+    cu_q = torch.tensor([0] + list(_cumsum(seqlens_q)), dtype=torch.int32, device=q.device)
+    cu_k = torch.tensor([0] + list(_cumsum(seqlens_kv)), dtype=torch.int32, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if return_lse else None
+    sc = default_scale(q.shape[-1]) if scale is None else scale
+    attn_prefill_varlen_fwd(q, k, v, o, cu_q, cu_k, max(seqlens_q, default=0), max(seqlens_kv, default=0), sc, causal,
+                            window, lse, sinks, stream)
+    return (o, lse) if return_lse else o
+
+
+def _cumsum(xs):
+    t = 0
+    for x in xs:
+        t += int(x)
+        yield t
 
 
 class DecodeWorkspace:

@@ -62,10 +62,17 @@ const char* attn_status_string(int status) {
     }
 }
 
-int attn_prefill_fwd_ex(const void* q, attn_strides q_st, const void* k, attn_strides k_st, const void* v,
-                        attn_strides v_st, void* o, attn_strides o_st, attn_dtype dtype, int batch, int n_q_heads,
-                        int n_kv_heads, int seqlen_q, int seqlen_kv, int head_dim, float scale, int causal,
-                        int window, float* lse, const float* sinks, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+// Shared by the prefill entry points. With cu_seqlens_q != NULL the sequences
+// are packed (seqlen_q / seqlen_kv are then the largest lengths and the batch
+// strides are not used).
+int prefill_impl(const void* q, attn_strides q_st, const void* k, attn_strides k_st, const void* v,
+                 attn_strides v_st, void* o, attn_strides o_st, attn_dtype dtype, int batch, int n_q_heads,
+                 int n_kv_heads, int seqlen_q, int seqlen_kv, int head_dim, float scale, int causal, int window,
+                 float* lse, const float* sinks, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                 void* hip_stream) {
     if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
     if (batch < 0 || n_q_heads < 0 || n_kv_heads < 0 || seqlen_q < 0 || seqlen_kv < 0 || head_dim <= 0)
         return ATTN_ERR_INVALID;
@@ -80,6 +87,8 @@ int attn_prefill_fwd_ex(const void* q, attn_strides q_st, const void* k, attn_st
     if (!strides_ok(q_st, eb) || !strides_ok(k_st, eb) || !strides_ok(v_st, eb) || !strides_ok(o_st, eb))
         return ATTN_ERR_INVALID;
     if (!aligned4(lse) || !aligned4(sinks)) return ATTN_ERR_INVALID;
+    if ((cu_seqlens_q == nullptr) != (cu_seqlens_kv == nullptr)) return ATTN_ERR_INVALID;
+    if (cu_seqlens_q && (!aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_kv))) return ATTN_ERR_INVALID;
     // lane offsets inside one 64-row K/V tile are kept in 32 bits
     if (k_st.seq * 64 + head_dim >= ((int64_t)1 << 31) || v_st.seq * 64 + head_dim >= ((int64_t)1 << 31))
         return ATTN_ERR_UNSUPPORTED;
@@ -90,14 +99,39 @@ int attn_prefill_fwd_ex(const void* q, attn_strides q_st, const void* k, attn_st
     p.q = q; p.k = k; p.v = v; p.o = o;
     p.qs = conv(q_st); p.ks = conv(k_st); p.vs = conv(v_st); p.os = conv(o_st);
     p.batch = batch; p.n_q_heads = n_q_heads; p.n_kv_heads = n_kv_heads; p.group = n_q_heads / n_kv_heads;
-    p.seqlen_q = seqlen_q; p.seqlen_kv = seqlen_kv; p.off = seqlen_kv - seqlen_q;
+    p.seqlen_q = seqlen_q; p.seqlen_kv = seqlen_kv;
     p.window = window > 0 ? window : 0;
     p.c = scaled_log2e(scale, dtype == ATTN_F32 ? 1e-30 : 1e-8);
     p.qflip = q_flip_mask(scale, dtype);
     p.lse = lse;
     p.sinks = sinks;
+    p.cu_seqlens_q = cu_seqlens_q;
+    p.cu_seqlens_kv = cu_seqlens_kv;
     const int mask = !causal ? attn::kMaskNone : (p.window > 0 ? attn::kMaskCausalWindow : attn::kMaskCausal);
     return status_of(attn::launch_prefill(p, (int)dtype, head_dim, mask, (hipStream_t)hip_stream));
+}
+}  // namespace
+
+extern "C" {
+
+int attn_prefill_fwd_ex(const void* q, attn_strides q_st, const void* k, attn_strides k_st, const void* v,
+                        attn_strides v_st, void* o, attn_strides o_st, attn_dtype dtype, int batch, int n_q_heads,
+                        int n_kv_heads, int seqlen_q, int seqlen_kv, int head_dim, float scale, int causal,
+                        int window, float* lse, const float* sinks, void* hip_stream) {
+    return prefill_impl(q, q_st, k, k_st, v, v_st, o, o_st, dtype, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_kv,
+                        head_dim, scale, causal, window, lse, sinks, nullptr, nullptr, hip_stream);
+}
+
+int attn_prefill_varlen_fwd(const void* q, attn_strides q_st, const void* k, attn_strides k_st, const void* v,
+                            attn_strides v_st, void* o, attn_strides o_st, attn_dtype dtype, int batch,
+                            int n_q_heads, int n_kv_heads, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_kv, int max_seqlen_q, int max_seqlen_kv, int head_dim,
+                            float scale, int causal, int window, float* lse, const float* sinks,
+                            void* hip_stream) {
+    if (batch > 0 && (!cu_seqlens_q || !cu_seqlens_kv)) return ATTN_ERR_INVALID;
+    return prefill_impl(q, q_st, k, k_st, v, v_st, o, o_st, dtype, batch, n_q_heads, n_kv_heads, max_seqlen_q,
+                        max_seqlen_kv, head_dim, scale, causal, window, lse, sinks, cu_seqlens_q, cu_seqlens_kv,
+                        hip_stream);
 }
 
 int attn_prefill_fwd(const void* q, attn_strides q_st, const void* k, attn_strides k_st, const void* v,

@@ -17,13 +17,18 @@ struct PrefillParams {
     void* o;
     Strides3 qs, ks, vs, os;
     int batch, n_q_heads, n_kv_heads, group;  // group = n_q_heads / n_kv_heads
-    int seqlen_q, seqlen_kv, off;              // off = seqlen_kv - seqlen_q
+    int seqlen_q, seqlen_kv;                   // per sequence, or the largest ones with cu_seqlens_*
     int window;                                // > 0 only together with causal
     int n_q_tiles;
     float c;          // |scale| * log2(e): scores are kept in scaled log2 units
     uint32_t qflip;   // 0x80008000 (16-bit) / 0x80000000 (f32) flips Q's sign when scale < 0
     float* lse;           // NULL, or [batch, seqlen_q, n_q_heads] natural-log log-sum-exp per row
     const float* sinks;   // NULL, or [n_q_heads] sink logits (scaled-score units)
+    // NULL, or packed sequences: [batch + 1] cumulative row offsets; sequence b
+    // owns q/o rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) and k/v rows
+    // [cu_seqlens_kv[b], cu_seqlens_kv[b+1]) (batch strides unused; lse is [total_q, n_q_heads])
+    const int32_t* cu_seqlens_q;
+    const int32_t* cu_seqlens_kv;
 };
 
 struct DecodeParams {

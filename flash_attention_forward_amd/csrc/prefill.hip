@@ -92,40 +92,58 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     const int h = bh % p.n_q_heads;
     const int hk = h / p.group;
 
+    // Sequence b's sizes and the element offsets of its first rows: sequences
+    // of one fixed size, or packed sequences delimited by cumulative offsets.
+    int sq = p.seqlen_q, skv = p.seqlen_kv;
+    int64_t q_at = (int64_t)b * p.qs.batch, k_at = (int64_t)b * p.ks.batch, v_at = (int64_t)b * p.vs.batch,
+            o_at = (int64_t)b * p.os.batch, lse_at = (int64_t)b * p.seqlen_q;
+    if (p.cu_seqlens_q) {
+        const int qs0 = p.cu_seqlens_q[b], ks0 = p.cu_seqlens_kv[b];
+        sq = min(p.cu_seqlens_q[b + 1] - qs0, p.seqlen_q);
+        skv = p.cu_seqlens_kv[b + 1] - ks0;
+        q_at = (int64_t)qs0 * p.qs.seq;
+        o_at = (int64_t)qs0 * p.os.seq;
+        lse_at = qs0;
+        k_at = (int64_t)ks0 * p.ks.seq;
+        v_at = (int64_t)ks0 * p.vs.seq;
+    }
+    const int off = skv - sq;  // query row i sits at position i + off
+
     const int q0 = qt * PF_BM;
-    const int qlast = min(q0 + PF_BM, p.seqlen_q) - 1;
-    int kv_lo = 0, kv_hi = p.seqlen_kv;
-    if (MASK >= kMaskCausal) kv_hi = min(kv_hi, qlast + p.off + 1);
-    if (MASK == kMaskCausalWindow) kv_lo = max(0, q0 + p.off - p.window + 1);
+    if (q0 >= sq) return;  // a tile past this sequence's end (packed sequences only)
+    const int qlast = min(q0 + PF_BM, sq) - 1;
+    int kv_lo = 0, kv_hi = skv;
+    if (MASK >= kMaskCausal) kv_hi = min(kv_hi, qlast + off + 1);
+    if (MASK == kMaskCausalWindow) kv_lo = max(0, q0 + off - p.window + 1);
     const int j_begin = kv_lo / PF_BN;
     const int j_end = kv_hi > kv_lo ? (kv_hi + PF_BN - 1) / PF_BN : j_begin;
 
     const int wq0 = q0 + 32 * w;                   // first row of this wave
-    const int wq1 = min(wq0 + 31, p.seqlen_q - 1); // last valid row of this wave
-    const bool wave_live = wq0 < p.seqlen_q;
+    const int wq1 = min(wq0 + 31, sq - 1); // last valid row of this wave
+    const bool wave_live = wq0 < sq;
     const int my_q = wq0 + l32;                    // the query row this lane owns
-    const int my_pos = my_q + p.off;
+    const int my_pos = my_q + off;
 
     // Q fragments: B operand of S^T = K Q^T (lane: row l32, d = 16s + 8hf .. +8).
     s16x8 qf[D / 16];
     {
-        const uint16_t* qrow = (const uint16_t*)p.q + (int64_t)b * p.qs.batch + (int64_t)my_q * p.qs.seq +
+        const uint16_t* qrow = (const uint16_t*)p.q + q_at + (int64_t)my_q * p.qs.seq +
                                (int64_t)h * p.qs.head + 8 * hf;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
             uint4 x = make_uint4(0, 0, 0, 0);
-            if (my_q < p.seqlen_q) x = *(const uint4*)(qrow + 16 * s);
+            if (my_q < sq) x = *(const uint4*)(qrow + 16 * s);
             x.x ^= p.qflip; x.y ^= p.qflip; x.z ^= p.qflip; x.w ^= p.qflip;
             qf[s] = __builtin_bit_cast(s16x8, x);
         }
     }
 
-    const uint16_t* kbase = (const uint16_t*)p.k + (int64_t)b * p.ks.batch + (int64_t)hk * p.ks.head;
-    const uint16_t* vbase = (const uint16_t*)p.v + (int64_t)b * p.vs.batch + (int64_t)hk * p.vs.head;
+    const uint16_t* kbase = (const uint16_t*)p.k + k_at + (int64_t)hk * p.ks.head;
+    const uint16_t* vbase = (const uint16_t*)p.v + v_at + (int64_t)hk * p.vs.head;
     // Tile rows outside [kv_lo, seqlen_kv) are loaded as copies of the nearest
     // valid row: they are masked out (probability exactly 0) and no memory
     // outside the visible key range is touched. Every load is unconditional.
-    const int key_min = kv_lo, key_max = p.seqlen_kv - 1;
+    const int key_min = kv_lo, key_max = skv - 1;
     // Tiles are filled with buffer loads straight into LDS: the tile's first
     // row is the buffer base (a uniform descriptor), lane offsets are 32-bit
     // byte offsets. Direct load i (0 <= i < TILE/512) covers tile rows RPL*i
@@ -217,15 +235,15 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     auto tile_empty = [&](int j) __attribute__((always_inline)) {
         const int kv0 = j * PF_BN;
         bool e = !wave_live || j >= j_end;
-        if (MASK >= kMaskCausal) e |= kv0 > wq1 + p.off;
-        if (MASK == kMaskCausalWindow) e |= kv0 + PF_BN - 1 < wq0 + p.off - p.window + 1;
+        if (MASK >= kMaskCausal) e |= kv0 > wq1 + off;
+        if (MASK == kMaskCausalWindow) e |= kv0 + PF_BN - 1 < wq0 + off - p.window + 1;
         return e;
     };
     auto tile_full = [&](int j) __attribute__((always_inline)) {
         const int kv0 = j * PF_BN;
-        bool f = kv0 + PF_BN <= p.seqlen_kv;
-        if (MASK >= kMaskCausal) f &= kv0 + PF_BN - 1 <= wq0 + p.off;
-        if (MASK == kMaskCausalWindow) f &= kv0 >= wq1 + p.off - p.window + 1;
+        bool f = kv0 + PF_BN <= skv;
+        if (MASK >= kMaskCausal) f &= kv0 + PF_BN - 1 <= wq0 + off;
+        if (MASK == kMaskCausalWindow) f &= kv0 >= wq1 + off - p.window + 1;
         return f;
     };
 
@@ -283,7 +301,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
-            bool keep = key < p.seqlen_kv;
+            bool keep = key < skv;
             if (MASK >= kMaskCausal) keep &= key <= my_pos;
             if (MASK == kMaskCausalWindow) keep &= key >= my_pos - p.window + 1;
             sacc[r] = keep ? sacc[r] : kMaskedScore;
@@ -477,11 +495,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     float m_fin = m_i;
     const float osc = p.sinks ? fold_sink(p.sinks[h] * kLog2e, m_fin, l_tot) : 1.f;
     const float inv = l_tot > 0.f ? osc / l_tot : 0.f;
-    if (p.lse && hf == 0 && wave_live && my_q < p.seqlen_q)
-        p.lse[((int64_t)b * p.seqlen_q + my_q) * p.n_q_heads + h] =
+    if (p.lse && hf == 0 && wave_live && my_q < sq)
+        p.lse[(lse_at + my_q) * p.n_q_heads + h] =
             l_tot > 0.f ? (m_fin + __log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
-    if (wave_live && my_q < p.seqlen_q) {
-        uint16_t* orow = (uint16_t*)p.o + (int64_t)b * p.os.batch + (int64_t)my_q * p.os.seq +
+    if (wave_live && my_q < sq) {
+        uint16_t* orow = (uint16_t*)p.o + o_at + (int64_t)my_q * p.os.seq +
                          (int64_t)h * p.os.head;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
@@ -512,19 +530,37 @@ __global__ __launch_bounds__(256) void prefill_f32(PrefillParams p) {
     const int qt = p.n_q_tiles - 1 - (int)(blockIdx.x / nbh);
     const int bh = blockIdx.x % nbh;
     const int b = bh / p.n_q_heads, h = bh % p.n_q_heads, hk = h / p.group;
+
+    // Sequence b's sizes and the element offsets of its first rows: sequences
+    // of one fixed size, or packed sequences delimited by cumulative offsets.
+    int sq = p.seqlen_q, skv = p.seqlen_kv;
+    int64_t q_at = (int64_t)b * p.qs.batch, k_at = (int64_t)b * p.ks.batch, v_at = (int64_t)b * p.vs.batch,
+            o_at = (int64_t)b * p.os.batch, lse_at = (int64_t)b * p.seqlen_q;
+    if (p.cu_seqlens_q) {
+        const int qs0 = p.cu_seqlens_q[b], ks0 = p.cu_seqlens_kv[b];
+        sq = min(p.cu_seqlens_q[b + 1] - qs0, p.seqlen_q);
+        skv = p.cu_seqlens_kv[b + 1] - ks0;
+        q_at = (int64_t)qs0 * p.qs.seq;
+        o_at = (int64_t)qs0 * p.os.seq;
+        lse_at = qs0;
+        k_at = (int64_t)ks0 * p.ks.seq;
+        v_at = (int64_t)ks0 * p.vs.seq;
+    }
+    const int off = skv - sq;  // query row i sits at position i + off
     const int q0 = qt * F32_BM;
-    const int qlast = min(q0 + F32_BM, p.seqlen_q) - 1;
-    int kv_lo = 0, kv_hi = p.seqlen_kv;
-    if (MASK >= kMaskCausal) kv_hi = min(kv_hi, qlast + p.off + 1);
-    if (MASK == kMaskCausalWindow) kv_lo = max(0, q0 + p.off - p.window + 1);
+    if (q0 >= sq) return;  // a tile past this sequence's end (packed sequences only)
+    const int qlast = min(q0 + F32_BM, sq) - 1;
+    int kv_lo = 0, kv_hi = skv;
+    if (MASK >= kMaskCausal) kv_hi = min(kv_hi, qlast + off + 1);
+    if (MASK == kMaskCausalWindow) kv_lo = max(0, q0 + off - p.window + 1);
     const int j_begin = kv_lo / F32_BN;
     const int j_end = kv_hi > kv_lo ? (kv_hi + F32_BN - 1) / F32_BN : j_begin;
 
-    const int my_q = q0 + r, my_pos = my_q + p.off;
-    const bool live = my_q < p.seqlen_q;
+    const int my_q = q0 + r, my_pos = my_q + off;
+    const bool live = my_q < sq;
     float qv[DQ], acc[DQ];
     {
-        const float* qrow = (const float*)p.q + (int64_t)b * p.qs.batch + (int64_t)my_q * p.qs.seq +
+        const float* qrow = (const float*)p.q + q_at + (int64_t)my_q * p.qs.seq +
                             (int64_t)h * p.qs.head + qd * DQ;
 #pragma unroll
         for (int e = 0; e < DQ; e += 4) {
@@ -537,8 +573,8 @@ __global__ __launch_bounds__(256) void prefill_f32(PrefillParams p) {
 #pragma unroll
         for (int e = 0; e < DQ; ++e) acc[e] = 0.f;
     }
-    const float* kbase = (const float*)p.k + (int64_t)b * p.ks.batch + (int64_t)hk * p.ks.head;
-    const float* vbase = (const float*)p.v + (int64_t)b * p.vs.batch + (int64_t)hk * p.vs.head;
+    const float* kbase = (const float*)p.k + k_at + (int64_t)hk * p.ks.head;
+    const float* vbase = (const float*)p.v + v_at + (int64_t)hk * p.vs.head;
     float m_i = kMaxInit, l_i = 0.f;
 
     for (int j = j_begin; j < j_end; ++j) {
@@ -547,7 +583,7 @@ __global__ __launch_bounds__(256) void prefill_f32(PrefillParams p) {
         for (int c = tid; c < F32_BN * D / 4; c += 256) {
             const int row = c / (D / 4), col = (c % (D / 4)) * 4;
             float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
-            if (kv0 + row < p.seqlen_kv && kv0 + row >= kv_lo) {
+            if (kv0 + row < skv && kv0 + row >= kv_lo) {
                 kx = *(const float4*)(kbase + (int64_t)(kv0 + row) * p.ks.seq + col);
                 vx = *(const float4*)(vbase + (int64_t)(kv0 + row) * p.vs.seq + col);
             }
@@ -566,7 +602,7 @@ __global__ __launch_bounds__(256) void prefill_f32(PrefillParams p) {
             part += __shfl_xor(part, 1);
             part += __shfl_xor(part, 2);
             const int key = kv0 + kk;
-            bool keep = key < p.seqlen_kv;
+            bool keep = key < skv;
             if (MASK >= kMaskCausal) keep &= key <= my_pos;
             if (MASK == kMaskCausalWindow) keep &= key >= my_pos - p.window + 1;
             s[kk] = keep ? part : kMaskedScore;
@@ -591,9 +627,9 @@ __global__ __launch_bounds__(256) void prefill_f32(PrefillParams p) {
         const float osc = p.sinks ? fold_sink(p.sinks[h] * kLog2e, m_fin, l_i) : 1.f;
         const float inv = l_i > 0.f ? osc / l_i : 0.f;
         if (p.lse && qd == 0)
-            p.lse[((int64_t)b * p.seqlen_q + my_q) * p.n_q_heads + h] =
+            p.lse[(lse_at + my_q) * p.n_q_heads + h] =
                 l_i > 0.f ? (m_fin + __log2f(l_i)) * 0.69314718055994531f : -__builtin_inff();
-        float* orow = (float*)p.o + (int64_t)b * p.os.batch + (int64_t)my_q * p.os.seq + (int64_t)h * p.os.head +
+        float* orow = (float*)p.o + o_at + (int64_t)my_q * p.os.seq + (int64_t)h * p.os.head +
                       qd * DQ;
 #pragma unroll
         for (int e = 0; e < DQ; e += 4)

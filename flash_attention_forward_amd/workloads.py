@@ -232,6 +232,72 @@ def make_prefill(spec: PrefillSpec, seed: int) -> PrefillInputs:
     return PrefillInputs(spec, q, k, v, spikes)
 
 
+# --------------------------------------------------------------------------- packed sequences
+@dataclass(frozen=True)
+class VarlenSpec:
+    """Packed sequences: lengths drawn per sequence; each sequence's keys are a
+    prefix of prefix_lo..prefix_hi cached tokens followed by its query tokens."""
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    dtype: str
+    causal: bool
+    len_lo: int
+    len_hi: int
+    window: int = 0
+    prefix_lo: int = 0
+    prefix_hi: int = 0
+    scale: float | None = None
+
+    @property
+    def scale_f32(self) -> float:
+        s = 1.0 / math.sqrt(self.head_dim) if self.scale is None else self.scale
+        return float(np.float32(s))
+
+
+@dataclass
+class VarlenInputs:
+    spec: VarlenSpec
+    lens_q: np.ndarray    # [B] int64
+    lens_kv: np.ndarray   # [B] int64
+    cu_q: np.ndarray      # [B + 1] int64 cumulative offsets
+    cu_kv: np.ndarray
+    q: np.ndarray         # [total_q, Hq, D] storage
+    k: np.ndarray         # [total_kv, Hkv, D]
+    v: np.ndarray
+
+
+def make_varlen(spec: VarlenSpec, seed: int, lens_q=None, prefixes=None) -> VarlenInputs:
+    """Draw order: q lengths U{len_lo..len_hi}, prefix lengths U{prefix_lo..prefix_hi}, q, k, v
+    (explicit lens_q / prefixes replace the draws)."""
+    rng = np.random.default_rng(seed)
+    B = spec.batch
+    lq = rng.integers(spec.len_lo, spec.len_hi + 1, size=B) if lens_q is None else np.asarray(lens_q)
+    pre = rng.integers(spec.prefix_lo, spec.prefix_hi + 1, size=B) if prefixes is None else np.asarray(prefixes)
+    lq = lq.astype(np.int64)
+    lk = lq + pre.astype(np.int64)
+    cq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int64)
+    ck = np.concatenate([[0], np.cumsum(lk)]).astype(np.int64)
+    q = normal_rounded(rng, (int(cq[-1]), spec.n_q_heads, spec.head_dim), spec.dtype)
+    k = normal_rounded(rng, (int(ck[-1]), spec.n_kv_heads, spec.head_dim), spec.dtype)
+    v = normal_rounded(rng, (int(ck[-1]), spec.n_kv_heads, spec.head_dim), spec.dtype)
+    return VarlenInputs(spec, lq, lk, cq, ck, q, k, v)
+
+
+def varlen_visible_pairs(inp: VarlenInputs) -> int:
+    """Visible (query, key) pairs per q-head, summed over the sequences (bottom-right alignment)."""
+    s = inp.spec
+    tot = 0
+    for Lq, Lk in zip(inp.lens_q.tolist(), inp.lens_kv.tolist()):
+        for i in range(Lq):
+            pos = i + Lk - Lq
+            hi = min(Lk, pos + 1) if s.causal else Lk
+            lo = max(0, pos - s.window + 1) if s.window > 0 else 0
+            tot += max(0, hi - lo)
+    return tot
+
+
 # --------------------------------------------------------------------------- decode
 @dataclass(frozen=True)
 class DecodeSpec:
@@ -316,6 +382,12 @@ WORKLOADS = {
 FP8_DECODE = replace(WORKLOADS["paged_decode_b32_d128"], kv_dtype="fp8")
 
 WORKLOAD_SEEDS = {name: 1001 + i for i, name in enumerate(WORKLOADS)}
+
+# Packed-sequence prefill (per-row dynamic bounds): the 7B-shaped heads of the
+# 2K context workload over 16 packed prompts of 256..4096 tokens.
+VARLEN = "bf16_varlen_gqa7_b16"
+VARLEN_SPEC = VarlenSpec(16, 28, 4, 128, "bf16", causal=True, len_lo=256, len_hi=4096)
+VARLEN_SEED = 1006
 
 
 def shrink(spec, **kw):

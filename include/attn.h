@@ -7,7 +7,8 @@
  *
  * with the online-softmax recurrence (running row max m, running sum l,
  * rescale alpha = exp(m_old - m_new) of O and l, final O * (1/l)):
- *   - attn_prefill_fwd     long Q against K/V of the same sequence (compute bound);
+ *   - attn_prefill_fwd     long Q against K/V of the same sequence (compute bound),
+ *                          with _ex (lse output, sinks) and _varlen (packed sequences);
  *   - attn_decode_fwd      a few query tokens against a long, optionally paged,
  *                          KV cache, split along the cache into partial results;
  *   - attn_decode_combine  the log-sum-exp merge of those partials.
@@ -121,6 +122,37 @@ int attn_prefill_fwd_ex(const void* q, attn_strides q_st, const void* k, attn_st
                         int seqlen_q, int seqlen_kv, int head_dim,
                         float scale, int causal, int window,
                         float* lse, const float* sinks, void* hip_stream);
+
+/*
+ * Prefill over packed sequences of different lengths (sequence packing):
+ * the bounds of every sequence are data, not shapes (the CTE page's dynamic
+ * range_select family, section "Algorithm — the dynamic range_select
+ * family": sequence-packing bounds and a dynamic prefix length; the minfer
+ * page's kernel, section 3.1, reads the key bound from its positions input).
+ *   q, o   [total_q, n_q_heads, head_dim] and k, v [total_kv, n_kv_heads,
+ *          head_dim], device, `dtype`, addressed with the seq and head
+ *          strides of q_st, k_st, v_st, o_st (their batch strides are ignored).
+ *   cu_seqlens_q, cu_seqlens_kv  device int32 [batch + 1], nondecreasing:
+ *          sequence b owns q/o rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) and
+ *          k/v rows [cu_seqlens_kv[b], cu_seqlens_kv[b+1]).
+ *   max_seqlen_q, max_seqlen_kv  at least every sequence's q and k/v length
+ *          (the launch covers max_seqlen_q rows per sequence; rows of a longer
+ *          sequence beyond it are not computed).
+ * Within each sequence the usual rules hold: its query row i sits at position
+ * i + (len_kv - len_q) (so len_q < len_kv is a chunk of new tokens after a
+ * cached prefix), causal and window apply to those positions, GQA and the
+ * optional lse ([total_q, n_q_heads], natural log) and sinks are as for
+ * attn_prefill_fwd_ex. A sequence with no query rows writes nothing; one
+ * with no keys outputs zeros. The offsets are not validated on the host:
+ * offsets outside the tensors are undefined behaviour.
+ */
+int attn_prefill_varlen_fwd(const void* q, attn_strides q_st, const void* k, attn_strides k_st,
+                            const void* v, attn_strides v_st, void* o, attn_strides o_st,
+                            attn_dtype dtype, int batch, int n_q_heads, int n_kv_heads,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                            int max_seqlen_q, int max_seqlen_kv, int head_dim,
+                            float scale, int causal, int window,
+                            float* lse, const float* sinks, void* hip_stream);
 
 /*
  * Decode attention against a KV cache, split along the cache (split-KV).

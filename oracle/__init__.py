@@ -125,6 +125,34 @@ def attention(q, k, v, scale: float, causal: bool = False, window: int = 0, retu
     return (o, lse) if return_lse else o
 
 
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale: float, causal: bool = False, window: int = 0,
+                     sinks=None, return_lse: bool = False):
+    """Oracle for packed sequences: each sequence is attended on its own.
+
+    q: float64 [total_q, Hq, D]; k, v: float64 [total_kv, Hkv, D]; cu_seqlens_*:
+    [B + 1] cumulative offsets (sequence b owns q rows cu_q[b]..cu_q[b+1] and
+    k/v rows cu_kv[b]..cu_kv[b+1]). Each sequence is the plain definition on its
+    own slice, with its query rows bottom-right aligned to its own keys — the
+    per-sequence bounds of the CTE page's dynamic range_select family
+    ("Algorithm — the dynamic range_select family": sequence-packing bounds and
+    a dynamic prefix length). Returns o [total_q, Hq, D] (and lse [total_q, Hq]).
+    """
+    cq = np.asarray(cu_seqlens_q, dtype=np.int64)
+    ck = np.asarray(cu_seqlens_kv, dtype=np.int64)
+    assert cq.shape == ck.shape and cq.ndim == 1
+    o = np.zeros(q.shape, dtype=np.float64)
+    lse = np.full(q.shape[:2], -np.inf, dtype=np.float64)
+    for b in range(cq.shape[0] - 1):
+        q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        if q1 <= q0:
+            continue
+        ob, lb = attention(np.ascontiguousarray(q[None, q0:q1]), np.ascontiguousarray(k[None, k0:k1]),
+                           np.ascontiguousarray(v[None, k0:k1]), scale, causal, window, return_lse=True, sinks=sinks)
+        o[q0:q1] = ob[0]
+        lse[q0:q1] = lb[0]
+    return (o, lse) if return_lse else o
+
+
 def gather_paged(pool: np.ndarray, block_table_row: np.ndarray, length: int) -> np.ndarray:
     """Logical KV [length, Hkv, D] of one sequence from a [pages, page_size, Hkv, D] pool."""
     ps = pool.shape[1]

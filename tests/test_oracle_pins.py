@@ -521,3 +521,66 @@ def test_e4m3_rounding_is_nearest_even_and_saturating():
     # the bulk path of the generator is the same rounding
     big = np.tile(x, 3)
     np.testing.assert_array_equal(W.f32_to_e4m3_bits(big), W.f32_to_e4m3_bits_by_definition(big))
+
+
+# ----------------------------------------------------------------------------- packed sequences
+def packed_case(lens_q, lens_kv, Hq, Hkv, D, seed):
+    cq = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int64)
+    ck = np.concatenate([[0], np.cumsum(lens_kv)]).astype(np.int64)
+    q = rand((int(cq[-1]), Hq, D), seed)
+    k, v = rand((int(ck[-1]), Hkv, D), seed + 1), rand((int(ck[-1]), Hkv, D), seed + 2)
+    return q, k, v, cq, ck
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 3)])
+def test_varlen_matches_sdpa_with_a_segment_mask(causal, window):
+    """One float64 SDPA over the whole packed batch with a mask built from
+    segment ids and positions (not from per-sequence slices)."""
+    lens_q, lens_kv = [5, 0, 9, 3, 7], [5, 4, 12, 3, 0]  # a prefix-prior sequence, an empty q, an empty kv
+    Hq, Hkv, D = 6, 2, 8
+    q, k, v, cq, ck = packed_case(lens_q, lens_kv, Hq, Hkv, D, 41)
+    scale = 0.45
+    o, lse = oracle.attention_varlen(q, k, v, cq, ck, scale, causal, window, return_lse=True)
+    seg_q = np.repeat(np.arange(len(lens_q)), lens_q)
+    seg_k = np.repeat(np.arange(len(lens_kv)), lens_kv)
+    pos_q = np.arange(q.shape[0]) - cq[seg_q] + (np.asarray(lens_kv) - np.asarray(lens_q))[seg_q]
+    idx_k = np.arange(k.shape[0]) - ck[seg_k]
+    mask = seg_q[:, None] == seg_k[None, :]
+    if causal:
+        mask &= idx_k[None, :] <= pos_q[:, None]
+    if window > 0:
+        mask &= idx_k[None, :] >= pos_q[:, None] - window + 1
+    tq = torch.from_numpy(q).permute(1, 0, 2)[None]
+    tk, tv = (torch.from_numpy(x).permute(1, 0, 2)[None] for x in (k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(mask), scale=scale,
+                                                           enable_gqa=True)[0].permute(1, 0, 2).numpy()
+    seen = mask.any(axis=1)
+    np.testing.assert_allclose(o[seen], ref[seen], rtol=1e-12, atol=1e-12)
+    assert np.all(o[~seen] == 0.0) and np.all(lse[~seen] == -np.inf)
+    # log-sum-exp over the same mask, from the same scores computed here
+    s = scale * np.einsum("qhd,khd->hqk", q, np.repeat(k, Hq // Hkv, axis=1))
+    s = np.where(mask[None], s, -np.inf)
+    with np.errstate(divide="ignore"):
+        ref_lse = np.log(np.exp(s).sum(axis=2)).T
+    np.testing.assert_allclose(lse[seen], ref_lse[seen], rtol=1e-12, atol=1e-12)
+
+
+def test_varlen_equal_lengths_equal_the_batched_oracle_bitwise():
+    B, S, Hq, Hkv, D = 3, 11, 4, 2, 8
+    q, k, v, cq, ck = packed_case([S] * B, [S] * B, Hq, Hkv, D, 43)
+    o = oracle.attention_varlen(q, k, v, cq, ck, 0.3, True, 4)
+    ob = oracle.attention(q.reshape(B, S, Hq, D), k.reshape(B, S, Hkv, D), v.reshape(B, S, Hkv, D), 0.3, True, 4)
+    assert np.array_equal(o, ob.reshape(B * S, Hq, D))
+
+
+def test_varlen_sequence_order_does_not_matter():
+    lens = [4, 9, 1, 6]
+    q, k, v, cq, ck = packed_case(lens, lens, 2, 1, 4, 45)
+    o = oracle.attention_varlen(q, k, v, cq, ck, 0.8, True)
+    perm = [2, 0, 3, 1]
+    take_q = np.concatenate([np.arange(cq[b], cq[b + 1]) for b in perm])
+    take_k = np.concatenate([np.arange(ck[b], ck[b + 1]) for b in perm])
+    lp = [lens[b] for b in perm]
+    cp = np.concatenate([[0], np.cumsum(lp)])
+    op = oracle.attention_varlen(q[take_q], k[take_k], v[take_k], cp, cp, 0.8, True)
+    assert np.array_equal(op, o[take_q])
