@@ -653,12 +653,15 @@ static hipError_t launch_mfma_nw(PrefillParams p, int mask, hipStream_t s) {
 // Eight-wave workgroups halve the K/V traffic per FLOP but hold a whole CU
 // each; they are used for D <= 128 when there are enough of them to fill the
 // chip at least twice over (D = 256 needs more than half a SIMD's registers
-// per wave, so it stays at four waves).
+// per wave, so it stays at four waves). Packed sequences keep four waves: their
+// many short sequences each end in a partly filled tile, and 128-row tiles
+// halve that waste (measured 8% faster on 16 prompts of 256..4096 tokens).
 constexpr int kPrefillWideMinWorkgroups = 512;
 
 template <bool BF16, int D>
 static hipError_t launch_mfma_mask(PrefillParams p, int mask, hipStream_t s) {
     if constexpr (D <= 128) {
+        if (p.cu_seqlens_q) return launch_mfma_nw<BF16, D, 4>(p, mask, s);
         const long wide = (long)((p.seqlen_q + 255) / 256) * p.batch * p.n_q_heads;
         if (wide >= kPrefillWideMinWorkgroups) return launch_mfma_nw<BF16, D, 8>(p, mask, s);
     }

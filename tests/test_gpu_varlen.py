@@ -80,7 +80,7 @@ def test_varlen_lse_and_sinks(name):
 
 @pytest.mark.parametrize("B,Hq,Hkv,S,dtype,window", [
     (3, 4, 2, 200, "bf16", 0),
-    (32, 8, 2, 300, "bf16", 0),     # enough workgroups for the eight-wave launch, in both calls
+    (32, 8, 2, 300, "bf16", 0),     # the batched call takes the eight-wave launch, the packed one four waves
     (2, 4, 4, 150, "f16", 40),
     (2, 2, 1, 90, "f32", 0),
 ])
