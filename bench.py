@@ -406,8 +406,11 @@ def main():
             "flops": varlen_flops,
             "ms": round(varlen_ms, 4),
             "tflops": round(varlen_flops / (varlen_ms * 1e-3) / 1e12, 2),
-            "frac_of_peak": round(varlen_flops / (varlen_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "note": "packed causal prompts, 28/4 heads, D128, bf16, lengths uniform in [256, 4096]",
+            "roofline": {"bound": "mfma", "achieved": round(varlen_flops / (varlen_ms * 1e-3) / 1e12, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(varlen_flops / (varlen_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "traffic": traffic_from_profiles("prefill_varlen_b16")},
         },
         "sinks_and_lse": {
             "prefill_ex_ms": round(pre_ex_ms, 4),
