@@ -107,6 +107,7 @@ int prefill_impl(const void* q, attn_strides q_st, const void* k, attn_strides k
     p.sinks = sinks;
     p.cu_seqlens_q = cu_seqlens_q;
     p.cu_seqlens_kv = cu_seqlens_kv;
+    p.xcd_chunks = ((int64_t)batch * n_kv_heads) % 8 == 0;
     const int mask = !causal ? attn::kMaskNone : (p.window > 0 ? attn::kMaskCausalWindow : attn::kMaskCausal);
     return status_of(attn::launch_prefill(p, (int)dtype, head_dim, mask, (hipStream_t)hip_stream));
 }

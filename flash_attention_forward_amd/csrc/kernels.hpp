@@ -29,6 +29,7 @@ struct PrefillParams {
     // [cu_seqlens_kv[b], cu_seqlens_kv[b+1]) (batch strides unused; lse is [total_q, n_q_heads])
     const int32_t* cu_seqlens_q;
     const int32_t* cu_seqlens_kv;
+    int xcd_chunks;   // deal workgroups to XCDs in kv-head groups (batch * n_kv_heads % 8 == 0)
 };
 
 struct DecodeParams {

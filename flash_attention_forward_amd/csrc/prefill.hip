@@ -83,11 +83,29 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     const int g = lane >> 4;    // 16-lane group
     const int r16 = lane & 15;
 
-    // Workgroup -> (q tile, batch, q-head). Consecutive workgroups are the
-    // heads of one q tile; causal tiles are issued heaviest first.
+    // Workgroup -> (q tile, batch, q-head). In the logical order, consecutive
+    // workgroups are the heads of one q tile and causal tiles come heaviest
+    // first. The hardware deals workgroups to the 8 XCDs round robin
+    // (workgroup i to XCD i % 8) and each XCD has its own L2. When batch *
+    // n_kv_heads is a multiple of 8 (p.xcd_chunks), the logical order is dealt
+    // out in chunks of `group` workgroups — the q-heads that share one kv-head
+    // — with a whole chunk on one XCD; all chunks of one (sequence, kv-head)
+    // then land on the same XCD, so each K/V stream is fetched into one L2
+    // only (measured 8% faster on 16 packed prompts; on one long sequence
+    // with one kv-head the plain order is 3% faster). The last partial round
+    // keeps the plain order.
     const int nbh = p.batch * p.n_q_heads;
-    const int qt = p.n_q_tiles - 1 - (int)(blockIdx.x / nbh);
-    const int bh = blockIdx.x % nbh;
+    int wid = (int)blockIdx.x;
+    if (p.xcd_chunks) {
+        const int G = p.group, round = 8 * G;
+        const int full = ((int)gridDim.x / round) * round;
+        if (wid < full) {
+            const int xcd = wid & 7, k = wid >> 3;
+            wid = ((k / G) * 8 + xcd) * G + k % G;
+        }
+    }
+    const int qt = p.n_q_tiles - 1 - wid / nbh;
+    const int bh = wid % nbh;
     const int b = bh / p.n_q_heads;
     const int h = bh % p.n_q_heads;
     const int hk = h / p.group;
