@@ -104,6 +104,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             wid = ((k / G) * 8 + xcd) * G + k % G;
         }
     }
+    // A grid that fits on the chip in one go (256 < workgroups <= 512, two
+    // per CU) has no later workgroups to fill in behind the heavy ones, so
+    // its second half runs lightest first: the CU that starts a heavy tile
+    // is then paired with a light one (2K causal, 28 heads: 4% faster).
+    if constexpr (NW == 4 && D <= 128) {
+        const int n = (int)gridDim.x;
+        if (n > 256 && n <= 512 && wid >= 256) wid = 256 + (n - 1 - wid);
+    }
     const int qt = p.n_q_tiles - 1 - wid / nbh;
     const int bh = wid % nbh;
     const int b = bh / p.n_q_heads;
