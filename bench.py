@@ -189,7 +189,11 @@ def main():
     rng = np.random.default_rng(W.WORKLOAD_SEEDS[DECODE] + 100)
     dq4 = W.to_torch(W.round_to(rng.standard_normal((dspec.batch, 4, dspec.n_q_heads, dspec.head_dim),
                                                     dtype=np.float32), dspec.dtype), dspec.dtype, dev)
-    ws4 = F.DecodeWorkspace(dspec.batch, 4, dspec.n_q_heads, dspec.head_dim, ms, dev)
+    # four tokens make the partials four times larger, so fewer, longer splits pay
+    # (measured: 483 us at split_len 1024, 456 us at 4096)
+    spec_split = 4096
+    ms4 = F.attn.max_splits_for(max_len, spec_split)
+    ws4 = F.DecodeWorkspace(dspec.batch, 4, dspec.n_q_heads, dspec.head_dim, ms4, dev)
     do4 = torch.empty_like(dq4)
     btl = bt.long()
     kflat = kc[btl].reshape(dspec.batch, max_len, dspec.n_kv_heads, dspec.head_dim)
@@ -267,20 +271,21 @@ def main():
     varlen_flops = 4.0 * vspec.head_dim * vspec.n_q_heads * W.varlen_visible_pairs(vin)
     del vq, vk, vv, vo
 
-    def time_decode(qq, kk, vv, table, w, out, reps=20):
+    def time_decode(qq, kk, vv, table, w, out, reps=20, split_len=None):
+        sl = args.split_len if split_len is None else split_len
         for _ in range(3):
-            F.attn_decode_fwd(qq, kk, vv, cl, w.part_o, w.part_lse, args.split_len, ms, dspec.scale_f32, table)
-            F.attn_decode_combine(w.part_o, w.part_lse, cl, args.split_len, ms, out)
+            F.attn_decode_fwd(qq, kk, vv, cl, w.part_o, w.part_lse, sl, w.max_splits, dspec.scale_f32, table)
+            F.attn_decode_combine(w.part_o, w.part_lse, cl, sl, w.max_splits, out)
         evv = [[ev(), ev()] for _ in range(reps)]
         for e in evv:
             e[0].record(stream)
-            F.attn_decode_fwd(qq, kk, vv, cl, w.part_o, w.part_lse, args.split_len, ms, dspec.scale_f32, table)
-            F.attn_decode_combine(w.part_o, w.part_lse, cl, args.split_len, ms, out)
+            F.attn_decode_fwd(qq, kk, vv, cl, w.part_o, w.part_lse, sl, w.max_splits, dspec.scale_f32, table)
+            F.attn_decode_combine(w.part_o, w.part_lse, cl, sl, w.max_splits, out)
             e[1].record(stream)
         torch.cuda.synchronize()
         return float(np.mean([e[0].elapsed_time(e[1]) for e in evv]))
 
-    spec_us = time_decode(dq4, kc, vc, bt, ws4, do4) * 1e3
+    spec_us = time_decode(dq4, kc, vc, bt, ws4, do4, split_len=spec_split) * 1e3
     flat_us = time_decode(dq, kflat, vflat, None, ws, torch.empty_like(dq)) * 1e3
     del kflat, vflat
 
@@ -421,6 +426,7 @@ def main():
         "decode_variants": {
             "speculative_s_active4_us": round(spec_us, 2),
             "speculative_s_active4_gbps": round(kv_bytes / (spec_us * 1e-6) / 1e9, 1),
+            "speculative_split_len": spec_split,
             "flat_cache_us": round(flat_us, 2),
             "flat_cache_gbps": round(kv_bytes / (flat_us * 1e-6) / 1e9, 1),
             "fp8_kv_split_us": round(fp8_split_us, 2),
