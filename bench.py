@@ -32,6 +32,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E, published
 PREFILL = "bf16_causal_32k"
 DECODE = "paged_decode_b32_d128"
+SWA = "bf16_swa1024_d256_8k"
 CONTEXT = "f16_gqa7_causal_2k"  # the 7B-shaped 2K prefill the minfer page times
 PAGES_CONTEXT_MS_PER_LAYER = 8.5   # minfer 8n page, results: 7B @2K prefill attention, on its own (NVIDIA) GPU
 DEFAULT_SPLIT_LEN = 1024  # decode keys per split (timed sweep: 512 and 2048 are slower on the paged workload)
@@ -251,6 +252,23 @@ def main():
     torch.cuda.synchronize()
     ctx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in cev]))
 
+    # sliding window over D = 256 (bf16, B2, 16/8 heads, 8192 tokens, window 1024): 20 back-to-back launches
+    wspec = W.WORKLOADS[SWA]
+    win = W.make_prefill(wspec, W.WORKLOAD_SEEDS[SWA])
+    wq, wk, wv = (W.to_torch(a, wspec.dtype, dev) for a in (win.q, win.k, win.v))
+    wo = torch.empty_like(wq)
+    for _ in range(3):
+        F.attn_prefill_fwd(wq, wk, wv, wo, wspec.scale_f32, True, wspec.window)
+    wev = [ev(), ev()]
+    wev[0].record(stream)
+    for _ in range(20):
+        F.attn_prefill_fwd(wq, wk, wv, wo, wspec.scale_f32, True, wspec.window)
+    wev[1].record(stream)
+    torch.cuda.synchronize()
+    swa_ms = wev[0].elapsed_time(wev[1]) / 20
+    swa_flops = prefill_flops(wspec)
+    del wq, wk, wv, wo, win
+
     # packed prompts of different lengths (attn_prefill_varlen_fwd): 10 back-to-back launches
     vspec = W.VARLEN_SPEC
     vin = W.make_varlen(vspec, W.VARLEN_SEED)
@@ -403,6 +421,17 @@ def main():
             "tflops": round(prefill_flops(cspec) / (ctx_ms * 1e-3) / 1e12, 2),
             "pages_ms_per_layer": PAGES_CONTEXT_MS_PER_LAYER,
             "pages_hardware": "unnamed NVIDIA GPU (minfer 8n page); context only",
+        },
+        "swa_d256": {
+            "workload": SWA,
+            "flops": swa_flops,
+            "ms": round(swa_ms, 4),
+            "tflops": round(swa_flops / (swa_ms * 1e-3) / 1e12, 2),
+            "note": "B2 Sq=Skv=8192 Hq16 Hkv8 D256 bf16 causal + window 1024; FLOPs over visible pairs only",
+            "roofline": {"bound": "mfma", "achieved": round(swa_flops / (swa_ms * 1e-3) / 1e12, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(swa_flops / (swa_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "traffic": traffic_from_profiles("prefill_swa_d256")},
         },
         "varlen": {
             "workload": W.VARLEN,
