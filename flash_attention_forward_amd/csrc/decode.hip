@@ -13,10 +13,14 @@
 // are loaded straight into LDS, K read back as the MFMA A operand and V read
 // back transposed with ds_read_b64_tr_b16 for O^T += V^T P^T. The next 32 keys
 // are in flight while the current ones are used. All loads go to LDS, so the
-// only waits on them are the explicit per-block ones. Rows of a split's last page at or beyond
-// cache_len are neither read nor used (decode page, section "gen_mask_tkg":
-// index < cache length), and their V rows are zero so that nothing there can
-// leak into the product.
+// only waits on them are the explicit per-block ones. Rows at or beyond
+// cache_len are never read (decode page, section "gen_mask_tkg": index <
+// cache length): their loads are clamped to the last valid row, whose copy
+// gets probability exactly 0, so nothing past the end can leak into the
+// product.
+//
+// decode_split_f8: the same split for an FP8 E4M3 cache, read into registers
+// with full-row loads and widened exactly to 16 bits before the same MFMAs.
 //
 // Each split writes its normalised output and its natural-log log-sum-exp
 // (the decode page's deferred normalisation on its flash path: the partial
@@ -125,6 +129,8 @@ template <int D>
 constexpr int dc_max_heads() {
     return D >= 256 ? 1 : (D >= 128 ? 2 : 4);
 }
+// decode_split_f8 holds one 16-bit V tile and one byte K tile per wave (24 KB *
+// D / 128), so four kv-heads fit under the same 64 KB (two at D = 256).
 template <int D>
 constexpr int dc_max_heads_f8() {
     return D >= 256 ? 2 : 4;
