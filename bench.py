@@ -66,6 +66,24 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def utilisation_from_profiles():
+    """MFMA-busy fraction and average shader clock per kernel from the committed counter
+    summary (profiles/utilisation.md), while the kernel sources match the ones it was taken with."""
+    path = os.path.join(ROOT, "profiles", "utilisation.md")
+    out = {}
+    if not os.path.exists(path):
+        return out
+    for line in open(path):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 5 and cells[1] == kernel_source_digest():
+            try:
+                busy, ghz = float(cells[2]), float(cells[3])
+            except ValueError:
+                continue
+            out[cells[0]] = {"mfma_busy": busy, "clock_ghz": ghz, "frac_of_peak_at_clock": float(cells[4])}
+    return out
+
+
 def traffic_from_profiles(kernel_key: str):
     """HBM bytes per launch from the committed counter summary (profiles/hbm_traffic.md),
     or None if the kernel sources changed since the counters were taken."""
@@ -77,6 +95,27 @@ def traffic_from_profiles(kernel_key: str):
         if len(cells) == 3 and cells[0] == kernel_key:
             return int(cells[2]) if cells[1] == kernel_source_digest() else None
     return None
+
+
+def practical_hbm_gbps(stream, ev) -> float:
+    """Read + write rate of a plain 1 GiB device copy: the practical HBM line."""
+    import torch
+
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1)
+    for _ in range(3):
+        y.copy_(x)
+    e = [ev(), ev()]
+    e[0].record(stream)
+    for _ in range(10):
+        y.copy_(x)
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = e[0].elapsed_time(e[1]) / 10
+    del x, y
+    return 2.0 * n / (ms * 1e-3) / 1e9
 
 
 def calibrate_copy():
@@ -356,6 +395,7 @@ def main():
         comb_ex.append(cev[0].elapsed_time(cev[1]) / n_ex)
     comb_ex_us = float(np.median(comb_ex)) * 1e3
 
+    copy_gbps = practical_hbm_gbps(stream, ev)
     flops = prefill_flops(pspec)
     kv_bytes = decode_kv_bytes(din)
     pre_tflops = flops / (pre_ms.mean() * 1e-3) / 1e12
@@ -397,6 +437,9 @@ def main():
             "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_from_profiles("prefill_causal_32k"),
         },
+        "practical_hbm": {"what": "1 GiB device copy, bytes read + written per second", "gbps": round(copy_gbps, 1),
+                          "frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4)},
+        "utilisation": utilisation_from_profiles(),
         "roofline_decode": {
             "kernel": "decode_split<bf16, D128>",
             "bound": "hbm",
