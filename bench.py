@@ -80,7 +80,8 @@ def utilisation_from_profiles():
                 busy, ghz = float(cells[2]), float(cells[3])
             except ValueError:
                 continue
-            out[cells[0]] = {"mfma_busy": busy, "clock_ghz": ghz, "frac_of_peak_at_clock": float(cells[4])}
+            frac = None if cells[4] == "-" else float(cells[4])
+            out[cells[0]] = {"mfma_busy": busy, "clock_ghz": ghz, "frac_of_peak_at_clock": frac}
     return out
 
 
