@@ -53,7 +53,7 @@ def _load():
         p = ctypes.c_void_p
         i64 = ctypes.c_int64
         lib.oracle_attention_rows.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64,
-                                              ctypes.c_double, ctypes.c_int, i64, p, p, i64, p, p]
+                                              ctypes.c_double, ctypes.c_int, i64, p, p, p, i64, p, p]
         lib.oracle_attention_rows.restype = ctypes.c_int
         lib.oracle_visible_mask.argtypes = [i64, i64, ctypes.c_int, i64, p]
         lib.oracle_visible_mask.restype = None
@@ -81,12 +81,13 @@ def visible_mask(Sq: int, Skv: int, causal: bool, window: int = 0) -> np.ndarray
     return m.astype(bool)
 
 
-def attention_rows(q, k, v, scale: float, causal: bool, window: int, rows, sinks=None):
+def attention_rows(q, k, v, scale: float, causal: bool, window: int, rows, sinks=None, positions=None):
     """Oracle output for selected rows.
 
     q: float64 [B, Sq, Hq, D]; k, v: float64 [B, Skv, Hkv, D] (views allowed,
     head_dim contiguous). rows: int array [n, 3] of (b, i, h). sinks: None or
-    [Hq] sink logits (scaled-score units; see attn_oracle.c).
+    [Hq] sink logits (scaled-score units; see attn_oracle.c). positions: None or
+    [Sq] integer position of each query row (default i + Skv - Sq).
     Returns (o [n, D] float64, lse [n] float64, natural log).
     """
     lib = _load()
@@ -102,9 +103,14 @@ def attention_rows(q, k, v, scale: float, causal: bool, window: int, rows, sinks
     if sinks is not None:
         sk = np.ascontiguousarray(sinks, dtype=np.float64).reshape(-1)
         assert sk.shape[0] == Hq
+    qp = None
+    if positions is not None:
+        qp = np.ascontiguousarray(positions, dtype=np.int64).reshape(-1)
+        assert qp.shape[0] == Sq
     rc = lib.oracle_attention_rows(_ptr(q), _ptr(qs), _ptr(k), _ptr(ks), _ptr(v), _ptr(vs),
                                    Hq, Hkv, Sq, Skv, D, float(scale), int(bool(causal)), int(window),
-                                   _ptr(sk) if sk is not None else None, _ptr(rows), n, _ptr(o), _ptr(lse))
+                                   _ptr(sk) if sk is not None else None, _ptr(qp) if qp is not None else None,
+                                   _ptr(rows), n, _ptr(o), _ptr(lse))
     if rc != 0:
         raise ValueError("oracle_attention_rows rejected its arguments")
     return o, lse
@@ -116,17 +122,17 @@ def all_rows(B: int, Sq: int, Hq: int) -> np.ndarray:
 
 
 def attention(q, k, v, scale: float, causal: bool = False, window: int = 0, return_lse: bool = False,
-              sinks=None):
-    """Full oracle output [B, Sq, Hq, D] (and lse [B, Sq, Hq])."""
+              sinks=None, positions=None):
+    """Full oracle output [B, Sq, Hq, D] (and lse [B, Sq, Hq]); positions as for attention_rows."""
     B, Sq, Hq, D = q.shape
-    o, lse = attention_rows(q, k, v, scale, causal, window, all_rows(B, Sq, Hq), sinks)
+    o, lse = attention_rows(q, k, v, scale, causal, window, all_rows(B, Sq, Hq), sinks, positions)
     o = o.reshape(B, Sq, Hq, D)
     lse = lse.reshape(B, Sq, Hq)
     return (o, lse) if return_lse else o
 
 
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale: float, causal: bool = False, window: int = 0,
-                     sinks=None, return_lse: bool = False):
+                     sinks=None, return_lse: bool = False, positions=None):
     """Oracle for packed sequences: each sequence is attended on its own.
 
     q: float64 [total_q, Hq, D]; k, v: float64 [total_kv, Hkv, D]; cu_seqlens_*:
@@ -135,7 +141,10 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale: float, causal:
     own slice, with its query rows bottom-right aligned to its own keys — the
     per-sequence bounds of the CTE page's dynamic range_select family
     ("Algorithm — the dynamic range_select family": sequence-packing bounds and
-    a dynamic prefix length). Returns o [total_q, Hq, D] (and lse [total_q, Hq]).
+    a dynamic prefix length). positions: None, or [total_q] integer position of
+    every packed query row within its sequence's keys (the minfer page's
+    positions input), replacing that alignment. Returns o [total_q, Hq, D] (and
+    lse [total_q, Hq]).
     """
     cq = np.asarray(cu_seqlens_q, dtype=np.int64)
     ck = np.asarray(cu_seqlens_kv, dtype=np.int64)
@@ -146,8 +155,10 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale: float, causal:
         q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
         if q1 <= q0:
             continue
+        pos = None if positions is None else np.asarray(positions)[q0:q1]
         ob, lb = attention(np.ascontiguousarray(q[None, q0:q1]), np.ascontiguousarray(k[None, k0:k1]),
-                           np.ascontiguousarray(v[None, k0:k1]), scale, causal, window, return_lse=True, sinks=sinks)
+                           np.ascontiguousarray(v[None, k0:k1]), scale, causal, window, return_lse=True, sinks=sinks,
+                           positions=pos)
         o[q0:q1] = ob[0]
         lse[q0:q1] = lb[0]
     return (o, lse) if return_lse else o

@@ -50,12 +50,16 @@
 #include <stdint.h>
 #include <stdlib.h>
 
-static int visible(int64_t i, int64_t j, int64_t Sq, int64_t Skv, int causal, int64_t window)
+static int visible_at(int64_t qpos, int64_t j, int causal, int64_t window)
 {
-    int64_t qpos = i + (Skv - Sq);
     if (causal && j > qpos) return 0;
     if (window > 0 && j < qpos - window + 1) return 0;
     return 1;
+}
+
+static int visible(int64_t i, int64_t j, int64_t Sq, int64_t Skv, int causal, int64_t window)
+{
+    return visible_at(i + (Skv - Sq), j, causal, window);
 }
 
 /* mask[i*Skv + j] = 1 if query row i sees key j */
@@ -69,14 +73,14 @@ void oracle_visible_mask(int64_t Sq, int64_t Skv, int causal, int64_t window, ui
 /* One output row. s is scratch of length Skv. Returns the lse. */
 static double attention_row(const double* qrow, const double* k, const int64_t* k_st,
                             const double* v, const int64_t* v_st, int64_t b, int64_t hk,
-                            int64_t i, int64_t Sq, int64_t Skv, int64_t D, double scale,
+                            int64_t qpos, int64_t Skv, int64_t D, double scale,
                             int causal, int64_t window, int has_sink, double sink, double* s,
                             double* orow)
 {
     double m = -INFINITY;
     int64_t nvis = 0;
     for (int64_t j = 0; j < Skv; ++j) {
-        if (!visible(i, j, Sq, Skv, causal, window)) continue;
+        if (!visible_at(qpos, j, causal, window)) continue;
         const double* krow = k + b * k_st[0] + j * k_st[1] + hk * k_st[2];
         double dot = 0.0;
         for (int64_t d = 0; d < D; ++d) dot += qrow[d] * krow[d];
@@ -91,7 +95,7 @@ static double attention_row(const double* qrow, const double* k, const int64_t* 
 
     double l = has_sink ? exp(sink - m) : 0.0;
     for (int64_t j = 0; j < Skv; ++j) {
-        if (!visible(i, j, Sq, Skv, causal, window)) continue;
+        if (!visible_at(qpos, j, causal, window)) continue;
         double p = exp(s[j] - m);
         const double* vrow = v + b * v_st[0] + j * v_st[1] + hk * v_st[2];
         l += p;
@@ -105,14 +109,18 @@ static double attention_row(const double* qrow, const double* k, const int64_t* 
  * Attention for a list of output rows.
  *   rows:  nrows triples (b, i, h)
  *   sinks: [Hq] sink logits, or NULL for none
+ *   qpos:  [Sq] position of query row i (the same for every b), or NULL for
+ *          i + (Skv - Sq); key j is visible to a row at position P iff j <= P
+ *          (causal) and j >= P - window + 1 (the minfer page's positions input:
+ *          KV positions are data, section 3.1)
  *   o:     [nrows, D] output; lse: [nrows] output (may be NULL)
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
 int oracle_attention_rows(const double* q, const int64_t* q_st, const double* k, const int64_t* k_st,
                           const double* v, const int64_t* v_st, int64_t Hq, int64_t Hkv,
                           int64_t Sq, int64_t Skv, int64_t D, double scale, int causal,
-                          int64_t window, const double* sinks, const int64_t* rows, int64_t nrows,
-                          double* o, double* lse)
+                          int64_t window, const double* sinks, const int64_t* qpos, const int64_t* rows,
+                          int64_t nrows, double* o, double* lse)
 {
     if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || Sq < 0 || Skv < 0) return -1;
     const int64_t group = Hq / Hkv;
@@ -126,7 +134,8 @@ int oracle_attention_rows(const double* q, const int64_t* q_st, const double* k,
             if (!s) continue;
             const int64_t b = rows[3 * r], i = rows[3 * r + 1], h = rows[3 * r + 2];
             const double* qrow = q + b * q_st[0] + i * q_st[1] + h * q_st[2];
-            double L = attention_row(qrow, k, k_st, v, v_st, b, h / group, i, Sq, Skv, D, scale,
+            const int64_t pos = qpos ? qpos[i] : i + (Skv - Sq);
+            double L = attention_row(qrow, k, k_st, v, v_st, b, h / group, pos, Skv, D, scale,
                                      causal, window, sinks != NULL, sinks ? sinks[h] : 0.0, s,
                                      o + r * D);
             if (lse) lse[r] = L;

@@ -584,3 +584,63 @@ def test_varlen_sequence_order_does_not_matter():
     cp = np.concatenate([[0], np.cumsum(lp)])
     op = oracle.attention_varlen(q[take_q], k[take_k], v[take_k], cp, cp, 0.8, True)
     assert np.array_equal(op, o[take_q])
+
+
+# ----------------------------------------------------------------------------- per-row positions
+def brute_row_at(q, k, v, b, i, h, scale, causal, window, qpos):
+    """brute_row with the query position given, not derived from the shapes."""
+    mpmath.mp.dps = 50
+    D = q.shape[3]
+    Skv, Hkv = k.shape[1], k.shape[2]
+    hk = h // (q.shape[2] // Hkv)
+    hi = min(Skv, qpos + 1) if causal else Skv
+    lo = max(0, qpos - window + 1) if window > 0 else 0
+    keys = list(range(lo, max(lo, hi)))
+    if not keys:
+        return [mpmath.mpf(0)] * D, -mpmath.inf
+    e = [mpmath.exp(mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(q[b, i, h, d]) * mpmath.mpf(k[b, j, hk, d])
+                                                  for d in range(D))) for j in keys]
+    Z = mpmath.fsum(e)
+    return [mpmath.fsum(e[t] * mpmath.mpf(v[b, j, hk, d]) for t, j in enumerate(keys)) / Z for d in range(D)], \
+        mpmath.log(Z)
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 3), (False, 0)])
+def test_positions_bruteforce_mpmath(causal, window):
+    Sq, Skv, Hq, Hkv, D = 7, 12, 2, 1, 4
+    q, k, v = rand((1, Sq, Hq, D), 61), rand((1, Skv, Hkv, D), 62), rand((1, Skv, Hkv, D), 63)
+    pos = np.array([-2, 0, 0, 3, 7, 11, 15])  # repeats, gaps, a row before the first key, one past the last
+    o, lse = oracle.attention(q, k, v, 0.6, causal, window, return_lse=True, positions=pos)
+    for i in range(Sq):
+        for h in range(Hq):
+            ref, ref_lse = brute_row_at(q, k, v, 0, i, h, 0.6, causal, window, int(pos[i]))
+            assert np.allclose(o[0, i, h], [float(x) for x in ref], rtol=1e-13, atol=1e-13)
+            if ref_lse == -mpmath.inf:
+                assert lse[0, i, h] == -np.inf
+            else:
+                assert abs(lse[0, i, h] - float(ref_lse)) <= 1e-13 * max(1.0, abs(float(ref_lse)))
+
+
+def test_positions_of_the_default_alignment_change_nothing():
+    Sq, Skv = 9, 14
+    q, k, v = rand((2, Sq, 4, 8), 64), rand((2, Skv, 2, 8), 65), rand((2, Skv, 2, 8), 66)
+    a = oracle.attention(q, k, v, 0.4, True, 5)
+    b = oracle.attention(q, k, v, 0.4, True, 5, positions=np.arange(Sq) + Skv - Sq)
+    assert np.array_equal(a, b)
+
+
+def test_varlen_positions_match_sdpa_with_a_position_mask():
+    lens_q, lens_kv = [6, 4, 9], [10, 4, 20]
+    q, k, v, cq, ck = packed_case(lens_q, lens_kv, 4, 2, 8, 67)
+    rng = np.random.default_rng(68)
+    pos = np.concatenate([np.sort(rng.integers(0, L, n)) for n, L in zip(lens_q, lens_kv)])
+    o = oracle.attention_varlen(q, k, v, cq, ck, 0.5, True, 4, positions=pos)
+    seg_q = np.repeat(np.arange(3), lens_q)
+    seg_k = np.repeat(np.arange(3), lens_kv)
+    idx_k = np.arange(k.shape[0]) - ck[seg_k]
+    mask = (seg_q[:, None] == seg_k[None, :]) & (idx_k[None, :] <= pos[:, None]) & (idx_k[None, :] >= pos[:, None] - 3)
+    tq = torch.from_numpy(q).permute(1, 0, 2)[None]
+    tk, tv = (torch.from_numpy(x).permute(1, 0, 2)[None] for x in (k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(mask), scale=0.5,
+                                                           enable_gqa=True)[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
