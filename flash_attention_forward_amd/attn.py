@@ -54,7 +54,7 @@ def lib() -> ctypes.CDLL:
                                       i32, i32, f32, i32, i32, vp, vp, vp]
     L.attn_prefill_fwd_ex.restype = i32
     L.attn_prefill_varlen_fwd.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, i32, i32, i32, i32, vp,
-                                          vp, i32, i32, i32, f32, i32, i32, vp, vp, vp]
+                                          vp, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp]
     L.attn_prefill_varlen_fwd.restype = i32
     L.attn_decode_fwd.argtypes = [vp, Strides, vp, vp, Strides, vp, i32, i32, vp, i32, i32, i32, i32, i32, i32,
                                   f32, i32, vp, vp, i32, i32, vp]
@@ -163,9 +163,11 @@ def _strides3(t, name: str) -> Strides:
 
 
 def attn_prefill_varlen_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int, max_seqlen_kv: int,
-                            scale: float, causal: bool, window: int = 0, lse=None, sinks=None, stream=None) -> None:
+                            scale: float, causal: bool, window: int = 0, lse=None, sinks=None, positions=None,
+                            stream=None) -> None:
     """Packed sequences: q, o [total_q, Hq, D]; k, v [total_kv, Hkv, D]; cu_seqlens_* int32 [B + 1] on the GPU.
-    lse: float32 [total_q, Hq] out; sinks: float32 [Hq] in; both optional."""
+    lse: float32 [total_q, Hq] out; sinks: float32 [Hq] in; positions: int32 [total_q] in (each row's position
+    within its sequence's keys, nondecreasing per sequence); all optional."""
     import torch
 
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (cu_seqlens_q, "cu_seqlens_q"),
@@ -185,11 +187,15 @@ def attn_prefill_varlen_fwd(q, k, v, o, cu_seqlens_q, cu_seqlens_kv, max_seqlen_
     B = cu_seqlens_q.numel() - 1
     lse = _f32_vec(lse, "lse", Tq * Hq)
     sinks = _f32_vec(sinks, "sinks", Hq)
+    if positions is not None:
+        _gpu(positions, "positions")
+        if positions.dtype != torch.int32 or not positions.is_contiguous() or positions.numel() != Tq:
+            raise ValueError(f"positions must be a contiguous int32 tensor of {Tq} elements")
     rc = lib().attn_prefill_varlen_fwd(_ptr(q), _strides3(q, "q"), _ptr(k), _strides3(k, "k"), _ptr(v),
                                        _strides3(v, "v"), _ptr(o), _strides3(o, "o"), _dtype_code(q), B, Hq, Hkv,
                                        _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), int(max_seqlen_q), int(max_seqlen_kv),
                                        D, float(scale), int(bool(causal)), int(window), _ptr(lse), _ptr(sinks),
-                                       _stream(stream))
+                                       _ptr(positions), _stream(stream))
     _check("attn_prefill_varlen_fwd", rc)
 
 
@@ -286,7 +292,7 @@ def prefill(q, k, v, scale: float | None = None, causal: bool = False, window: i
 
 
 def prefill_varlen(q, k, v, seqlens_q, seqlens_kv=None, scale: float | None = None, causal: bool = False,
-                   window: int = 0, out=None, stream=None, sinks=None, return_lse: bool = False):
+                   window: int = 0, out=None, stream=None, sinks=None, return_lse: bool = False, positions=None):
     """Packed-sequence prefill from per-sequence lengths (host ints); the offsets go to the GPU as int32."""
     import torch
 
@@ -299,7 +305,7 @@ def prefill_varlen(q, k, v, seqlens_q, seqlens_kv=None, scale: float | None = No
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if return_lse else None
     sc = default_scale(q.shape[-1]) if scale is None else scale
     attn_prefill_varlen_fwd(q, k, v, o, cu_q, cu_k, max(seqlens_q, default=0), max(seqlens_kv, default=0), sc, causal,
-                            window, lse, sinks, stream)
+                            window, lse, sinks, positions, stream)
     return (o, lse) if return_lse else o
 
 

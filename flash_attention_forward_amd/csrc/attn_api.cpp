@@ -72,7 +72,7 @@ int prefill_impl(const void* q, attn_strides q_st, const void* k, attn_strides k
                  attn_strides v_st, void* o, attn_strides o_st, attn_dtype dtype, int batch, int n_q_heads,
                  int n_kv_heads, int seqlen_q, int seqlen_kv, int head_dim, float scale, int causal, int window,
                  float* lse, const float* sinks, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
-                 void* hip_stream) {
+                 const int32_t* positions, void* hip_stream) {
     if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
     if (batch < 0 || n_q_heads < 0 || n_kv_heads < 0 || seqlen_q < 0 || seqlen_kv < 0 || head_dim <= 0)
         return ATTN_ERR_INVALID;
@@ -89,6 +89,7 @@ int prefill_impl(const void* q, attn_strides q_st, const void* k, attn_strides k
     if (!aligned4(lse) || !aligned4(sinks)) return ATTN_ERR_INVALID;
     if ((cu_seqlens_q == nullptr) != (cu_seqlens_kv == nullptr)) return ATTN_ERR_INVALID;
     if (cu_seqlens_q && (!aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_kv))) return ATTN_ERR_INVALID;
+    if (!aligned4(positions)) return ATTN_ERR_INVALID;
     // lane offsets inside one 64-row K/V tile are kept in 32 bits
     if (k_st.seq * 64 + head_dim >= ((int64_t)1 << 31) || v_st.seq * 64 + head_dim >= ((int64_t)1 << 31))
         return ATTN_ERR_UNSUPPORTED;
@@ -107,6 +108,7 @@ int prefill_impl(const void* q, attn_strides q_st, const void* k, attn_strides k
     p.sinks = sinks;
     p.cu_seqlens_q = cu_seqlens_q;
     p.cu_seqlens_kv = cu_seqlens_kv;
+    p.positions = positions;
     p.xcd_chunks = ((int64_t)batch * n_kv_heads) % 8 == 0;
     const int mask = !causal ? attn::kMaskNone : (p.window > 0 ? attn::kMaskCausalWindow : attn::kMaskCausal);
     return status_of(attn::launch_prefill(p, (int)dtype, head_dim, mask, (hipStream_t)hip_stream));
@@ -120,7 +122,7 @@ int attn_prefill_fwd_ex(const void* q, attn_strides q_st, const void* k, attn_st
                         int n_kv_heads, int seqlen_q, int seqlen_kv, int head_dim, float scale, int causal,
                         int window, float* lse, const float* sinks, void* hip_stream) {
     return prefill_impl(q, q_st, k, k_st, v, v_st, o, o_st, dtype, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_kv,
-                        head_dim, scale, causal, window, lse, sinks, nullptr, nullptr, hip_stream);
+                        head_dim, scale, causal, window, lse, sinks, nullptr, nullptr, nullptr, hip_stream);
 }
 
 int attn_prefill_varlen_fwd(const void* q, attn_strides q_st, const void* k, attn_strides k_st, const void* v,
@@ -128,11 +130,11 @@ int attn_prefill_varlen_fwd(const void* q, attn_strides q_st, const void* k, att
                             int n_q_heads, int n_kv_heads, const int32_t* cu_seqlens_q,
                             const int32_t* cu_seqlens_kv, int max_seqlen_q, int max_seqlen_kv, int head_dim,
                             float scale, int causal, int window, float* lse, const float* sinks,
-                            void* hip_stream) {
+                            const int32_t* positions, void* hip_stream) {
     if (batch > 0 && (!cu_seqlens_q || !cu_seqlens_kv)) return ATTN_ERR_INVALID;
     return prefill_impl(q, q_st, k, k_st, v, v_st, o, o_st, dtype, batch, n_q_heads, n_kv_heads, max_seqlen_q,
                         max_seqlen_kv, head_dim, scale, causal, window, lse, sinks, cu_seqlens_q, cu_seqlens_kv,
-                        hip_stream);
+                        positions, hip_stream);
 }
 
 int attn_prefill_fwd(const void* q, attn_strides q_st, const void* k, attn_strides k_st, const void* v,

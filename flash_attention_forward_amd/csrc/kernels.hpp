@@ -29,6 +29,10 @@ struct PrefillParams {
     // [cu_seqlens_kv[b], cu_seqlens_kv[b+1]) (batch strides unused; lse is [total_q, n_q_heads])
     const int32_t* cu_seqlens_q;
     const int32_t* cu_seqlens_kv;
+    // NULL, or the position of every query row ([batch * seqlen_q] or [total_q], the
+    // lse row order); key j is visible to a row at position P iff j <= P (causal)
+    // and j >= P - window + 1. Nondecreasing within a sequence.
+    const int32_t* positions;
     int xcd_chunks;   // deal workgroups to XCDs in kv-head groups (batch * n_kv_heads % 8 == 0)
 };
 

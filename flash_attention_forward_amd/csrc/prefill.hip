@@ -138,9 +138,12 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     const int q0 = qt * PF_BM;
     if (q0 >= sq) return;  // a tile past this sequence's end (packed sequences only)
     const int qlast = min(q0 + PF_BM, sq) - 1;
+    // Position of query row i: i + off (bottom-right alignment), or the caller's
+    // positions of packed rows (nondecreasing within a sequence).
+    auto pos_of = [&](int i) -> int { return p.positions ? p.positions[lse_at + min(i, sq - 1)] : i + off; };
     int kv_lo = 0, kv_hi = skv;
-    if (MASK >= kMaskCausal) kv_hi = min(kv_hi, qlast + off + 1);
-    if (MASK == kMaskCausalWindow) kv_lo = max(0, q0 + off - p.window + 1);
+    if (MASK >= kMaskCausal) kv_hi = min(kv_hi, pos_of(qlast) + 1);
+    if (MASK == kMaskCausalWindow) kv_lo = max(0, pos_of(q0) - p.window + 1);
     const int j_begin = kv_lo / PF_BN;
     const int j_end = kv_hi > kv_lo ? (kv_hi + PF_BN - 1) / PF_BN : j_begin;
 
@@ -148,7 +151,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     const int wq1 = min(wq0 + 31, sq - 1); // last valid row of this wave
     const bool wave_live = wq0 < sq;
     const int my_q = wq0 + l32;                    // the query row this lane owns
-    const int my_pos = my_q + off;
+    const int my_pos = pos_of(my_q);
+    const int wpos0 = pos_of(wq0), wpos1 = pos_of(wq1);  // positions of the wave's first and last rows
 
     // Q fragments: B operand of S^T = K Q^T (lane: row l32, d = 16s + 8hf .. +8).
     s16x8 qf[D / 16];
@@ -261,15 +265,15 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     auto tile_empty = [&](int j) __attribute__((always_inline)) {
         const int kv0 = j * PF_BN;
         bool e = !wave_live || j >= j_end;
-        if (MASK >= kMaskCausal) e |= kv0 > wq1 + off;
-        if (MASK == kMaskCausalWindow) e |= kv0 + PF_BN - 1 < wq0 + off - p.window + 1;
+        if (MASK >= kMaskCausal) e |= kv0 > wpos1;
+        if (MASK == kMaskCausalWindow) e |= kv0 + PF_BN - 1 < wpos0 - p.window + 1;
         return e;
     };
     auto tile_full = [&](int j) __attribute__((always_inline)) {
         const int kv0 = j * PF_BN;
         bool f = kv0 + PF_BN <= skv;
-        if (MASK >= kMaskCausal) f &= kv0 + PF_BN - 1 <= wq0 + off;
-        if (MASK == kMaskCausalWindow) f &= kv0 >= wq1 + off - p.window + 1;
+        if (MASK >= kMaskCausal) f &= kv0 + PF_BN - 1 <= wpos0;
+        if (MASK == kMaskCausalWindow) f &= kv0 >= wpos1 - p.window + 1;
         return f;
     };
 
@@ -576,13 +580,16 @@ __global__ __launch_bounds__(256) void prefill_f32(PrefillParams p) {
     const int q0 = qt * F32_BM;
     if (q0 >= sq) return;  // a tile past this sequence's end (packed sequences only)
     const int qlast = min(q0 + F32_BM, sq) - 1;
+    // Position of query row i: i + off (bottom-right alignment), or the caller's
+    // positions of packed rows (nondecreasing within a sequence).
+    auto pos_of = [&](int i) -> int { return p.positions ? p.positions[lse_at + min(i, sq - 1)] : i + off; };
     int kv_lo = 0, kv_hi = skv;
-    if (MASK >= kMaskCausal) kv_hi = min(kv_hi, qlast + off + 1);
-    if (MASK == kMaskCausalWindow) kv_lo = max(0, q0 + off - p.window + 1);
+    if (MASK >= kMaskCausal) kv_hi = min(kv_hi, pos_of(qlast) + 1);
+    if (MASK == kMaskCausalWindow) kv_lo = max(0, pos_of(q0) - p.window + 1);
     const int j_begin = kv_lo / F32_BN;
     const int j_end = kv_hi > kv_lo ? (kv_hi + F32_BN - 1) / F32_BN : j_begin;
 
-    const int my_q = q0 + r, my_pos = my_q + off;
+    const int my_q = q0 + r, my_pos = pos_of(my_q);
     const bool live = my_q < sq;
     float qv[DQ], acc[DQ];
     {

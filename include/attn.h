@@ -143,8 +143,18 @@ int attn_prefill_fwd_ex(const void* q, attn_strides q_st, const void* k, attn_st
  * cached prefix), causal and window apply to those positions, GQA and the
  * optional lse ([total_q, n_q_heads], natural log) and sinks are as for
  * attn_prefill_fwd_ex. A sequence with no query rows writes nothing; one
- * with no keys outputs zeros. The offsets are not validated on the host:
- * offsets outside the tensors are undefined behaviour.
+ * with no keys outputs zeros.
+ *   positions  NULL, or device int32 [total_q] (4-byte aligned): the position
+ *          of every packed query row within its sequence's keys, replacing
+ *          i + (len_kv - len_q) — the positions input of the minfer page's
+ *          kernel (section 3.1: the key bound is the position of the tile's
+ *          last row plus one, and key j is visible to a row at position P iff
+ *          j <= P). Causal and window apply to these positions; they must be
+ *          nondecreasing within each sequence (the tile bounds are taken from
+ *          a tile's first and last rows). A position at or past len_kv sees
+ *          all keys; a negative one sees none.
+ * The offsets and positions are not validated on the host: offsets outside
+ * the tensors are undefined behaviour.
  */
 int attn_prefill_varlen_fwd(const void* q, attn_strides q_st, const void* k, attn_strides k_st,
                             const void* v, attn_strides v_st, void* o, attn_strides o_st,
@@ -152,7 +162,8 @@ int attn_prefill_varlen_fwd(const void* q, attn_strides q_st, const void* k, att
                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
                             int max_seqlen_q, int max_seqlen_kv, int head_dim,
                             float scale, int causal, int window,
-                            float* lse, const float* sinks, void* hip_stream);
+                            float* lse, const float* sinks, const int32_t* positions,
+                            void* hip_stream);
 
 /*
  * Decode attention against a KV cache, split along the cache (split-KV).

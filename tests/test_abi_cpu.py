@@ -212,18 +212,19 @@ def test_decode_fp8_accepts_byte_strides():
 def prefill_varlen(**kw):
     a = dict(q=FAKE, qs=st(0, 8 * 128, 128), k=FAKE, ks=st(0, 128, 128), v=FAKE, vs=st(0, 128, 128), o=FAKE,
              os=st(0, 8 * 128, 128), dtype=A.ATTN_BF16, batch=4, hq=8, hkv=1, cuq=FAKE, cuk=FAKE, mq=2048, mk=2048,
-             d=128, scale=0.088, causal=1, window=0, lse=None, sinks=None)
+             d=128, scale=0.088, causal=1, window=0, lse=None, sinks=None, pos=None)
     a.update(kw)
     return A.lib().attn_prefill_varlen_fwd(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["o"], a["os"],
                                            a["dtype"], a["batch"], a["hq"], a["hkv"], a["cuq"], a["cuk"], a["mq"],
                                            a["mk"], a["d"], a["scale"], a["causal"], a["window"], a["lse"],
-                                           a["sinks"], None)
+                                           a["sinks"], a["pos"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(cuq=None), INVALID), (dict(cuk=None), INVALID), (dict(cuq=FAKE + 2), INVALID), (dict(cuk=FAKE + 1), INVALID),
     (dict(hq=6, hkv=4), INVALID), (dict(d=96), UNSUPPORTED), (dict(window=16, causal=0), UNSUPPORTED),
     (dict(mq=-1), INVALID), (dict(mk=-5), INVALID), (dict(lse=FAKE + 2), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(pos=FAKE + 2), INVALID),
     (dict(qs=st(0, 8 * 128 + 4, 128)), INVALID),  # 8-byte token stride: rows not 16-byte aligned
     (dict(ks=st(0, 1 << 25, 128)), UNSUPPORTED),  # a 64-row tile would span more than 2^31 elements
     (dict(batch=0, cuq=None, cuk=None), 0), (dict(mq=0), 0),  # empty: nothing is enqueued

@@ -120,3 +120,58 @@ def test_varlen_full_size_sampled():
         ref, _ = oracle.attention_rows(qa[None, q0:q1], ka[None, k0:k1], va[None, k0:k1], spec.scale_f32, True, 0,
                                        rows)
         check(got[q0 + rows[:, 1], rows[:, 2]], ref, spec.dtype, f"sequence {b}")
+
+
+def monotone_positions(inp, seed, gap=True):
+    """Nondecreasing positions per sequence inside [0, len_kv) (sorted draws, so repeats and gaps occur)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for Lq, Lk in zip(inp.lens_q.tolist(), inp.lens_kv.tolist()):
+        if Lq == 0:
+            continue
+        out.append(np.sort(rng.integers(0, max(Lk, 1), Lq)) if gap else np.arange(Lq) + Lk - Lq)
+    return np.concatenate(out).astype(np.int32) if out else np.zeros(0, np.int32)
+
+
+def run_pos(inp, pos, lse=False):
+    import flash_attention_forward_amd as F
+
+    torch = torch_cuda()
+    s = inp.spec
+    q, k, v = dev(inp.q, s.dtype), dev(inp.k, s.dtype), dev(inp.v, s.dtype)
+    o = torch.empty_like(q)
+    cq = torch.from_numpy(inp.cu_q.astype(np.int32)).cuda()
+    ck = torch.from_numpy(inp.cu_kv.astype(np.int32)).cuda()
+    lse_t = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda") if lse else None
+    F.attn_prefill_varlen_fwd(q, k, v, o, cq, ck, int(inp.lens_q.max(initial=0)), int(inp.lens_kv.max(initial=0)),
+                              s.scale_f32, s.causal, s.window, lse_t, None, torch.from_numpy(pos).cuda())
+    torch.cuda.synchronize()
+    return host64(o, s.dtype), (lse_t.cpu().numpy().astype(np.float64) if lse else None)
+
+
+@pytest.mark.parametrize("name", ["bf16_causal_ragged", "f16_window_prefix", "bf16_d256_causal", "f32_d64_causal_prefix",
+                                  "f32_d128_window"])
+def test_varlen_positions_parity(name):
+    spec, lq, pre = CASES[name]
+    inp = W.make_varlen(spec, seed=800 + len(name), lens_q=lq, prefixes=pre)
+    pos = monotone_positions(inp, 9)
+    say("varlen positions", name)
+    got, lse = run_pos(inp, pos, lse=True)
+    s = spec
+    f64 = lambda a: W.as_f64(a, s.dtype)
+    ref, ref_lse = oracle.attention_varlen(f64(inp.q), f64(inp.k), f64(inp.v), inp.cu_q, inp.cu_kv, s.scale_f32,
+                                           s.causal, s.window, return_lse=True, positions=pos)
+    check(got, ref, s.dtype, name)
+    fin = np.isfinite(ref_lse)
+    assert (np.isneginf(lse) == ~fin).all()
+    assert np.abs(lse[fin] - ref_lse[fin]).max(initial=0.0) <= LSE_TOL[s.dtype]
+
+
+@pytest.mark.parametrize("name", ["bf16_causal_empty_and_prefix", "f16_window_prefix", "f32_d128_window"])
+def test_varlen_positions_of_the_default_alignment_are_bitwise_the_default(name):
+    spec, lq, pre = CASES[name]
+    inp = W.make_varlen(spec, seed=900 + len(name), lens_q=lq, prefixes=pre)
+    say("varlen default positions", name)
+    got, _ = run_pos(inp, monotone_positions(inp, 0, gap=False))
+    plain, _ = run(inp)
+    assert np.array_equal(got, plain)
