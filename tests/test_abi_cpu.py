@@ -231,3 +231,15 @@ def prefill_varlen(**kw):
 ])
 def test_prefill_varlen_rejects_before_any_hip_call(kw, status):
     assert prefill_varlen(**kw) == status
+
+
+@pytest.mark.parametrize("batch,hkv,max_len,ps", [(32, 8, 32768, 16), (1, 8, 32768, 16), (4, 8, 2048, 0), (128, 8, 4096, 16),
+                                                  (32, 8, 32768, 1), (32, 8, 32768, 24), (2, 1, 100, 100), (64, 4, 8192, 8)])
+def test_auto_split_len_is_accepted_by_the_library_rules(batch, hkv, max_len, ps):
+    sl = A.auto_split_len(batch, hkv, max_len, ps)
+    assert sl > 0 and sl % 16 == 0
+    if ps:
+        assert sl % ps == 0 and sl // ps <= 256
+    assert A.max_splits_for(max_len, sl) * sl >= max_len
+    if (batch, hkv, max_len, ps) == (32, 8, 32768, 16):
+        assert sl == 4096  # the paged-decode workload's measured best
