@@ -326,6 +326,18 @@ def main():
     vev[1].record(stream)
     torch.cuda.synchronize()
     varlen_ms = vev[0].elapsed_time(vev[1]) / 10
+    # the same launch with every row's position passed explicitly (the default alignment)
+    vpos = torch.from_numpy(np.concatenate([np.arange(lq) + lk - lq for lq, lk in zip(vin.lens_q, vin.lens_kv)])
+                            .astype(np.int32)).to(dev)
+    for _ in range(3):
+        F.attn_prefill_varlen_fwd(vq, vk, vv, vo, vcq, vck, vmq, vmk, vspec.scale_f32, True, 0, None, None, vpos)
+    vev = [ev(), ev()]
+    vev[0].record(stream)
+    for _ in range(10):
+        F.attn_prefill_varlen_fwd(vq, vk, vv, vo, vcq, vck, vmq, vmk, vspec.scale_f32, True, 0, None, None, vpos)
+    vev[1].record(stream)
+    torch.cuda.synchronize()
+    varlen_pos_ms = vev[0].elapsed_time(vev[1]) / 10
     varlen_flops = 4.0 * vspec.head_dim * vspec.n_q_heads * W.varlen_visible_pairs(vin)
     del vq, vk, vv, vo
 
@@ -484,6 +496,7 @@ def main():
             "flops": varlen_flops,
             "ms": round(varlen_ms, 4),
             "tflops": round(varlen_flops / (varlen_ms * 1e-3) / 1e12, 2),
+            "ms_with_positions": round(varlen_pos_ms, 4),
             "note": "packed causal prompts, 28/4 heads, D128, bf16, lengths uniform in [256, 4096]",
             "roofline": {"bound": "mfma", "achieved": round(varlen_flops / (varlen_ms * 1e-3) / 1e12, 2),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
