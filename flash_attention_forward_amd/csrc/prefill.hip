@@ -327,14 +327,21 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             s1 = mfma32x32x16<BF16>(a1, qf[s], s1);
         }
     };
+    // This lane's visible keys form one range [key_lo, key_lo + key_span]
+    // (span < 0: none), so each score takes one unsigned compare: key - key_lo
+    // in [0, span].
+    int key_hi = skv - 1, key_lo = 0;
+    if (MASK >= kMaskCausal) key_hi = min(key_hi, my_pos);
+    if (MASK == kMaskCausalWindow) key_lo = max(key_lo, my_pos - p.window + 1);
+    const bool none_visible = key_hi < key_lo;
+    const uint32_t key_span = none_visible ? 0u : (uint32_t)(key_hi - key_lo);
+    if (none_visible) key_lo = INT_MIN / 2;  // no key of any tile lies at key_lo + [0, 0]
     auto mask_half = [&](f32x16& sacc, int kv0, int t) __attribute__((always_inline)) {
+        const int base = kv0 + 32 * t + 4 * hf - key_lo;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
-            bool keep = key < skv;
-            if (MASK >= kMaskCausal) keep &= key <= my_pos;
-            if (MASK == kMaskCausalWindow) keep &= key >= my_pos - p.window + 1;
-            sacc[r] = keep ? sacc[r] : kMaskedScore;
+            const uint32_t d = (uint32_t)(base + 8 * (r >> 2) + (r & 3));
+            sacc[r] = d <= key_span ? sacc[r] : kMaskedScore;
         }
     };
     // Row max of a tile (raw scores), combined over the two lane halves.
