@@ -175,3 +175,23 @@ def test_varlen_positions_of_the_default_alignment_are_bitwise_the_default(name)
     got, _ = run_pos(inp, monotone_positions(inp, 0, gap=False))
     plain, _ = run(inp)
     assert np.array_equal(got, plain)
+
+
+@pytest.mark.parametrize("name", ["bf16_causal_ragged", "f16_window_prefix", "f32_d64_causal_prefix"])
+def test_varlen_positions_outside_the_keys(name):
+    """Positions below 0 see no key (zeros, lse -inf); positions at or past len_kv see all keys."""
+    spec, lq, pre = CASES[name]
+    inp = W.make_varlen(spec, seed=950 + len(name), lens_q=lq, prefixes=pre)
+    rng = np.random.default_rng(11)
+    pos = np.concatenate([np.sort(rng.integers(-40, Lk + 40, Lq)) for Lq, Lk in
+                          zip(inp.lens_q.tolist(), inp.lens_kv.tolist()) if Lq > 0]).astype(np.int32)
+    say("varlen positions outside the keys", name)
+    got, lse = run_pos(inp, pos, lse=True)
+    f64 = lambda a: W.as_f64(a, spec.dtype)
+    ref, ref_lse = oracle.attention_varlen(f64(inp.q), f64(inp.k), f64(inp.v), inp.cu_q, inp.cu_kv, spec.scale_f32,
+                                           spec.causal, spec.window, return_lse=True, positions=pos)
+    check(got, ref, spec.dtype, name)
+    fin = np.isfinite(ref_lse)
+    assert (~fin).any() and (np.isneginf(lse) == ~fin).all()
+    assert np.all(got[~fin.any(axis=1)] == 0.0)
+    assert np.abs(lse[fin] - ref_lse[fin]).max(initial=0.0) <= LSE_TOL[spec.dtype]
