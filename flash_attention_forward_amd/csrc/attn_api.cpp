@@ -174,7 +174,7 @@ int decode_fwd_impl(const void* q, attn_strides q_st, const void* k_cache, const
     }
     if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
     if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
-    if ((int64_t)(n_q_heads / n_kv_heads) * s_active > 16) return ATTN_ERR_UNSUPPORTED;
+    if ((int64_t)(n_q_heads / n_kv_heads) * s_active > (head_dim <= 128 ? 32 : 16)) return ATTN_ERR_UNSUPPORTED;
     if (max_splits > 65535 || batch > 65535) return ATTN_ERR_UNSUPPORTED;
     const int eb = elem_bytes(dtype);
     if (!q || !k_cache || !v_cache || !cache_len || !part_o || !part_lse) return ATTN_ERR_INVALID;

@@ -143,7 +143,7 @@ __device__ __forceinline__ int dc_kswz(int row) {
     return D == 64 ? ((row >> 1) & 7) : (row & 15);
 }
 
-template <bool BF16, int D, int MODE, int HW>
+template <bool BF16, int D, int MODE, int HW, int QB>
 __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
     constexpr int NKS = D / 32;              // k-steps of S^T = K Q^T
     constexpr int NDT = D / 16;              // 16-row d tiles of O^T
@@ -168,10 +168,18 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
     const int hk = blockIdx.x * HW + w, split = blockIdx.y, b = blockIdx.z;
 
     const int t0 = split * p.split_len;
+    // Query rows (G * s_active of them) ride the 16 MFMA columns, in QB blocks
+    // of 16: block qb, column n is row 16 qb + n.
     const int nrows = p.group * p.s_active;
-    const bool row_real = n < nrows;
-    const int qi = row_real ? n / p.group : 0;
-    const int qh = hk * p.group + (row_real ? n % p.group : 0);
+    bool row_real[QB];
+    int qi[QB], qh[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int row = 16 * qb + n;
+        row_real[qb] = row < nrows;
+        qi[qb] = row_real[qb] ? row / p.group : 0;
+        qh[qb] = hk * p.group + (row_real[qb] ? row % p.group : 0);
+    }
 
     // Requested together before anything waits: cache_len[b], this split's
     // whole slice of the page table (clamped to the table row; entries past
@@ -189,33 +197,41 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
         }
     }
     // Q fragments: B operand of S^T = K Q^T (lane: column n, d = 32ks + 8g .. +8).
-    s16x8 qf[NKS];
-    {
-        const uint16_t* qrow = (const uint16_t*)p.q + (int64_t)b * p.qs.batch + (int64_t)qi * p.qs.seq +
-                               (int64_t)qh * p.qs.head + 8 * g;
+    s16x8 qf[QB][NKS];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const uint16_t* qrow = (const uint16_t*)p.q + (int64_t)b * p.qs.batch + (int64_t)qi[qb] * p.qs.seq +
+                               (int64_t)qh[qb] * p.qs.head + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             uint4 x = make_uint4(0, 0, 0, 0);
-            if (row_real) x = *(const uint4*)(qrow + 32 * ks);
+            if (row_real[qb]) x = *(const uint4*)(qrow + 32 * ks);
             x.x ^= p.qflip; x.y ^= p.qflip; x.z ^= p.qflip; x.w ^= p.qflip;
-            qf[ks] = __builtin_bit_cast(s16x8, x);
+            qf[qb][ks] = __builtin_bit_cast(s16x8, x);
         }
     }
     const int len = p.cache_len[b];
     if (t0 >= len) return;  // this split is past the cache: nothing is written (uniform in the workgroup)
     const int t1 = min(len, t0 + p.split_len);
-    const int qpos = len - p.s_active + qi;  // the query sits at the end of its cache
-    const int64_t prow = (((int64_t)b * p.s_active + qi) * p.n_q_heads + qh) * p.max_splits + split;
+    int qpos[QB];      // the queries sit at the end of their cache
+    int64_t prow[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        qpos[qb] = len - p.s_active + qi[qb];
+        prow[qb] = (((int64_t)b * p.s_active + qi[qb]) * p.n_q_heads + qh[qb]) * p.max_splits + split;
+    }
 
     // Keys this split may use: [t0, t1) clipped to the window of the earliest query.
     int tlo = t0;
     if (p.window > 0) tlo = max(tlo, (len - p.s_active) - p.window + 1);
     if (tlo >= t1) {  // no visible key: empty partial
-        if (row_real) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            if (!row_real[qb]) continue;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
-                *(float4*)(p.part_o + prow * D + 16 * dt + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (g == 0) p.part_lse[prow] = -__builtin_inff();
+                *(float4*)(p.part_o + prow[qb] * D + 16 * dt + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (g == 0) p.part_lse[prow[qb]] = -__builtin_inff();
         }
         return;
     }
@@ -290,18 +306,16 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
     // arithmetic) plus a per-lane byte offset fixed for the whole loop (row
     // within the group, swizzled chunk), so its loads cost no vector ALU work.
     const bool lane_addr = MODE != kDecodeGeneric && p.lane_addr32;
-    auto load_rows = [&](uint16_t* dst, const uint16_t* base, int tb, bool is_k) {
+    auto load_rows = [&](uint16_t* dst, const uint16_t* base, int tb, bool is_k) __attribute__((always_inline)) {
         if (lane_addr && tb + DC_KB <= t1) {
-            int64_t gofs[2];
-#pragma unroll
-            for (int gi = 0; gi < 2; ++gi) gofs[gi] = group_off(tb + 16 * gi);
+            const int64_t g0 = group_off(tb), g1 = group_off(tb + 16);
 #pragma unroll
             for (int i = 0; i < VLD; ++i) {
                 // (loop-invariant: computed once, outside the key loop)
                 const int row = i * RPL + lane / CPR;
                 const int c = cs ^ (is_k ? dc_kswz<D>(row) : dc_vswz<D>(row));
                 const uint32_t lane_off = (uint32_t)(((row & 15) * seq + 8 * c) * 2);
-                const char* gb = (const char*)(base + gofs[(i * RPL) / 16]);
+                const char* gb = (const char*)(base + (i * RPL < 16 ? g0 : g1));
                 __builtin_amdgcn_global_load_lds(gb + lane_off,
                                                  (__attribute__((address_space(3))) void*)(dst + 512 * i), 16, 0,
                                                  kStreamPolicy);
@@ -318,10 +332,15 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
                                              16, 0, kStreamPolicy);
         }
     };
-    float m_i = kMaxInit, l_i = 0.f;
-    f32x4 o[NDT];
+    float m_i[QB], l_i[QB];
+    f32x4 o[QB][NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{};
+    for (int qb = 0; qb < QB; ++qb) {
+        m_i[qb] = kMaxInit;
+        l_i[qb] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[qb][dt] = f32x4{};
+    }
 
     // One block: wait for its loads, S^T = K Q^T, refill these K registers with
     // block it+2, online softmax, O^T += V^T P^T, refill this V tile with block it+2.
@@ -330,22 +349,30 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
         wait_vmcnt<2 * VLD>();  // only block it+1's loads may still be in flight
 
         // S^T = K Q^T: lane (n, g) reads key row 16gi + n, d chunk 4ks + g.
-        f32x4 sacc[2] = {f32x4{}, f32x4{}};
+        f32x4 sacc[QB][2];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sacc[qb][0] = sacc[qb][1] = f32x4{};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
             for (int gi = 0; gi < 2; ++gi) {
                 const int row = 16 * gi + n;
                 const s16x8 a = *(const s16x8*)&K[row * D + 8 * ((4 * ks + g) ^ dc_kswz<D>(row))];
-                sacc[gi] = mfma16x16x32<BF16>(a, qf[ks], sacc[gi]);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) sacc[qb][gi] = mfma16x16x32<BF16>(a, qf[qb][ks], sacc[qb][gi]);
             }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // K fragment reads done before the tile is refilled
         load_rows(K, kbase, tb + 2 * DC_KB, true);  // block it+2 (clamped rows when past the end)
 
         // rows at or beyond t1 hold another row's keys: masked in the edge blocks
-        const s16x8 pb = tb + DC_KB <= t_full && tb >= t_from
-                             ? dc_block_probs<BF16, false>(sacc, o, m_i, l_i, p.c, tb, g, t1, qpos, p.window)
-                             : dc_block_probs<BF16, true>(sacc, o, m_i, l_i, p.c, tb, g, t1, qpos, p.window);
+        const bool full = tb + DC_KB <= t_full && tb >= t_from;
+        s16x8 pb[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            pb[qb] = full ? dc_block_probs<BF16, false>(sacc[qb], o[qb], m_i[qb], l_i[qb], p.c, tb, g, t1, qpos[qb],
+                                                        p.window)
+                          : dc_block_probs<BF16, true>(sacc[qb], o[qb], m_i[qb], l_i[qb], p.c, tb, g, t1, qpos[qb],
+                                                       p.window);
 
         // O^T[d, q] += V^T[d, keys] P^T[keys, q]; lane n of group g reads rows
         // 4g + n/4 (and 16 + ...), column 16dt + 4(n%4), receiving column 16dt + n.
@@ -355,7 +382,9 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
             const int r0 = 4 * g + (n >> 2), r1 = r0 + 16;
             const s16x4 lo = lds_read_tr16(&V[r0 * D + 8 * (c ^ dc_vswz<D>(r0)) + half]);
             const s16x4 hi4 = lds_read_tr16(&V[r1 * D + 8 * (c ^ dc_vswz<D>(r1)) + half]);
-            o[dt] = mfma16x16x32<BF16>(concat4(lo, hi4), pb, o[dt]);
+            const s16x8 vf = concat4(lo, hi4);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) o[qb][dt] = mfma16x16x32<BF16>(vf, pb[qb], o[qb][dt]);
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // transpose reads done before the tile is refilled
         load_rows(V, vbase, tb + 2 * DC_KB, false);
@@ -372,14 +401,19 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
     }
     wait_vmcnt<0>();  // drain the clamped prefetches before the wave ends
 
-    const float l_tot = sum_over_groups(l_i);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (row_real) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-            *(float4*)(p.part_o + prow * D + 16 * dt + 4 * g) =
-                make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
-        if (g == 0) p.part_lse[prow] = l_tot > 0.f ? (m_i + __log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
+    for (int qb = 0; qb < QB; ++qb) {
+        const float l_tot = sum_over_groups(l_i[qb]);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (row_real[qb]) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+                *(float4*)(p.part_o + prow[qb] * D + 16 * dt + 4 * g) =
+                    make_float4(o[qb][dt][0] * inv, o[qb][dt][1] * inv, o[qb][dt][2] * inv, o[qb][dt][3] * inv);
+            if (g == 0)
+                p.part_lse[prow[qb]] =
+                    l_tot > 0.f ? (m_i[qb] + __log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
+        }
     }
 }
 
@@ -413,7 +447,7 @@ __device__ __forceinline__ int dc_kcswz(int row) {
     return D == 64 ? ((row >> 1) & 3) : (row & 7);
 }
 
-template <bool BF16, int D, int MODE, int HW>
+template <bool BF16, int D, int MODE, int HW, int QB>
 __global__ __launch_bounds__(64 * HW) void decode_split_f8(DecodeParams p) {
     constexpr int NKS = D / 32;   // k-steps of S^T = K Q^T
     constexpr int NDT = D / 16;   // 16-row d tiles of O^T
@@ -432,10 +466,18 @@ __global__ __launch_bounds__(64 * HW) void decode_split_f8(DecodeParams p) {
     const int hk = blockIdx.x * HW + w, split = blockIdx.y, b = blockIdx.z;
 
     const int t0 = split * p.split_len;
+    // Query rows (G * s_active of them) ride the 16 MFMA columns, in QB blocks
+    // of 16: block qb, column n is row 16 qb + n.
     const int nrows = p.group * p.s_active;
-    const bool row_real = n < nrows;
-    const int qi = row_real ? n / p.group : 0;
-    const int qh = hk * p.group + (row_real ? n % p.group : 0);
+    bool row_real[QB];
+    int qi[QB], qh[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int row = 16 * qb + n;
+        row_real[qb] = row < nrows;
+        qi[qb] = row_real[qb] ? row / p.group : 0;
+        qh[qb] = hk * p.group + (row_real[qb] ? row % p.group : 0);
+    }
 
     constexpr int PPT = (kDecodeMaxSplitPages + 64 * HW - 1) / (64 * HW);
     uint32_t pe[PPT];
@@ -450,32 +492,40 @@ __global__ __launch_bounds__(64 * HW) void decode_split_f8(DecodeParams p) {
         }
     }
     // Q fragments in the permuted d order: lane (n, g), k-step ks holds d = 64 (ks/2) + 16 g + 8 (ks%2) .. +8.
-    s16x8 qf[NKS];
-    {
-        const uint16_t* qrow = (const uint16_t*)p.q + (int64_t)b * p.qs.batch + (int64_t)qi * p.qs.seq +
-                               (int64_t)qh * p.qs.head + 16 * g;
+    s16x8 qf[QB][NKS];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const uint16_t* qrow = (const uint16_t*)p.q + (int64_t)b * p.qs.batch + (int64_t)qi[qb] * p.qs.seq +
+                               (int64_t)qh[qb] * p.qs.head + 16 * g;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             uint4 x = make_uint4(0, 0, 0, 0);
-            if (row_real) x = *(const uint4*)(qrow + 64 * (ks / 2) + 8 * (ks % 2));
+            if (row_real[qb]) x = *(const uint4*)(qrow + 64 * (ks / 2) + 8 * (ks % 2));
             x.x ^= p.qflip; x.y ^= p.qflip; x.z ^= p.qflip; x.w ^= p.qflip;
-            qf[ks] = __builtin_bit_cast(s16x8, x);
+            qf[qb][ks] = __builtin_bit_cast(s16x8, x);
         }
     }
     const int len = p.cache_len[b];
     if (t0 >= len) return;
     const int t1 = min(len, t0 + p.split_len);
-    const int qpos = len - p.s_active + qi;
-    const int64_t prow = (((int64_t)b * p.s_active + qi) * p.n_q_heads + qh) * p.max_splits + split;
+    int qpos[QB];
+    int64_t prow[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        qpos[qb] = len - p.s_active + qi[qb];
+        prow[qb] = (((int64_t)b * p.s_active + qi[qb]) * p.n_q_heads + qh[qb]) * p.max_splits + split;
+    }
 
     int tlo = t0;
     if (p.window > 0) tlo = max(tlo, (len - p.s_active) - p.window + 1);
     if (tlo >= t1) {
-        if (row_real) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            if (!row_real[qb]) continue;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
-                *(float4*)(p.part_o + prow * D + 16 * dt + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (g == 0) p.part_lse[prow] = -__builtin_inff();
+                *(float4*)(p.part_o + prow[qb] * D + 16 * dt + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (g == 0) p.part_lse[prow[qb]] = -__builtin_inff();
         }
         return;
     }
@@ -543,7 +593,7 @@ __global__ __launch_bounds__(64 * HW) void decode_split_f8(DecodeParams p) {
     // base plus this lane's fixed offset, so its loads cost no vector ALU
     // work; other blocks clamp row by row.
     const bool lane_addr = MODE != kDecodeGeneric && p.lane_addr32;
-    auto load_block = [&](uint4 (&kr)[NI], uint4 (&vr)[NI], int tb) {
+    auto load_block = [&](uint4 (&kr)[NI], uint4 (&vr)[NI], int tb) __attribute__((always_inline)) {
         if (lane_addr && tb + DC_KB <= t1) {
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
@@ -579,10 +629,15 @@ __global__ __launch_bounds__(64 * HW) void decode_split_f8(DecodeParams p) {
         return __builtin_bit_cast(s16x8, make_uint4(w[0], w[1], w[2], w[3]));
     };
 
-    float m_i = kMaxInit, l_i = 0.f;
-    f32x4 o[NDT];
+    float m_i[QB], l_i[QB];
+    f32x4 o[QB][NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{};
+    for (int qb = 0; qb < QB; ++qb) {
+        m_i[qb] = kMaxInit;
+        l_i[qb] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[qb][dt] = f32x4{};
+    }
     uint16_t* V = Vs[w];
     uint8_t* K = Kc[w];
 
@@ -603,26 +658,39 @@ __global__ __launch_bounds__(64 * HW) void decode_split_f8(DecodeParams p) {
         load_block(kr, vr, tb + 2 * DC_KB);  // this set now carries block it+2 (clamped past the end)
 
         // S^T = K Q^T from the code tile (one wave's own LDS writes are seen by its later reads)
-        f32x4 sacc[2] = {f32x4{}, f32x4{}};
+        f32x4 sacc[QB][2];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sacc[qb][0] = sacc[qb][1] = f32x4{};
 #pragma unroll
         for (int j = 0; j < NLD; ++j)
 #pragma unroll
             for (int gi = 0; gi < 2; ++gi) {
                 const int row = 16 * gi + n;
                 const uint4 c4 = *(const uint4*)&K[row * D + 16 * ((4 * j + g) ^ dc_kcswz<D>(row))];
-                sacc[gi] = mfma16x16x32<BF16>(operand8(c4.x, c4.y), qf[2 * j], sacc[gi]);
-                sacc[gi] = mfma16x16x32<BF16>(operand8(c4.z, c4.w), qf[2 * j + 1], sacc[gi]);
+                const s16x8 a0 = operand8(c4.x, c4.y), a1 = operand8(c4.z, c4.w);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    sacc[qb][gi] = mfma16x16x32<BF16>(a0, qf[qb][2 * j], sacc[qb][gi]);
+                    sacc[qb][gi] = mfma16x16x32<BF16>(a1, qf[qb][2 * j + 1], sacc[qb][gi]);
+                }
             }
-        const s16x8 pb = tb + DC_KB <= t_full && tb >= t_from
-                             ? dc_block_probs<BF16, false>(sacc, o, m_i, l_i, p.c, tb, g, t1, qpos, p.window)
-                             : dc_block_probs<BF16, true>(sacc, o, m_i, l_i, p.c, tb, g, t1, qpos, p.window);
+        const bool full = tb + DC_KB <= t_full && tb >= t_from;
+        s16x8 pb[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            pb[qb] = full ? dc_block_probs<BF16, false>(sacc[qb], o[qb], m_i[qb], l_i[qb], p.c, tb, g, t1, qpos[qb],
+                                                        p.window)
+                          : dc_block_probs<BF16, true>(sacc[qb], o[qb], m_i[qb], l_i[qb], p.c, tb, g, t1, qpos[qb],
+                                                       p.window);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
             const int c = 2 * dt + ((n & 3) >> 1), half = 4 * (n & 1);
             const int r0 = 4 * g + (n >> 2), r1 = r0 + 16;
             const s16x4 lo = lds_read_tr16(&V[r0 * D + 8 * (c ^ dc_vswz<D>(r0)) + half]);
             const s16x4 hi4 = lds_read_tr16(&V[r1 * D + 8 * (c ^ dc_vswz<D>(r1)) + half]);
-            o[dt] = mfma16x16x32<BF16>(concat4(lo, hi4), pb, o[dt]);
+            const s16x8 vf = concat4(lo, hi4);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) o[qb][dt] = mfma16x16x32<BF16>(vf, pb[qb], o[qb][dt]);
         }
     };
 
@@ -635,14 +703,19 @@ __global__ __launch_bounds__(64 * HW) void decode_split_f8(DecodeParams p) {
     }
     wait_vmcnt<0>();
 
-    const float l_tot = sum_over_groups(l_i);
-    const float inv = l_tot > 0.f ? p.v_scale / l_tot : 0.f;
-    if (row_real) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-            *(float4*)(p.part_o + prow * D + 16 * dt + 4 * g) =
-                make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
-        if (g == 0) p.part_lse[prow] = l_tot > 0.f ? (m_i + __log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
+    for (int qb = 0; qb < QB; ++qb) {
+        const float l_tot = sum_over_groups(l_i[qb]);
+        const float inv = l_tot > 0.f ? p.v_scale / l_tot : 0.f;
+        if (row_real[qb]) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+                *(float4*)(p.part_o + prow[qb] * D + 16 * dt + 4 * g) =
+                    make_float4(o[qb][dt][0] * inv, o[qb][dt][1] * inv, o[qb][dt][2] * inv, o[qb][dt][3] * inv);
+            if (g == 0)
+                p.part_lse[prow[qb]] =
+                    l_tot > 0.f ? (m_i[qb] + __log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
+        }
     }
 }
 
@@ -740,38 +813,52 @@ __global__ __launch_bounds__(64) void decode_combine(CombineParams p) {
     }
 }
 
-template <bool BF16, int D, int HW>
+template <bool BF16, int D, int HW, int QB>
 static void launch_decode_hw(const DecodeParams& p, hipStream_t s) {
     const dim3 grid((unsigned)(p.n_kv_heads / HW), (unsigned)p.max_splits, (unsigned)p.batch), block(64 * HW);
-    if (!p.block_table) hipLaunchKernelGGL((decode_split<BF16, D, kDecodeFlat, HW>), grid, block, 0, s, p);
-    else if (p.page_shift >= 4) hipLaunchKernelGGL((decode_split<BF16, D, kDecodeFast, HW>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((decode_split<BF16, D, kDecodeGeneric, HW>), grid, block, 0, s, p);
+    if (!p.block_table) hipLaunchKernelGGL((decode_split<BF16, D, kDecodeFlat, HW, QB>), grid, block, 0, s, p);
+    else if (p.page_shift >= 4) hipLaunchKernelGGL((decode_split<BF16, D, kDecodeFast, HW, QB>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((decode_split<BF16, D, kDecodeGeneric, HW, QB>), grid, block, 0, s, p);
 }
 
-template <bool BF16, int D, int HW>
+template <bool BF16, int D, int HW, int QB>
 static void launch_decode_f8_hw(const DecodeParams& p, hipStream_t s) {
     const dim3 grid((unsigned)(p.n_kv_heads / HW), (unsigned)p.max_splits, (unsigned)p.batch), block(64 * HW);
-    if (!p.block_table) hipLaunchKernelGGL((decode_split_f8<BF16, D, kDecodeFlat, HW>), grid, block, 0, s, p);
-    else if (p.page_shift >= 4) hipLaunchKernelGGL((decode_split_f8<BF16, D, kDecodeFast, HW>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((decode_split_f8<BF16, D, kDecodeGeneric, HW>), grid, block, 0, s, p);
+    if (!p.block_table) hipLaunchKernelGGL((decode_split_f8<BF16, D, kDecodeFlat, HW, QB>), grid, block, 0, s, p);
+    else if (p.page_shift >= 4) hipLaunchKernelGGL((decode_split_f8<BF16, D, kDecodeFast, HW, QB>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((decode_split_f8<BF16, D, kDecodeGeneric, HW, QB>), grid, block, 0, s, p);
 }
 
 // Waves per workgroup: the largest power of two up to the LDS-bound maximum
 // that divides n_kv_heads (decode_split_f8 holds one V tile per wave, decode_split four).
-template <bool BF16, int D>
-static void launch_decode_d(const DecodeParams& p, hipStream_t s) {
+template <bool BF16, int D, int QB>
+static void launch_decode_q(const DecodeParams& p, hipStream_t s) {
     if (p.kv_fp8) {
         constexpr int MH = dc_max_heads_f8<D>();
-        if (MH >= 8 && p.n_kv_heads % 8 == 0) launch_decode_f8_hw<BF16, D, (MH >= 8 ? 8 : 1)>(p, s);
-        else if (MH >= 4 && p.n_kv_heads % 4 == 0) launch_decode_f8_hw<BF16, D, (MH >= 4 ? 4 : 1)>(p, s);
-        else if (MH >= 2 && p.n_kv_heads % 2 == 0) launch_decode_f8_hw<BF16, D, (MH >= 2 ? 2 : 1)>(p, s);
-        else launch_decode_f8_hw<BF16, D, 1>(p, s);
+        if (MH >= 8 && p.n_kv_heads % 8 == 0) launch_decode_f8_hw<BF16, D, (MH >= 8 ? 8 : 1), QB>(p, s);
+        else if (MH >= 4 && p.n_kv_heads % 4 == 0) launch_decode_f8_hw<BF16, D, (MH >= 4 ? 4 : 1), QB>(p, s);
+        else if (MH >= 2 && p.n_kv_heads % 2 == 0) launch_decode_f8_hw<BF16, D, (MH >= 2 ? 2 : 1), QB>(p, s);
+        else launch_decode_f8_hw<BF16, D, 1, QB>(p, s);
         return;
     }
     constexpr int MH = dc_max_heads<D>();
-    if (MH >= 4 && p.n_kv_heads % 4 == 0) launch_decode_hw<BF16, D, (MH >= 4 ? 4 : 1)>(p, s);
-    else if (MH >= 2 && p.n_kv_heads % 2 == 0) launch_decode_hw<BF16, D, (MH >= 2 ? 2 : 1)>(p, s);
-    else launch_decode_hw<BF16, D, 1>(p, s);
+    if (MH >= 4 && p.n_kv_heads % 4 == 0) launch_decode_hw<BF16, D, (MH >= 4 ? 4 : 1), QB>(p, s);
+    else if (MH >= 2 && p.n_kv_heads % 2 == 0) launch_decode_hw<BF16, D, (MH >= 2 ? 2 : 1), QB>(p, s);
+    else launch_decode_hw<BF16, D, 1, QB>(p, s);
+}
+
+// More than 16 query rows per kv-head (G * s_active) take a second 16-column
+// block of MFMAs over the same K/V fragments (D <= 128; the host rejects more
+// than 16 rows at D = 256, whose registers leave no room for it).
+template <bool BF16, int D>
+static void launch_decode_d(const DecodeParams& p, hipStream_t s) {
+    if constexpr (D <= 128) {
+        if (p.group * p.s_active > 16) {
+            launch_decode_q<BF16, D, 2>(p, s);
+            return;
+        }
+    }
+    launch_decode_q<BF16, D, 1>(p, s);
 }
 
 template <bool BF16>

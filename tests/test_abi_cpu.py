@@ -101,7 +101,8 @@ def decode(**kw):
     (dict(ps=0), INVALID),
     (dict(dtype=A.ATTN_F32), UNSUPPORTED),
     (dict(d=80), UNSUPPORTED),
-    (dict(sa=5), UNSUPPORTED),           # 4 q-heads per kv-head x 5 tokens > 16 rows
+    (dict(sa=9), UNSUPPORTED),           # 4 q-heads per kv-head x 9 tokens > 32 rows
+    (dict(sa=5, d=256), UNSUPPORTED),    # more than 16 rows at head_dim 256
     (dict(hq=30), INVALID),
     (dict(cl=0), INVALID),
     (dict(po=0), INVALID),

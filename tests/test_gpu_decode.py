@@ -29,6 +29,9 @@ def test_decode_parity_small(split_len):
     dict(head_dim=64), dict(head_dim=256), dict(dtype="f16"), dict(n_q_heads=8, n_kv_heads=8),
     dict(n_q_heads=16, n_kv_heads=1), dict(page_size=32), dict(page_size=8), dict(page_size=1, len_hi=300),
     dict(s_active=4, len_lo=4), dict(s_active=2, n_q_heads=16, n_kv_heads=2, len_lo=2),
+    # more than 16 query rows per kv-head: a second 16-column MFMA block
+    dict(s_active=8, len_lo=8), dict(s_active=3, n_q_heads=32, n_kv_heads=4, len_lo=3),
+    dict(s_active=6, head_dim=64, len_lo=6), dict(s_active=5, dtype="f16", len_lo=5, page_size=8),
 ])
 def test_decode_parity_variants(kw):
     inp = small(2, **kw)
@@ -218,3 +221,30 @@ def test_decode_repeated_runs_bit_identical():
     for _ in range(30):
         o = F.decode(t["q"], t["k"], t["v"], t["cache_len"], block_table=t["block_table"], scale=inp.spec.scale_f32)
         assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("window", [3, 200])
+def test_decode_many_rows_window_and_flat(window):
+    """32 rows per kv-head (8 tokens x 4 q-heads) with a window, paged and through a flat copy (bitwise equal)."""
+    torch = torch_cuda()
+    import flash_attention_forward_amd as F
+
+    inp = small(3, s_active=8, len_lo=8)
+    s = inp.spec
+    say("decode 32 rows window", window)
+    maxlen = s.max_pages_per_seq * s.page_size
+    kf = np.zeros((s.batch, maxlen, s.n_kv_heads, s.head_dim), np.uint16)
+    vf = np.zeros_like(kf)
+    for b in range(s.batch):
+        for p in range(s.max_pages_per_seq):
+            kf[b, p * s.page_size:(p + 1) * s.page_size] = inp.k_pool[inp.block_table[b, p]]
+            vf[b, p * s.page_size:(p + 1) * s.page_size] = inp.v_pool[inp.block_table[b, p]]
+    t = decode_tensors(inp)
+    o_paged = F.decode(t["q"], t["k"], t["v"], t["cache_len"], block_table=t["block_table"], scale=s.scale_f32,
+                       window=window, split_len=64)
+    o_flat = F.decode(t["q"], W.to_torch(kf, "bf16", "cuda"), W.to_torch(vf, "bf16", "cuda"), t["cache_len"],
+                      scale=s.scale_f32, window=window, split_len=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o_flat.view(torch.int16), o_paged.view(torch.int16))
+    check(W.as_f64(W.from_torch(o_paged, "bf16"), "bf16"), oracle_decode(inp, window=window), "bf16",
+          f"32 rows window {window}")

@@ -58,6 +58,7 @@ def test_fp8_decode_parity_split_lens(split_len):
     dict(head_dim=64), dict(head_dim=256), dict(dtype="f16"), dict(n_q_heads=8, n_kv_heads=8),
     dict(n_q_heads=16, n_kv_heads=1), dict(page_size=32), dict(page_size=8), dict(page_size=1, len_hi=300),
     dict(s_active=4, len_lo=4), dict(k_scale=0.03125, v_scale=3.0), dict(k_scale=0.37, v_scale=0.011),
+    dict(s_active=8, len_lo=8), dict(s_active=3, n_q_heads=32, n_kv_heads=4, len_lo=3),  # > 16 rows per kv-head
 ])
 def test_fp8_decode_parity_variants(kw):
     inp = small(2, **kw)
