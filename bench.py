@@ -356,6 +356,12 @@ def main():
         return float(np.mean([e[0].elapsed_time(e[1]) for e in evv]))
 
     spec_us = time_decode(dq4, kc, vc, bt, ws4, do4, split_len=spec_split) * 1e3
+    # eight draft tokens: 32 query rows per kv-head (two 16-column MFMA blocks per wave)
+    dq8 = W.to_torch(W.round_to(rng.standard_normal((dspec.batch, 8, dspec.n_q_heads, dspec.head_dim),
+                                                    dtype=np.float32), dspec.dtype), dspec.dtype, dev)
+    ws8 = F.DecodeWorkspace(dspec.batch, 8, dspec.n_q_heads, dspec.head_dim, ms4, dev)
+    spec8_us = time_decode(dq8, kc, vc, bt, ws8, torch.empty_like(dq8), split_len=spec_split) * 1e3
+    del dq8, ws8
     flat_us = time_decode(dq, kflat, vflat, None, ws, torch.empty_like(dq)) * 1e3
     del kflat, vflat
 
@@ -513,6 +519,8 @@ def main():
             "speculative_s_active4_us": round(spec_us, 2),
             "speculative_s_active4_gbps": round(kv_bytes / (spec_us * 1e-6) / 1e9, 1),
             "speculative_split_len": spec_split,
+            "speculative_s_active8_us": round(spec8_us, 2),
+            "speculative_s_active8_gbps": round(kv_bytes / (spec8_us * 1e-6) / 1e9, 1),
             "flat_cache_us": round(flat_us, 2),
             "flat_cache_gbps": round(kv_bytes / (flat_us * 1e-6) / 1e9, 1),
             "fp8_kv_split_us": round(fp8_split_us, 2),
