@@ -198,7 +198,7 @@ int attn_prefill_varlen_fwd(const void* q, attn_strides q_st, const void* k, att
  *   (>= max_pages_per_seq * page_size when paged); a split may span at most
  *   256 pages (split_len / page_size <= 256, else ATTN_ERR_UNSUPPORTED).
  * Requires head_dim in {64, 128, 256}, dtype f16 or bf16, and
- * (n_q_heads / n_kv_heads) * s_active <= 16.
+ * (n_q_heads / n_kv_heads) * s_active <= 32 (<= 16 at head_dim 256).
  */
 int attn_decode_fwd(const void* q, attn_strides q_st,
                     const void* k_cache, const void* v_cache, attn_strides kv_st,
