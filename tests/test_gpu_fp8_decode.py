@@ -97,7 +97,7 @@ def test_fp8_decode_full_size_sampled():
     say("fp8 decode full size: generating the cache")
     inp = W.make_decode(W.FP8_DECODE, W.WORKLOAD_SEEDS["paged_decode_b32_d128"])
     say("fp8 decode full size", int(inp.cache_len.sum()))
-    got = gpu_fp8(inp, bench.DEFAULT_SPLIT_LEN)
+    got = gpu_fp8(inp, bench.FP8_SPLIT_LEN)
     order = np.argsort(inp.cache_len)
     batches = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 3, 17})
     check(got[batches], oracle_fp8(inp, batches=batches), "bf16", "fp8 full size")
