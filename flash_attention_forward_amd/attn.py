@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(HERE, "libattn.so")
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "kernel launch failed"}
 SYMBOLS = ("attn_prefill_fwd", "attn_prefill_fwd_ex", "attn_prefill_varlen_fwd", "attn_decode_fwd", "attn_decode_fwd_fp8kv",
-           "attn_decode_combine", "attn_decode_combine_ex", "attn_decode_workspace_size", "attn_status_string")
+           "attn_decode_combine", "attn_decode_combine_ex", "attn_decode_validate_pages", "attn_decode_workspace_size",
+           "attn_status_string")
 
 
 class AttnError(RuntimeError):
@@ -66,6 +67,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_combine.restype = i32
     L.attn_decode_combine_ex.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, Strides, i32, vp, vp, vp]
     L.attn_decode_combine_ex.restype = i32
+    L.attn_decode_validate_pages.argtypes = [vp, i32, i32, vp, i32, ctypes.c_int64, vp, vp]
+    L.attn_decode_validate_pages.restype = i32
     L.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t),
                                              ctypes.POINTER(ctypes.c_size_t)]
     L.attn_decode_workspace_size.restype = i32
@@ -269,6 +272,26 @@ def attn_decode_combine_ex(part_o, part_lse, cache_len, split_len: int, max_spli
     else:
         rc = L.attn_decode_combine_ex(*args, _ptr(lse), _ptr(sinks), _stream(stream))
     _check(_name, rc)
+
+
+def attn_decode_validate_pages(block_table, cache_len, page_size: int, num_pages: int, result=None,
+                               stream=None):
+    """Device check of a page table ([B, max_pages] 32-bit) against cache_len and the pool's page count.
+    Returns the int32 [2] GPU tensor (problem count, lowest bad flat index or INT32_MAX), written on the stream."""
+    import torch
+
+    for t, n in ((block_table, "block_table"), (cache_len, "cache_len")):
+        _gpu(t, n)
+    if block_table.dtype not in (torch.int32, torch.uint32) or block_table.dim() != 2 or not block_table.is_contiguous():
+        raise TypeError("block_table must be a contiguous 2-D 32-bit tensor")
+    if cache_len.dtype != torch.int32 or cache_len.numel() != block_table.shape[0]:
+        raise TypeError("cache_len must be int32 with one entry per sequence")
+    if result is None:
+        result = torch.empty(2, dtype=torch.int32, device=block_table.device)
+    _check("attn_decode_validate_pages",
+           lib().attn_decode_validate_pages(_ptr(block_table), block_table.shape[1], int(page_size), _ptr(cache_len),
+                                            block_table.shape[0], int(num_pages), _ptr(result), _stream(stream)))
+    return result
 
 
 # ----------------------------------------------------------------------------- conveniences

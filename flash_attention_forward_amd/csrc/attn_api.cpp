@@ -145,6 +145,18 @@ int attn_prefill_fwd(const void* q, attn_strides q_st, const void* k, attn_strid
                                seqlen_kv, head_dim, scale, causal, window, nullptr, nullptr, hip_stream);
 }
 
+int attn_decode_validate_pages(const uint32_t* block_table, int max_pages_per_seq, int page_size,
+                               const int32_t* cache_len, int batch, int64_t num_pages, int32_t* result,
+                               void* hip_stream) {
+    if (batch < 0 || max_pages_per_seq < 0 || page_size <= 0 || num_pages < 0) return ATTN_ERR_INVALID;
+    if (!result || !aligned4(result)) return ATTN_ERR_INVALID;
+    if (batch > 0 && (!block_table || !cache_len || max_pages_per_seq == 0)) return ATTN_ERR_INVALID;
+    if (!aligned4(block_table) || !aligned4(cache_len)) return ATTN_ERR_INVALID;
+    if ((int64_t)batch * max_pages_per_seq >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
+    return status_of(attn::launch_validate_pages(block_table, cache_len, batch, max_pages_per_seq, page_size,
+                                                 num_pages, result, (hipStream_t)hip_stream));
+}
+
 int attn_decode_workspace_size(int batch, int s_active, int n_q_heads, int head_dim, int max_splits,
                                size_t* part_o_bytes, size_t* part_lse_bytes) {
     if (batch < 0 || s_active < 0 || n_q_heads < 0 || head_dim < 0 || max_splits < 0) return ATTN_ERR_INVALID;

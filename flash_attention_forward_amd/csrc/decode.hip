@@ -31,6 +31,8 @@
 // maximum over rounds of splits, rescaling what was summed before) — the CTE page's
 // cross-section merge (section "Algorithm — running-sum update, reciprocal,
 // output accumulate") over any number of splits.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -890,6 +892,54 @@ static hipError_t launch_combine_t(const CombineParams& p, int head_dim, hipStre
 
 hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim, hipStream_t s) {
     return dtype == kBF16 ? launch_combine_t<true>(p, head_dim, s) : launch_combine_t<false>(p, head_dim, s);
+}
+
+// Page-table validation (the device-side range check of the page indices).
+// The decode page's gather faults on an out-of-range page index (section
+// "Paged / block cache"), and the split kernels trust the table, so a caller
+// can check it first. result[0] counts the problems, result[1] is the lowest
+// flat index (b * max_pages_per_seq + page) of a bad entry, or of the first
+// page slot of a sequence whose cache_len is negative or longer than its row
+// of the table. Only the pages below ceil(cache_len / page_size) are checked.
+__global__ __launch_bounds__(64) void validate_pages_init(int32_t* result) {
+    if (threadIdx.x == 0) {
+        result[0] = 0;
+        result[1] = 0x7fffffff;
+    }
+}
+
+__global__ __launch_bounds__(256) void validate_pages(const uint32_t* block_table, const int32_t* cache_len,
+                                                      int max_pages_per_seq, int page_size, int64_t num_pages,
+                                                      int32_t* result) {
+    const int b = blockIdx.y;
+    const int len = cache_len[b];
+    const int64_t row = (int64_t)b * max_pages_per_seq;
+    if (len < 0 || (int64_t)len > (int64_t)max_pages_per_seq * page_size) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            atomicAdd(&result[0], 1);
+            atomicMin(&result[1], (int32_t)row);
+        }
+        return;
+    }
+    const int npages = (len + page_size - 1) / page_size;
+    for (int i = blockIdx.x * 256 + (int)threadIdx.x; i < npages; i += gridDim.x * 256) {
+        if ((int64_t)block_table[row + i] >= num_pages) {
+            atomicAdd(&result[0], 1);
+            atomicMin(&result[1], (int32_t)(row + i));
+        }
+    }
+}
+
+hipError_t launch_validate_pages(const uint32_t* block_table, const int32_t* cache_len, int batch,
+                                 int max_pages_per_seq, int page_size, int64_t num_pages, int32_t* result,
+                                 hipStream_t s) {
+    hipLaunchKernelGGL(validate_pages_init, dim3(1), dim3(64), 0, s, result);
+    if (batch > 0) {
+        const unsigned gx = (unsigned)std::min(64, (max_pages_per_seq + 255) / 256);
+        hipLaunchKernelGGL(validate_pages, dim3(gx, (unsigned)batch), dim3(256), 0, s, block_table, cache_len,
+                           max_pages_per_seq, page_size, num_pages, result);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace attn

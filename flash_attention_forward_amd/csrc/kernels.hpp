@@ -76,5 +76,8 @@ enum DType { kF32 = 0, kF16 = 1, kBF16 = 2 };
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int mask, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim, hipStream_t s);
+hipError_t launch_validate_pages(const uint32_t* block_table, const int32_t* cache_len, int batch,
+                                 int max_pages_per_seq, int page_size, int64_t num_pages, int32_t* result,
+                                 hipStream_t s);
 
 }  // namespace attn

@@ -261,6 +261,24 @@ int attn_decode_combine_ex(const float* part_o, const float* part_lse, const int
                            int head_dim, void* o, attn_strides o_st, attn_dtype dtype,
                            float* lse, const float* sinks, void* hip_stream);
 
+/*
+ * Device-side check of a page table before attn_decode_fwd /
+ * attn_decode_fwd_fp8kv, which trust it: the decode page's gather faults on
+ * an out-of-range page index ("Flash-Attention: Decode (TKG)", section
+ * "Paged / block cache"). For every sequence b it checks that 0 <=
+ * cache_len[b] <= max_pages_per_seq * page_size and that the entries of the
+ * pages below ceil(cache_len[b] / page_size) are < num_pages (the pool's
+ * page count). result: device int32[2], written on the stream: result[0] =
+ * number of problems found, result[1] = the lowest flat index
+ * b * max_pages_per_seq + page of one (the first slot of the row for a bad
+ * cache_len), or INT32_MAX if none. Reads only the table rows' checked
+ * entries and cache_len. Returns ATTN_ERR_INVALID for malformed arguments,
+ * ATTN_ERR_UNSUPPORTED when batch * max_pages_per_seq >= 2^31.
+ */
+int attn_decode_validate_pages(const uint32_t* block_table, int max_pages_per_seq, int page_size,
+                               const int32_t* cache_len, int batch, int64_t num_pages, int32_t* result,
+                               void* hip_stream);
+
 /* Bytes of part_o and part_lse that attn_decode_fwd needs. Returns ATTN_OK or ATTN_ERR_INVALID. */
 int attn_decode_workspace_size(int batch, int s_active, int n_q_heads, int head_dim, int max_splits,
                                size_t* part_o_bytes, size_t* part_lse_bytes);

@@ -244,3 +244,19 @@ def test_auto_split_len_is_accepted_by_the_library_rules(batch, hkv, max_len, ps
     assert A.max_splits_for(max_len, sl) * sl >= max_len
     if (batch, hkv, max_len, ps) == (32, 8, 32768, 16):
         assert sl == 4096  # the paged-decode workload's measured best
+
+
+def validate(**kw):
+    a = dict(bt=FAKE, maxp=2048, ps=16, cl=FAKE, batch=32, num=100000, res=FAKE)
+    a.update(kw)
+    return A.lib().attn_decode_validate_pages(a["bt"], a["maxp"], a["ps"], a["cl"], a["batch"], a["num"], a["res"],
+                                              None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(res=None), INVALID), (dict(res=FAKE + 2), INVALID), (dict(bt=None), INVALID), (dict(cl=None), INVALID),
+    (dict(ps=0), INVALID), (dict(batch=-1), INVALID), (dict(num=-1), INVALID), (dict(maxp=0), INVALID),
+    (dict(bt=FAKE + 2), INVALID), (dict(batch=1 << 20, maxp=1 << 12), UNSUPPORTED),
+])
+def test_validate_pages_rejects_before_any_hip_call(kw, status):
+    assert validate(**kw) == status

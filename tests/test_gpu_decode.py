@@ -248,3 +248,47 @@ def test_decode_many_rows_window_and_flat(window):
     assert torch.equal(o_flat.view(torch.int16), o_paged.view(torch.int16))
     check(W.as_f64(W.from_torch(o_paged, "bf16"), "bf16"), oracle_decode(inp, window=window), "bf16",
           f"32 rows window {window}")
+
+
+def expected_problems(table, cache_len, page_size, num_pages):
+    """Count and lowest flat index of the problems attn_decode_validate_pages reports (plain numpy)."""
+    B, maxp = table.shape
+    bad = []
+    for b in range(B):
+        L = int(cache_len[b])
+        if L < 0 or L > maxp * page_size:
+            bad.append(b * maxp)
+            continue
+        n = -(-L // page_size)
+        bad += [b * maxp + i for i in range(n) if int(table[b, i]) >= num_pages]
+    return len(bad), (min(bad) if bad else 2**31 - 1)
+
+
+def test_validate_pages_accepts_the_workload_and_finds_planted_errors():
+    torch = torch_cuda()
+    import flash_attention_forward_amd as F
+
+    inp = W.make_decode(C5, W.WORKLOAD_SEEDS["paged_decode_b32_d128"])
+    s = inp.spec
+    num_pages = inp.k_pool.shape[0]
+    t = decode_tensors(inp)
+    say("validate pages: workload table")
+    r = F.attn_decode_validate_pages(t["block_table"], t["cache_len"], s.page_size, num_pages).cpu().tolist()
+    assert r == [0, 2**31 - 1]
+    # planted: out-of-range entries inside used pages, others past the used pages (not checked),
+    # and two sequences whose cache_len does not fit their row
+    table = inp.block_table.copy()
+    cl = inp.cache_len.astype(np.int32).copy()
+    rng = np.random.default_rng(5)
+    for b in rng.choice(s.batch, 6, replace=False):
+        used = -(-int(cl[b]) // s.page_size)
+        table[b, rng.integers(0, used)] = num_pages + int(rng.integers(0, 1000))
+        if used < table.shape[1]:
+            table[b, used] = 0xFFFFFFFF  # past the used pages: ignored
+    cl[3] = -5
+    cl[7] = table.shape[1] * s.page_size + 1
+    want = expected_problems(table, cl, s.page_size, num_pages)
+    say("validate pages: planted", want)
+    r = F.attn_decode_validate_pages(torch.from_numpy(table.view(np.int32)).cuda(), torch.from_numpy(cl).cuda(),
+                                     s.page_size, num_pages).cpu().tolist()
+    assert tuple(r) == want and want[0] >= 6
