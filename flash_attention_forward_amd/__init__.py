@@ -15,8 +15,10 @@ from .attn import (  # noqa: F401
     attn_prefill_fwd,
     attn_prefill_fwd_ex,
     attn_prefill_varlen_fwd,
+    auto_split_len,
     decode,
     lib,
+    max_splits_for,
     prefill,
     prefill_varlen,
 )
