@@ -11,7 +11,7 @@ Prints ONE JSON line. `value` is the prefill's effective TFLOP/s (only visible
 the K/V bytes of tokens below cache_len is reported beside it. Kernel times
 come from HIP events recorded on the launch stream around each kernel.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--small-batch-decode]
     python bench.py --calibrate-copy     # plain 1 GiB device copy, for counter scaling
 """
 from __future__ import annotations
@@ -121,6 +121,53 @@ def practical_hbm_gbps(stream, ev) -> float:
     return 2.0 * n / (ms * 1e-3) / 1e9
 
 
+def small_batch_decode(ev, batch: int, context: int, steps: int = 50) -> dict:
+    """Decode steps of `batch` sequences of `context` tokens each (the paged workload's heads
+    and pages) with the split length decode() picks. The steps are recorded into one graph,
+    so the events time the GPU and not the host's launch cost."""
+    import torch
+
+    import flash_attention_forward_amd as F
+    from flash_attention_forward_amd import workloads as W
+
+    spec = W.shrink(W.WORKLOADS[DECODE], batch=batch, len_lo=context, len_hi=context)
+    inp = W.make_decode(spec, W.WORKLOAD_SEEDS[DECODE])
+    s = inp.spec
+    q = W.to_torch(inp.q, s.dtype, "cuda")
+    k, v = W.to_torch(inp.k_pool, s.dtype, "cuda"), W.to_torch(inp.v_pool, s.dtype, "cuda")
+    cl = torch.from_numpy(inp.cache_len.astype(np.int32)).cuda()
+    bt = torch.from_numpy(inp.block_table.view(np.int32)).cuda()
+    max_len = s.max_pages_per_seq * s.page_size
+    sl = F.auto_split_len(batch, s.n_kv_heads, max_len, s.page_size)
+    ws = F.DecodeWorkspace(batch, s.s_active, s.n_q_heads, s.head_dim, F.max_splits_for(max_len, sl), "cuda")
+    out = torch.empty_like(q)
+
+    def step():
+        F.decode(q, k, v, cl, block_table=bt, scale=s.scale_f32, split_len=sl, max_len=max_len, workspace=ws, out=out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            step()
+    g.replay()
+    torch.cuda.synchronize()
+    e = [ev(), ev()]
+    e[0].record()
+    g.replay()
+    g.replay()
+    e[1].record()
+    torch.cuda.synchronize()
+    us = e[0].elapsed_time(e[1]) * 1e3 / (2 * steps)
+    kv = decode_kv_bytes(inp)
+    return {"us": round(us, 2), "gbps": round(kv / (us * 1e-6) / 1e9, 1), "split_len": sl}
+
+
 def calibrate_copy():
     import torch
 
@@ -184,6 +231,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--split-len", type=int, default=DEFAULT_SPLIT_LEN)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--small-batch-decode", action="store_true",
+                    help="also time decode steps of 1 and 4 sequences (graph-recorded)")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
 
@@ -387,6 +436,10 @@ def main():
     fp8_us = float(np.mean([e[0].elapsed_time(e[2]) for e in fev])) * 1e3
     del kc8, vc8, wsf
 
+    # opt-in: these launches share the paged decode's kernel and would dilute its profiled average
+    small = ({f"batch{b}_context{c // 1024}k": small_batch_decode(ev, b, c) for b, c in ((1, 4096), (4, 4096), (1, 32768))}
+             if args.small_batch_decode else None)
+
     # the same prefill and decode with an attention sink per q-head and the
     # per-row log-sum-exp written out (attn_prefill_fwd_ex, attn_decode_combine_ex)
     psinks = torch.linspace(-1.0, 2.0, pspec.n_q_heads, device=dev)
@@ -535,6 +588,9 @@ def main():
             "note": "split + combine over the same caches: 4 query tokens per sequence, a flat cache copy, and the "
                     "cache stored as FP8 E4M3 (half the bytes)",
         },
+        "decode_small_batch": None if small is None else dict(
+            small, note="split + combine with decode()'s split length, GPU time per step of 50 steps recorded in "
+                        "one graph"),
         "kernel_source_digest": kernel_source_digest(),
     }
     if not args.no_cpu_baseline:

@@ -354,14 +354,17 @@ def max_splits_for(max_len: int, split_len: int) -> int:
     return max(1, -(-max_len // split_len))
 
 
-def auto_split_len(batch: int, n_kv_heads: int, max_len: int, page_size: int = 0, min_waves: int = 2048,
+def auto_split_len(batch: int, n_kv_heads: int, max_len: int, page_size: int = 0, min_waves: int = 1024,
                    max_split: int = 4096) -> int:
     """The longest split (fewest partials to write and merge) that still gives the split kernel
-    about min_waves waves (one per kv-head, split and sequence): 4096 for 32 sequences of up to 32K
-    tokens with 8 kv-heads, where it measured best, and shorter splits for fewer or shorter caches.
-    With pages (page_size > 0) it is a multiple of 16 and of the page size and spans at most 256 pages."""
-    sl = 512
-    for cand in (c for c in (4096, 2048, 1024, 512) if c <= max_split):
+    about min_waves waves (one per kv-head, split and sequence), down to 64 tokens. Measured on
+    32 query heads over 8 kv-heads: 4096 for 32 sequences of up to 32K tokens, 1024 for 16 of 8K,
+    512 for 8 of 8K, 256 for one of 32K, 128 for 4 of 4K and 64 for one of 4K (11 us there,
+    against 28 us at 512-token splits). With pages (page_size > 0) it is a multiple of 16 and of
+    the page size and spans at most 256 pages."""
+    cands = [c for c in (4096, 2048, 1024, 512, 256, 128, 64) if c <= max_split] or [64]
+    sl = cands[-1]
+    for cand in cands:
         if batch * n_kv_heads * max_splits_for(max_len, cand) >= min_waves:
             sl = cand
             break

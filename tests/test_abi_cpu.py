@@ -246,6 +246,18 @@ def test_auto_split_len_is_accepted_by_the_library_rules(batch, hkv, max_len, ps
         assert sl == 4096  # the paged-decode workload's measured best
 
 
+@pytest.mark.parametrize("batch,max_len,best", [(32, 32768, 4096), (16, 8192, 1024), (8, 8192, 512), (4, 16384, 512),
+                                                (1, 32768, 256), (4, 4096, 128), (1, 4096, 64)])
+def test_auto_split_len_picks_the_measured_best(batch, max_len, best):
+    """32 q-heads over 8 kv-heads, page size 16: the split lengths that timed fastest for each shape."""
+    assert A.auto_split_len(batch, 8, max_len, 16) == best
+
+
+def test_auto_split_len_respects_max_split():
+    assert A.auto_split_len(32, 8, 32768, 16, max_split=1024) == 1024
+    assert A.auto_split_len(1, 8, 4096, 16, max_split=32) == 64
+
+
 def validate(**kw):
     a = dict(bt=FAKE, maxp=2048, ps=16, cl=FAKE, batch=32, num=100000, res=FAKE)
     a.update(kw)
