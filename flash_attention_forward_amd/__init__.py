@@ -14,6 +14,7 @@ from .attn import (  # noqa: F401
     attn_decode_validate_pages,
     attn_prefill_fwd,
     attn_prefill_fwd_ex,
+    attn_prefill_fwd_fp8kv,
     attn_prefill_varlen_fwd,
     auto_split_len,
     decode,

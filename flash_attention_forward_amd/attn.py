@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libattn.so")
 
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "kernel launch failed"}
-SYMBOLS = ("attn_prefill_fwd", "attn_prefill_fwd_ex", "attn_prefill_varlen_fwd", "attn_decode_fwd", "attn_decode_fwd_fp8kv",
+SYMBOLS = ("attn_prefill_fwd", "attn_prefill_fwd_ex", "attn_prefill_fwd_fp8kv", "attn_prefill_varlen_fwd", "attn_decode_fwd", "attn_decode_fwd_fp8kv",
            "attn_decode_combine", "attn_decode_combine_ex", "attn_decode_validate_pages", "attn_decode_workspace_size",
            "attn_status_string")
 
@@ -54,6 +54,9 @@ def lib() -> ctypes.CDLL:
     L.attn_prefill_fwd_ex.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, i32, i32, i32, i32, i32,
                                       i32, i32, f32, i32, i32, vp, vp, vp]
     L.attn_prefill_fwd_ex.restype = i32
+    L.attn_prefill_fwd_fp8kv.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, i32, i32, i32, i32, i32,
+                                         i32, i32, f32, f32, f32, i32, i32, vp, vp, vp]
+    L.attn_prefill_fwd_fp8kv.restype = i32
     L.attn_prefill_varlen_fwd.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, i32, i32, i32, i32, vp,
                                           vp, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp]
     L.attn_prefill_varlen_fwd.restype = i32
@@ -156,6 +159,32 @@ def attn_prefill_fwd_ex(q, k, v, o, scale: float, causal: bool, window: int = 0,
     else:
         rc = L.attn_prefill_fwd_ex(*args, _ptr(lse), _ptr(sinks), _stream(stream))
     _check(_name, rc)
+
+
+def attn_prefill_fwd_fp8kv(q, k, v, o, scale: float, causal: bool, window: int = 0, k_scale: float = 1.0,
+                           v_scale: float = 1.0, lse=None, sinks=None, stream=None) -> None:
+    """attn_prefill_fwd_ex with K and V as FP8 E4M3 codes (torch.float8_e4m3fn or uint8, [B, Skv, Hkv, D]);
+    a code stands for k_scale (v_scale) times its value. q and o are f16 or bf16."""
+    import torch
+
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _gpu(t, n)
+    B, Sq, Hq, D = q.shape
+    Bk, Skv, Hkv, Dk = k.shape
+    if v.shape != k.shape or o.shape != q.shape or Bk != B or Dk != D:
+        raise ValueError("shape mismatch between q, k, v, o")
+    if k.dtype not in (torch.float8_e4m3fn, torch.uint8) or v.dtype != k.dtype:
+        raise TypeError("k and v must be float8_e4m3fn (or uint8 codes)")
+    if o.dtype != q.dtype:
+        raise TypeError("q and o must share one dtype")
+    dt = _dtype_code(q)
+    lse = _f32_vec(lse, "lse", B * Sq * Hq)
+    sinks = _f32_vec(sinks, "sinks", Hq)
+    rc = lib().attn_prefill_fwd_fp8kv(_ptr(q), _strides4(q, "q"), _ptr(k), _strides4(k, "k"), _ptr(v),
+                                      _strides4(v, "v"), _ptr(o), _strides4(o, "o"), dt, B, Hq, Hkv, Sq, Skv, D,
+                                      float(scale), float(k_scale), float(v_scale), int(bool(causal)), int(window),
+                                      _ptr(lse), _ptr(sinks), _stream(stream))
+    _check("attn_prefill_fwd_fp8kv", rc)
 
 
 def _strides3(t, name: str) -> Strides:
@@ -300,12 +329,17 @@ def default_scale(head_dim: int) -> float:
 
 
 def prefill(q, k, v, scale: float | None = None, causal: bool = False, window: int = 0, out=None, stream=None,
-            sinks=None, return_lse: bool = False):
-    """Output (and, with return_lse, the float32 [B, Sq, Hq] log-sum-exp); sinks: float32 [Hq] or None."""
+            sinks=None, return_lse: bool = False, k_scale: float = 1.0, v_scale: float = 1.0):
+    """Output (and, with return_lse, the float32 [B, Sq, Hq] log-sum-exp); sinks: float32 [Hq] or None.
+    K and V may be FP8 E4M3 (float8_e4m3fn or uint8 codes, scaled by k_scale and v_scale)."""
     import torch
 
     o = torch.empty_like(q) if out is None else out
     sc = default_scale(q.shape[-1]) if scale is None else scale
+    if k.dtype in (torch.float8_e4m3fn, torch.uint8):
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+        attn_prefill_fwd_fp8kv(q, k, v, o, sc, causal, window, k_scale, v_scale, lse, sinks, stream)
+        return (o, lse) if return_lse else o
     if sinks is None and not return_lse:
         attn_prefill_fwd(q, k, v, o, sc, causal, window, stream)
         return o

@@ -72,7 +72,7 @@ int prefill_impl(const void* q, attn_strides q_st, const void* k, attn_strides k
                  attn_strides v_st, void* o, attn_strides o_st, attn_dtype dtype, int batch, int n_q_heads,
                  int n_kv_heads, int seqlen_q, int seqlen_kv, int head_dim, float scale, int causal, int window,
                  float* lse, const float* sinks, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
-                 const int32_t* positions, void* hip_stream) {
+                 const int32_t* positions, void* hip_stream, int kv_bytes = 0, float v_scale = 1.f) {
     if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
     if (batch < 0 || n_q_heads < 0 || n_kv_heads < 0 || seqlen_q < 0 || seqlen_kv < 0 || head_dim <= 0)
         return ATTN_ERR_INVALID;
@@ -82,9 +82,12 @@ int prefill_impl(const void* q, attn_strides q_st, const void* k, attn_strides k
     if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
     if (window > 0 && !causal) return ATTN_ERR_UNSUPPORTED;
     const int eb = elem_bytes(dtype);
+    const bool fp8 = kv_bytes == 1;  // K and V hold FP8 E4M3 codes (strides in bytes)
+    if (fp8 && dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+    const int kvb = fp8 ? 1 : eb;
     if (!q || !o || !aligned16(q) || !aligned16(o)) return ATTN_ERR_INVALID;
     if (seqlen_kv > 0 && (!k || !v || !aligned16(k) || !aligned16(v))) return ATTN_ERR_INVALID;
-    if (!strides_ok(q_st, eb) || !strides_ok(k_st, eb) || !strides_ok(v_st, eb) || !strides_ok(o_st, eb))
+    if (!strides_ok(q_st, eb) || !strides_ok(k_st, kvb) || !strides_ok(v_st, kvb) || !strides_ok(o_st, eb))
         return ATTN_ERR_INVALID;
     if (!aligned4(lse) || !aligned4(sinks)) return ATTN_ERR_INVALID;
     if ((cu_seqlens_q == nullptr) != (cu_seqlens_kv == nullptr)) return ATTN_ERR_INVALID;
@@ -110,7 +113,9 @@ int prefill_impl(const void* q, attn_strides q_st, const void* k, attn_strides k
     p.cu_seqlens_kv = cu_seqlens_kv;
     p.positions = positions;
     p.xcd_chunks = ((int64_t)batch * n_kv_heads) % 8 == 0;
+    p.v_scale = v_scale;
     const int mask = !causal ? attn::kMaskNone : (p.window > 0 ? attn::kMaskCausalWindow : attn::kMaskCausal);
+    if (fp8) return status_of(attn::launch_prefill_f8kv(p, (int)dtype, head_dim, mask, (hipStream_t)hip_stream));
     return status_of(attn::launch_prefill(p, (int)dtype, head_dim, mask, (hipStream_t)hip_stream));
 }
 }  // namespace
@@ -123,6 +128,17 @@ int attn_prefill_fwd_ex(const void* q, attn_strides q_st, const void* k, attn_st
                         int window, float* lse, const float* sinks, void* hip_stream) {
     return prefill_impl(q, q_st, k, k_st, v, v_st, o, o_st, dtype, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_kv,
                         head_dim, scale, causal, window, lse, sinks, nullptr, nullptr, nullptr, hip_stream);
+}
+
+int attn_prefill_fwd_fp8kv(const void* q, attn_strides q_st, const uint8_t* k, attn_strides k_st, const uint8_t* v,
+                           attn_strides v_st, void* o, attn_strides o_st, attn_dtype dtype, int batch, int n_q_heads,
+                           int n_kv_heads, int seqlen_q, int seqlen_kv, int head_dim, float scale, float k_scale,
+                           float v_scale, int causal, int window, float* lse, const float* sinks, void* hip_stream) {
+    if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !std::isfinite(scale * k_scale))
+        return ATTN_ERR_INVALID;
+    return prefill_impl(q, q_st, k, k_st, v, v_st, o, o_st, dtype, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_kv,
+                        head_dim, scale * k_scale, causal, window, lse, sinks, nullptr, nullptr, nullptr, hip_stream,
+                        1, v_scale);
 }
 
 int attn_prefill_varlen_fwd(const void* q, attn_strides q_st, const void* k, attn_strides k_st, const void* v,

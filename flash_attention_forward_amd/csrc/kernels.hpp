@@ -34,6 +34,7 @@ struct PrefillParams {
     // and j >= P - window + 1. Nondecreasing within a sequence.
     const int32_t* positions;
     int xcd_chunks;   // deal workgroups to XCDs in kv-head groups (batch * n_kv_heads % 8 == 0)
+    float v_scale;    // FP8 K/V (prefill_f8kv): V row = v_scale * its codes (K's scale is folded into c)
 };
 
 struct DecodeParams {
@@ -74,6 +75,8 @@ enum DType { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
 // Each returns the hipError_t of its launch (hipSuccess on success).
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int mask, hipStream_t s);
+// K and V as FP8 E4M3 codes (k/v strides in bytes); dtype (f16/bf16) is Q's and O's.
+hipError_t launch_prefill_f8kv(const PrefillParams& p, int dtype, int head_dim, int mask, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_validate_pages(const uint32_t* block_table, const int32_t* cache_len, int batch,

@@ -551,6 +551,261 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     }
 }
 
+// ---------------------------------------------------------------------------- FP8 K/V
+// prefill_f8kv: prefill for K and V stored as FP8 E4M3 codes with one scale
+// per tensor (a code stands for scale times its value; the host folds K's
+// scale into c and V's scale multiplies the output). The FP8 variant of the
+// decode page's quantised cache, applied to the prefill's K/V stream. Each
+// 64-key tile is read into registers (16 codes per load), widened exactly to
+// the 16-bit type (gfx950's v_cvt_scalef32_pk_*_fp8 with scale 1) and written
+// to LDS in prefill_mfma's swizzled tile layout, so the fragment reads, the
+// masks, the online softmax with its lazy rescale and the epilogue are
+// prefill_mfma's. Two LDS buffers per tensor: tile j+1 is requested before
+// the MFMAs of tile j and written after them, with one barrier per tile.
+// Four waves of 32 query rows; no software pipelining across tiles.
+template <bool BF16, int D, int MASK>
+__global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void prefill_f8kv(PrefillParams p) {
+    constexpr int NW = 4;
+    constexpr int PF_BM = PF_ROWS_PER_WAVE * NW;
+    constexpr int TILE = PF_BN * D;
+    constexpr int NDT = D / 32;
+    constexpr int CH8 = D / 16;             // 16-byte chunks of codes per row
+    constexpr int NLD = PF_BN * CH8 / 256;  // chunks per thread per tile and tensor
+    static_assert(NLD >= 1, "every thread loads part of each tile");
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][TILE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hf = lane >> 5;
+    const int g = lane >> 4;
+    const int r16 = lane & 15;
+
+    // Workgroup -> (q tile, batch, q-head), heaviest causal tiles first.
+    const int nbh = p.batch * p.n_q_heads;
+    const int wid = (int)blockIdx.x;
+    const int qt = p.n_q_tiles - 1 - wid / nbh;
+    const int bh = wid % nbh;
+    const int b = bh / p.n_q_heads;
+    const int h = bh % p.n_q_heads;
+    const int hk = h / p.group;
+    const int sq = p.seqlen_q, skv = p.seqlen_kv;
+    const int off = skv - sq;  // query row i sits at position i + off
+    const int q0 = qt * PF_BM;
+    const int qlast = min(q0 + PF_BM, sq) - 1;
+    int kv_lo = 0, kv_hi = skv;
+    if (MASK >= kMaskCausal) kv_hi = min(kv_hi, qlast + off + 1);
+    if (MASK == kMaskCausalWindow) kv_lo = max(0, q0 + off - p.window + 1);
+    const int j_begin = kv_lo / PF_BN;
+    const int j_end = kv_hi > kv_lo ? (kv_hi + PF_BN - 1) / PF_BN : j_begin;
+
+    const int wq0 = q0 + 32 * w;
+    const int wq1 = min(wq0 + 31, sq - 1);
+    const bool wave_live = wq0 < sq;
+    const int my_q = wq0 + l32;
+    const int my_pos = my_q + off;
+    const int wpos0 = wq0 + off, wpos1 = wq1 + off;
+
+    // Q fragments: B operand of S^T = K Q^T (lane: row l32, d = 16s + 8hf .. +8).
+    s16x8 qf[D / 16];
+    {
+        const uint16_t* qrow = (const uint16_t*)p.q + (int64_t)b * p.qs.batch + (int64_t)my_q * p.qs.seq +
+                               (int64_t)h * p.qs.head + 8 * hf;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            uint4 x = make_uint4(0, 0, 0, 0);
+            if (my_q < sq) x = *(const uint4*)(qrow + 16 * s);
+            x.x ^= p.qflip; x.y ^= p.qflip; x.z ^= p.qflip; x.w ^= p.qflip;
+            qf[s] = __builtin_bit_cast(s16x8, x);
+        }
+    }
+
+    // Tile staging. Thread chunk c = tid + 256 i covers codes 16 (c % CH8) ..
+    // +16 of tile row c / CH8; rows outside [kv_lo, skv) read the nearest valid
+    // row (masked later), so every load stays inside the visible key range.
+    const uint8_t* kb8 = (const uint8_t*)p.k + (int64_t)b * p.ks.batch + (int64_t)hk * p.ks.head;
+    const uint8_t* vb8 = (const uint8_t*)p.v + (int64_t)b * p.vs.batch + (int64_t)hk * p.vs.head;
+    const int key_min = kv_lo, key_max = skv - 1;
+    uint4 kr[NLD], vr[NLD];
+    auto fetch = [&](int j) __attribute__((always_inline)) {
+        const int kv0 = j * PF_BN;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int c = tid + 256 * i;
+            const int key = min(max(kv0 + c / CH8, key_min), key_max);
+            const int col = 16 * (c % CH8);
+            kr[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(kb8 + (int64_t)key * p.ks.seq + col)));
+            vr[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(vb8 + (int64_t)key * p.vs.seq + col)));
+        }
+    };
+    // 16 codes -> two 16-byte chunks of 16-bit floats (codes 0..7, 8..15)
+    auto widen = [](uint4 x, uint4& lo, uint4& hi) __attribute__((always_inline)) {
+        uint32_t wv[8];
+        const uint32_t src[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (BF16) {
+                wv[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[e], 1.0f, false));
+                wv[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[e], 1.0f, true));
+            } else {
+                wv[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src[e], 1.0f, false));
+                wv[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src[e], 1.0f, true));
+            }
+        }
+        lo = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        hi = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+    };
+    auto store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int c = tid + 256 * i;
+            const int row = c / CH8, cc = c % CH8;
+            uint4 lo, hi;
+            char* krow = (char*)Ks[buf] + row * D * 2;
+            widen(kr[i], lo, hi);
+            *(uint4*)(krow + 16 * ((2 * cc) ^ pf_kswz<D>(row))) = lo;
+            *(uint4*)(krow + 16 * ((2 * cc + 1) ^ pf_kswz<D>(row))) = hi;
+            char* vrow = (char*)Vs[buf] + row * D * 2;
+            widen(vr[i], lo, hi);
+            *(uint4*)(vrow + 16 * ((2 * cc) ^ pf_vswz<D>(row))) = lo;
+            *(uint4*)(vrow + 16 * ((2 * cc + 1) ^ pf_vswz<D>(row))) = hi;
+        }
+    };
+
+    // Fragment offsets and per-tile steps as in prefill_mfma.
+    const uint32_t kfrag = (uint32_t)(l32 * D * 2) | (16u * (uint32_t)(hf ^ pf_kswz<D>(l32)));
+    const int vr0 = 4 * hf + (r16 >> 2);
+    const int vcl = 2 * (g & 1) + ((r16 & 3) >> 1);
+    const uint32_t vfrag = (uint32_t)(vr0 * D * 2) | (16u * (uint32_t)(vcl ^ pf_vswz<D>(vr0))) | (8u * (r16 & 1));
+    const uint32_t one2 = BF16 ? 0x3F803F80u : 0x3C003C00u;
+    int key_hi = skv - 1, key_lo = 0;
+    if (MASK >= kMaskCausal) key_hi = min(key_hi, my_pos);
+    if (MASK == kMaskCausalWindow) key_lo = max(key_lo, my_pos - p.window + 1);
+    const bool none_visible = key_hi < key_lo;
+    const uint32_t key_span = none_visible ? 0u : (uint32_t)(key_hi - key_lo);
+    if (none_visible) key_lo = INT_MIN / 2;
+    auto mask_half = [&](f32x16& sacc, int kv0, int t) __attribute__((always_inline)) {
+        const int base = kv0 + 32 * t + 4 * hf - key_lo;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint32_t d = (uint32_t)(base + 8 * (r >> 2) + (r & 3));
+            sacc[r] = d <= key_span ? sacc[r] : kMaskedScore;
+        }
+    };
+    auto tile_full = [&](int j) __attribute__((always_inline)) {
+        const int kv0 = j * PF_BN;
+        bool f = kv0 + PF_BN <= skv;
+        if (MASK >= kMaskCausal) f &= kv0 + PF_BN - 1 <= wpos0;
+        if (MASK == kMaskCausalWindow) f &= kv0 >= wpos1 - p.window + 1;
+        return f;
+    };
+
+    constexpr float kLazyRescale = 8.0f;
+    float m_i = kMaxInit, l_i = 0.f;
+    f32x16 o[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
+
+    auto tile = [&](int j, int buf) __attribute__((always_inline)) {
+        const uint16_t* Kt = Ks[buf];
+        f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            const uint32_t koff = kfrag ^ (32u * s);
+            const s16x8 a0 = *(const s16x8*)((const char*)Kt + koff);
+            const s16x8 a1 = *(const s16x8*)((const char*)(Kt + 32 * D) + koff);
+            s0 = mfma32x32x16<BF16>(a0, qf[s], s0);
+            s1 = mfma32x32x16<BF16>(a1, qf[s], s1);
+        }
+        if (!(wave_live && tile_full(j))) {
+            mask_half(s0, j * PF_BN, 0);
+            mask_half(s1, j * PF_BN, 1);
+        }
+        float mx = kMaskedScore;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = max3f(mx, s0[r], s1[r]);
+        mx = max_with_other_half(mx);
+        // move m (rescaling O and l) only for rows whose tile max passed m + margin
+        const float m_cand = mx * p.c;
+        const bool grow = m_cand > m_i + kLazyRescale;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float m_new = grow ? m_cand : m_i;
+            const float alpha = fast_exp2(m_i - m_new);
+            m_i = m_new;
+            l_i *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        }
+        const float neg_m = -m_i;
+        uint32_t pk[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const f32x16& sc = i < 8 ? s0 : s1;
+            const int r = 2 * (i % 8);
+            pk[i] = pack2_16<BF16>(fast_exp2(fmaf(sc[r], p.c, neg_m)), fast_exp2(fmaf(sc[r + 1], p.c, neg_m)));
+        }
+        float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+            ps0 = dot2_16<BF16>(pk[e], one2, ps0);
+            ps1 = dot2_16<BF16>(pk[e + 1], one2, ps1);
+        }
+        l_i += ps0 + ps1;
+        const char* Vt = (const char*)Vs[buf];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const s16x8 pb = __builtin_bit_cast(s16x8, make_uint4(pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]));
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const char* vb0 = Vt + (vfrag ^ (64u * dt));
+                const s16x8 vb = concat4(lds_read_tr16((const uint16_t*)(vb0 + 2 * D * (16 * u))),
+                                         lds_read_tr16((const uint16_t*)(vb0 + 2 * D * (16 * u + 8))));
+                o[dt] = mfma32x32x16<BF16>(vb, pb, o[dt]);
+            }
+        }
+    };
+
+    if (j_end > j_begin) {
+        fetch(j_begin);
+        store(0);
+        __syncthreads();
+        for (int j = j_begin; j < j_end; ++j) {
+            const int buf = (j - j_begin) & 1;
+            const bool more = j + 1 < j_end;
+            if (more) fetch(j + 1);
+            tile(j, buf);
+            // the other buffer was last read in step j - 1, before the barrier that ended it
+            if (more) store(buf ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // Epilogue: O * (v_scale / l), with the sink folded in first; rows that saw
+    // no key are written as zeros. The log-sum-exp (natural log) goes to lse.
+    float l_tot = sum_with_other_half(l_i);
+    float m_fin = m_i;
+    const float osc = p.sinks ? fold_sink(p.sinks[h] * kLog2e, m_fin, l_tot) : 1.f;
+    const float inv = l_tot > 0.f ? osc * p.v_scale / l_tot : 0.f;
+    if (p.lse && hf == 0 && wave_live && my_q < sq)
+        p.lse[((int64_t)b * p.seqlen_q + my_q) * p.n_q_heads + h] =
+            l_tot > 0.f ? (m_fin + __log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
+    if (wave_live && my_q < sq) {
+        uint16_t* orow = (uint16_t*)p.o + (int64_t)b * p.os.batch + (int64_t)my_q * p.os.seq + (int64_t)h * p.os.head;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int d = 32 * dt + 8 * rq + 4 * hf;
+                uint2 pk;
+                pk.x = pack2_16<BF16>(o[dt][4 * rq + 0] * inv, o[dt][4 * rq + 1] * inv);
+                pk.y = pack2_16<BF16>(o[dt][4 * rq + 2] * inv, o[dt][4 * rq + 3] * inv);
+                *(uint2*)(orow + d) = pk;
+            }
+    }
+}
+
 // ---------------------------------------------------------------------------- f32
 constexpr int F32_BM = 64;
 constexpr int F32_BN = 32;
@@ -718,6 +973,31 @@ static hipError_t launch_f32_mask(PrefillParams p, int mask, hipStream_t s) {
         default: hipLaunchKernelGGL((prefill_f32<D, kMaskCausalWindow>), grid, dim3(256), 0, s, p); break;
     }
     return hipGetLastError();
+}
+
+template <bool BF16, int D>
+static hipError_t launch_f8kv_mask(PrefillParams p, int mask, hipStream_t s) {
+    p.n_q_tiles = (p.seqlen_q + 4 * PF_ROWS_PER_WAVE - 1) / (4 * PF_ROWS_PER_WAVE);
+    const dim3 grid((unsigned)p.n_q_tiles * p.batch * p.n_q_heads), block(256);
+    switch (mask) {
+        case kMaskNone: hipLaunchKernelGGL((prefill_f8kv<BF16, D, kMaskNone>), grid, block, 0, s, p); break;
+        case kMaskCausal: hipLaunchKernelGGL((prefill_f8kv<BF16, D, kMaskCausal>), grid, block, 0, s, p); break;
+        default: hipLaunchKernelGGL((prefill_f8kv<BF16, D, kMaskCausalWindow>), grid, block, 0, s, p); break;
+    }
+    return hipGetLastError();
+}
+
+template <bool BF16>
+static hipError_t launch_f8kv_d(const PrefillParams& p, int head_dim, int mask, hipStream_t s) {
+    switch (head_dim) {
+        case 64: return launch_f8kv_mask<BF16, 64>(p, mask, s);
+        case 128: return launch_f8kv_mask<BF16, 128>(p, mask, s);
+        default: return launch_f8kv_mask<BF16, 256>(p, mask, s);
+    }
+}
+
+hipError_t launch_prefill_f8kv(const PrefillParams& p, int dtype, int head_dim, int mask, hipStream_t s) {
+    return dtype == kBF16 ? launch_f8kv_d<true>(p, head_dim, mask, s) : launch_f8kv_d<false>(p, head_dim, mask, s);
 }
 
 template <bool BF16>

@@ -393,3 +393,8 @@ VARLEN_SEED = 1006
 def shrink(spec, **kw):
     """Same workload structure at other sizes (for tests)."""
     return replace(spec, **kw)
+
+# Per-tensor scales (K, V) when the 32K causal workload's K and V are stored as FP8 E4M3: each
+# value is divided by its scale and rounded, so E4M3's largest code (448) stands for 14 (K, whose
+# spiked rows reach about 11) and 7 (V, N(0,1) draws).
+FP8_PREFILL_SCALES = (1.0 / 32.0, 1.0 / 64.0)

@@ -124,6 +124,28 @@ int attn_prefill_fwd_ex(const void* q, attn_strides q_st, const void* k, attn_st
                         float* lse, const float* sinks, void* hip_stream);
 
 /*
+ * attn_prefill_fwd_ex with K and V stored in FP8 E4M3 (the OCP "e4m3fn"
+ * encoding, as for attn_decode_fwd_fp8kv): the decode page's FP8-e4m3 cache
+ * ("Flash-Attention: Decode (TKG)", section "KV-cache layouts and access")
+ * read by the prefill, e.g. a chunk of new tokens attending to a cached FP8
+ * prefix. k and v hold one byte per element in the [batch, seqlen_kv,
+ * n_kv_heads, head_dim] layout with strides in elements (bytes); each row
+ * must start 16-byte aligned. A stored code x stands for k_scale * value(x)
+ * (K) or v_scale * value(x) (V). q and o are `dtype` (f16 or bf16; f32 is
+ * ATTN_ERR_UNSUPPORTED), and shapes, masks, lse and sinks are as for
+ * attn_prefill_fwd_ex. The codes are widened exactly to the 16-bit type of q
+ * before the products, so the only rounding beyond attn_prefill_fwd_ex is the
+ * cache's own. k_scale, v_scale and scale * k_scale must be finite (else
+ * ATTN_ERR_INVALID); NaN codes give NaN rows.
+ */
+int attn_prefill_fwd_fp8kv(const void* q, attn_strides q_st, const uint8_t* k, attn_strides k_st,
+                           const uint8_t* v, attn_strides v_st, void* o, attn_strides o_st,
+                           attn_dtype dtype, int batch, int n_q_heads, int n_kv_heads,
+                           int seqlen_q, int seqlen_kv, int head_dim,
+                           float scale, float k_scale, float v_scale, int causal, int window,
+                           float* lse, const float* sinks, void* hip_stream);
+
+/*
  * Prefill over packed sequences of different lengths (sequence packing):
  * the bounds of every sequence are data, not shapes (the CTE page's dynamic
  * range_select family, section "Algorithm — the dynamic range_select

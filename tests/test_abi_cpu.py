@@ -210,6 +210,35 @@ def test_decode_fp8_accepts_byte_strides():
     assert decode_fp8(batch=0) == 0
 
 
+def prefill_fp8(**kw):
+    a = dict(q=FAKE, qs=st(2048 * 8 * 128, 8 * 128, 128), k=FAKE, ks=st(2048 * 128, 128, 128), v=FAKE,
+             vs=st(2048 * 128, 128, 128), o=FAKE, os=st(2048 * 8 * 128, 8 * 128, 128), dtype=A.ATTN_BF16, batch=1,
+             hq=8, hkv=1, sq=2048, skv=2048, d=128, scale=0.088, kscale=1.0, vscale=1.0, causal=1, window=0,
+             lse=None, sinks=None)
+    a.update(kw)
+    return A.lib().attn_prefill_fwd_fp8kv(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["o"], a["os"],
+                                          a["dtype"], a["batch"], a["hq"], a["hkv"], a["sq"], a["skv"], a["d"],
+                                          a["scale"], a["kscale"], a["vscale"], a["causal"], a["window"], a["lse"],
+                                          a["sinks"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=A.ATTN_F32), UNSUPPORTED), (dict(dtype=7), INVALID), (dict(d=96), UNSUPPORTED),
+    (dict(kscale=float("inf")), INVALID), (dict(vscale=float("nan")), INVALID), (dict(kscale=1e30, scale=1e30), INVALID),
+    (dict(ks=st(2048 * 128, 128, 8)), INVALID),  # 8-byte head stride: rows not 16-byte aligned
+    (dict(k=FAKE + 8), INVALID), (dict(hq=6, hkv=4), INVALID), (dict(window=64, causal=0), UNSUPPORTED),
+    (dict(qs=st(2048 * 8 * 128, 8 * 128 + 1, 128)), INVALID), (dict(lse=FAKE + 2), INVALID),
+])
+def test_prefill_fp8_rejects(kw, status):
+    assert prefill_fp8(**kw) == status
+
+
+def test_prefill_fp8_accepts_byte_strides_and_empty_shapes():
+    # 16-byte-aligned byte strides are fine for one-byte codes; empty shapes enqueue nothing
+    assert prefill_fp8(batch=0, ks=st(2048 * 16, 16, 16), vs=st(2048 * 16, 16, 16)) == 0
+    assert prefill_fp8(sq=0) == 0
+
+
 def prefill_varlen(**kw):
     a = dict(q=FAKE, qs=st(0, 8 * 128, 128), k=FAKE, ks=st(0, 128, 128), v=FAKE, vs=st(0, 128, 128), o=FAKE,
              os=st(0, 8 * 128, 128), dtype=A.ATTN_BF16, batch=4, hq=8, hkv=1, cuq=FAKE, cuk=FAKE, mq=2048, mk=2048,

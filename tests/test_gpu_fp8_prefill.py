@@ -1,0 +1,131 @@
+"""GPU parity of attn_prefill_fwd_fp8kv (K and V as FP8 E4M3 codes with per-tensor scales,
+f16/bf16 queries) against the fp64 oracle applied to scale * value(code), with the
+tolerances of gpu_common; plus a bitwise comparison with attn_prefill_fwd fed the same
+codes widened to the 16-bit type (the widening is exact, and both kernels use 128-row
+tiles at these sizes)."""
+import numpy as np
+import pytest
+
+import oracle
+from flash_attention_forward_amd import workloads as W
+
+from gpu_common import check, dev, host64, say, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = {"bf16": 3e-3, "f16": 5e-4}
+
+# name: (B, Hq, Hkv, Sq, Skv, D, dtype, causal, window, k_scale, v_scale)
+CASES = {
+    "bf16_causal_gqa": (2, 8, 2, 300, 300, 128, "bf16", True, 0, 0.75, 1.25),
+    "f16_nomask_ragged": (1, 4, 4, 200, 333, 64, "f16", False, 0, 1.0, 1.0),
+    "bf16_d256_window": (1, 4, 2, 257, 257, 256, "bf16", True, 100, 0.5, 2.0),
+    "bf16_prefix": (2, 4, 1, 100, 500, 128, "bf16", True, 0, 1.5, 0.625),
+    "bf16_more_queries_than_keys": (1, 2, 1, 300, 100, 128, "bf16", True, 0, 1.0, 1.0),
+    "f16_window_1": (1, 4, 2, 130, 130, 128, "f16", True, 1, 0.9, 1.1),
+    "bf16_d64_window": (2, 6, 3, 190, 190, 64, "bf16", True, 33, 1.0, 0.8),
+}
+
+
+def make(case, seed):
+    B, Hq, Hkv, Sq, Skv, D, dtype, causal, window, ks, vs = case
+    rng = np.random.default_rng(seed)
+    q = W.normal_rounded(rng, (B, Sq, Hq, D), dtype)
+    k = W.normal_rounded(rng, (B, Skv, Hkv, D), "fp8", divide_by=ks)
+    v = W.normal_rounded(rng, (B, Skv, Hkv, D), "fp8", divide_by=vs)
+    return q, k, v
+
+
+def run(case, q, k, v, sinks=None, lse=False):
+    import flash_attention_forward_amd as F
+
+    torch = torch_cuda()
+    B, Hq, Hkv, Sq, Skv, D, dtype, causal, window, ks, vs = case
+    scale = np.float32(1.0 / np.sqrt(D))
+    out = F.prefill(dev(q, dtype), W.to_torch(k, "fp8", "cuda"), W.to_torch(v, "fp8", "cuda"), scale=float(scale),
+                    causal=causal, window=window, k_scale=ks, v_scale=vs, return_lse=lse,
+                    sinks=None if sinks is None else torch.from_numpy(sinks).cuda())
+    torch.cuda.synchronize()
+    o, l = out if lse else (out, None)
+    return host64(o, dtype), (l.cpu().numpy().astype(np.float64) if lse else None)
+
+
+def reference(case, q, k, v, sinks=None):
+    B, Hq, Hkv, Sq, Skv, D, dtype, causal, window, ks, vs = case
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    k64 = np.float64(np.float32(ks)) * W.as_f64(k, "fp8")
+    v64 = np.float64(np.float32(vs)) * W.as_f64(v, "fp8")
+    return oracle.attention(W.as_f64(q, dtype), k64, v64, scale, causal, window, return_lse=True,
+                            sinks=None if sinks is None else sinks.astype(np.float64))
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_fp8_prefill_parity(name):
+    case = CASES[name]
+    q, k, v = make(case, 70 + len(name))
+    say("fp8 prefill", name)
+    got, _ = run(case, q, k, v)
+    ref, _ = reference(case, q, k, v)
+    check(got, ref, case[6], name)
+
+
+@pytest.mark.parametrize("name", ["bf16_causal_gqa", "bf16_d256_window", "bf16_more_queries_than_keys"])
+def test_fp8_prefill_lse_and_sinks(name):
+    case = CASES[name]
+    q, k, v = make(case, 90 + len(name))
+    sinks = np.random.default_rng(4).uniform(-3.0, 4.0, case[1]).astype(np.float32)
+    for sk in (None, sinks):
+        say("fp8 prefill lse/sinks", name, sk is not None)
+        got, lse = run(case, q, k, v, sinks=sk, lse=True)
+        ref, ref_lse = reference(case, q, k, v, sinks=sk)
+        check(got, ref, case[6], name)
+        fin = np.isfinite(ref_lse)
+        assert (np.isneginf(lse) == ~fin).all()
+        assert np.abs(lse[fin] - ref_lse[fin]).max(initial=0.0) <= LSE_TOL[case[6]]
+
+
+@pytest.mark.parametrize("name", ["bf16_causal_gqa", "f16_nomask_ragged", "bf16_d256_window", "bf16_prefix"])
+def test_fp8_prefill_equals_the_16bit_kernel_on_widened_codes(name):
+    """Unit scales: the FP8 kernel and attn_prefill_fwd on the codes widened to the 16-bit type agree bitwise."""
+    import flash_attention_forward_amd as F
+
+    torch = torch_cuda()
+    case = CASES[name][:9] + (1.0, 1.0)
+    q, k, v = make(case, 110 + len(name))
+    dtype = case[6]
+    say("fp8 prefill vs widened", name)
+    got, _ = run(case, q, k, v)
+    kw = W.to_torch(W.round_to(W.as_f32(k, "fp8"), dtype), dtype, "cuda")
+    vw = W.to_torch(W.round_to(W.as_f32(v, "fp8"), dtype), dtype, "cuda")
+    o = F.prefill(dev(q, dtype), kw, vw, scale=float(np.float32(1.0 / np.sqrt(case[5]))), causal=case[7],
+                  window=case[8])
+    torch.cuda.synchronize()
+    assert np.array_equal(got, host64(o, dtype))
+
+
+def test_fp8_prefill_full_size_sampled():
+    """The 32K causal workload (8 q-heads over one kv-head, spiked keys) with K and V stored as FP8
+    (each value divided by its tensor's scale, then rounded to E4M3), on sampled rows, in the launch
+    the benchmark times."""
+    import flash_attention_forward_amd as F
+
+    torch = torch_cuda()
+    name = "bf16_causal_32k"
+    spec = W.WORKLOADS[name]
+    inp = W.make_prefill(spec, W.WORKLOAD_SEEDS[name])
+    ks, vs = W.FP8_PREFILL_SCALES
+    k8 = W.f32_to_e4m3_bits(W.as_f32(inp.k, spec.dtype) / np.float32(ks))
+    v8 = W.f32_to_e4m3_bits(W.as_f32(inp.v, spec.dtype) / np.float32(vs))
+    say("fp8 prefill full size", name)
+    o = F.prefill(dev(inp.q, spec.dtype), W.to_torch(k8, "fp8", "cuda"), W.to_torch(v8, "fp8", "cuda"),
+                  scale=spec.scale_f32, causal=True, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    got = host64(o, spec.dtype)
+    rng = np.random.default_rng(8)
+    S = spec.seqlen_q
+    rows_i = sorted({0, 1, 127, 128, 4095, 16384, S - 1} | set(rng.integers(0, S, 24).tolist()))
+    rows = np.array([(0, i, h) for i in rows_i for h in rng.choice(spec.n_q_heads, 2, replace=False)], dtype=np.int64)
+    k64 = np.float64(np.float32(ks)) * W.as_f64(k8, "fp8")
+    v64 = np.float64(np.float32(vs)) * W.as_f64(v8, "fp8")
+    ref, _ = oracle.attention_rows(W.as_f64(inp.q, spec.dtype), k64, v64, spec.scale_f32, True, 0, rows)
+    check(got[rows[:, 0], rows[:, 1], rows[:, 2]], ref, spec.dtype, "32K with an FP8 cache")
