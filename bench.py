@@ -360,6 +360,21 @@ def main():
     swa_flops = prefill_flops(wspec)
     del wq, wk, wv, wo, win
 
+    # the 32K causal workload with K and V stored as FP8 E4M3 (attn_prefill_fwd_fp8kv): 10 back-to-back launches
+    fks, fvs = W.FP8_PREFILL_SCALES
+    k8 = W.to_torch(W.f32_to_e4m3_bits(W.as_f32(pin.k, pspec.dtype) / np.float32(fks)), "fp8", dev)
+    v8 = W.to_torch(W.f32_to_e4m3_bits(W.as_f32(pin.v, pspec.dtype) / np.float32(fvs)), "fp8", dev)
+    for _ in range(5):
+        F.attn_prefill_fwd_fp8kv(q, k8, v8, o, pspec.scale_f32, True, 0, fks, fvs)
+    f8ev = [ev(), ev()]
+    f8ev[0].record(stream)
+    for _ in range(10):
+        F.attn_prefill_fwd_fp8kv(q, k8, v8, o, pspec.scale_f32, True, 0, fks, fvs)
+    f8ev[1].record(stream)
+    torch.cuda.synchronize()
+    pf8_ms = f8ev[0].elapsed_time(f8ev[1]) / 10
+    del k8, v8
+
     # packed prompts of different lengths (attn_prefill_varlen_fwd): 10 back-to-back launches
     vspec = W.VARLEN_SPEC
     vin = W.make_varlen(vspec, W.VARLEN_SEED)
@@ -551,6 +566,18 @@ def main():
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(swa_flops / (swa_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                          "traffic": traffic_from_profiles("prefill_swa_d256")},
+        },
+        "prefill_fp8kv": {
+            "workload": PREFILL,
+            "ms": round(pf8_ms, 4),
+            "tflops": round(prefill_flops(pspec) / (pf8_ms * 1e-3) / 1e12, 2),
+            "k_scale": fks,
+            "v_scale": fvs,
+            "note": "the 32K causal prefill with K and V stored as FP8 E4M3 (per-tensor scales), q and o bf16",
+            "roofline": {"bound": "mfma", "achieved": round(prefill_flops(pspec) / (pf8_ms * 1e-3) / 1e12, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(prefill_flops(pspec) / (pf8_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "traffic": traffic_from_profiles("prefill_fp8kv_32k")},
         },
         "varlen": {
             "workload": W.VARLEN,

@@ -562,15 +562,16 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
 // masks, the online softmax with its lazy rescale and the epilogue are
 // prefill_mfma's. Two LDS buffers per tensor: tile j+1 is requested before
 // the MFMAs of tile j and written after them, with one barrier per tile.
-// Four waves of 32 query rows; no software pipelining across tiles.
-template <bool BF16, int D, int MASK>
-__global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void prefill_f8kv(PrefillParams p) {
-    constexpr int NW = 4;
+// NW waves of 32 query rows (as prefill_mfma: 8 for D = 128 on wide grids);
+// no software pipelining across tiles.
+template <bool BF16, int D, int MASK, int NW>
+__global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefill_f8kv(PrefillParams p) {
     constexpr int PF_BM = PF_ROWS_PER_WAVE * NW;
     constexpr int TILE = PF_BN * D;
     constexpr int NDT = D / 32;
     constexpr int CH8 = D / 16;             // 16-byte chunks of codes per row
-    constexpr int NLD = PF_BN * CH8 / 256;  // chunks per thread per tile and tensor
+    constexpr int NT = 64 * NW;             // threads
+    constexpr int NLD = PF_BN * CH8 / NT;   // chunks per thread per tile and tensor
     static_assert(NLD >= 1, "every thread loads part of each tile");
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[2][TILE];
@@ -622,7 +623,7 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void prefill_f8kv(PrefillP
         }
     }
 
-    // Tile staging. Thread chunk c = tid + 256 i covers codes 16 (c % CH8) ..
+    // Tile staging. Thread chunk c = tid + NT i covers codes 16 (c % CH8) ..
     // +16 of tile row c / CH8; rows outside [kv_lo, skv) read the nearest valid
     // row (masked later), so every load stays inside the visible key range.
     const uint8_t* kb8 = (const uint8_t*)p.k + (int64_t)b * p.ks.batch + (int64_t)hk * p.ks.head;
@@ -633,7 +634,7 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void prefill_f8kv(PrefillP
         const int kv0 = j * PF_BN;
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-            const int c = tid + 256 * i;
+            const int c = tid + NT * i;
             const int key = min(max(kv0 + c / CH8, key_min), key_max);
             const int col = 16 * (c % CH8);
             kr[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(kb8 + (int64_t)key * p.ks.seq + col)));
@@ -660,7 +661,7 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void prefill_f8kv(PrefillP
     auto store = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-            const int c = tid + 256 * i;
+            const int c = tid + NT * i;
             const int row = c / CH8, cc = c % CH8;
             uint4 lo, hi;
             char* krow = (char*)Ks[buf] + row * D * 2;
@@ -975,16 +976,26 @@ static hipError_t launch_f32_mask(PrefillParams p, int mask, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <bool BF16, int D>
-static hipError_t launch_f8kv_mask(PrefillParams p, int mask, hipStream_t s) {
-    p.n_q_tiles = (p.seqlen_q + 4 * PF_ROWS_PER_WAVE - 1) / (4 * PF_ROWS_PER_WAVE);
-    const dim3 grid((unsigned)p.n_q_tiles * p.batch * p.n_q_heads), block(256);
+template <bool BF16, int D, int NW>
+static hipError_t launch_f8kv_nw(PrefillParams p, int mask, hipStream_t s) {
+    p.n_q_tiles = (p.seqlen_q + NW * PF_ROWS_PER_WAVE - 1) / (NW * PF_ROWS_PER_WAVE);
+    const dim3 grid((unsigned)p.n_q_tiles * p.batch * p.n_q_heads), block(64 * NW);
     switch (mask) {
-        case kMaskNone: hipLaunchKernelGGL((prefill_f8kv<BF16, D, kMaskNone>), grid, block, 0, s, p); break;
-        case kMaskCausal: hipLaunchKernelGGL((prefill_f8kv<BF16, D, kMaskCausal>), grid, block, 0, s, p); break;
-        default: hipLaunchKernelGGL((prefill_f8kv<BF16, D, kMaskCausalWindow>), grid, block, 0, s, p); break;
+        case kMaskNone: hipLaunchKernelGGL((prefill_f8kv<BF16, D, kMaskNone, NW>), grid, block, 0, s, p); break;
+        case kMaskCausal: hipLaunchKernelGGL((prefill_f8kv<BF16, D, kMaskCausal, NW>), grid, block, 0, s, p); break;
+        default: hipLaunchKernelGGL((prefill_f8kv<BF16, D, kMaskCausalWindow, NW>), grid, block, 0, s, p); break;
     }
     return hipGetLastError();
+}
+
+// Eight waves for D = 128 on the grids where prefill_mfma takes them.
+template <bool BF16, int D>
+static hipError_t launch_f8kv_mask(PrefillParams p, int mask, hipStream_t s) {
+    if constexpr (D == 128) {
+        const long wide = (long)((p.seqlen_q + 255) / 256) * p.batch * p.n_q_heads;
+        if (wide >= kPrefillWideMinWorkgroups) return launch_f8kv_nw<BF16, D, 8>(p, mask, s);
+    }
+    return launch_f8kv_nw<BF16, D, 4>(p, mask, s);
 }
 
 template <bool BF16>
