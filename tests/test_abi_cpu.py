@@ -301,3 +301,16 @@ def validate(**kw):
 ])
 def test_validate_pages_rejects_before_any_hip_call(kw, status):
     assert validate(**kw) == status
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback path: without the built library every entry point raises before doing anything."""
+    import torch
+
+    monkeypatch.setattr(A, "LIB_PATH", str(tmp_path / "libattn.so"))
+    monkeypatch.setattr(A, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        A.lib()
+    t = torch.zeros(1, 1, 1, 64)
+    with pytest.raises((RuntimeError, ValueError)):
+        A.prefill(t, t, t)
