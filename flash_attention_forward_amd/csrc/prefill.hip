@@ -29,6 +29,9 @@
 //
 // f32: prefill_f32 — the same recurrence on the vector ALUs (no f32 MFMA
 // shortcut is used): 64 rows per workgroup, four lanes per row.
+//
+// FP8 K/V: prefill_f8kv — K and V stored as E4M3 codes, widened into the
+// same LDS tiles, then prefill_mfma's per-tile math without the pipeline.
 #include "device_common.hpp"
 #include "kernels.hpp"
 

@@ -129,3 +129,27 @@ def test_fp8_prefill_full_size_sampled():
     v64 = np.float64(np.float32(vs)) * W.as_f64(v8, "fp8")
     ref, _ = oracle.attention_rows(W.as_f64(inp.q, spec.dtype), k64, v64, spec.scale_f32, True, 0, rows)
     check(got[rows[:, 0], rows[:, 1], rows[:, 2]], ref, spec.dtype, "32K with an FP8 cache")
+
+
+def test_fp8_prefill_nan_codes_outside_the_visible_keys_never_leak():
+    """NaN codes (0x7F) past seqlen_kv, and in keys before the first query's window, change no bit."""
+    import flash_attention_forward_amd as F
+
+    torch = torch_cuda()
+    case = (1, 2, 1, 130, 300, 128, "bf16", True, 90, 0.5, 0.25)
+    q, k, v = make(case, 12)
+    Sq, Skv, w = 130, 300, 90
+    scale = float(np.float32(1.0 / np.sqrt(128)))
+    qt = dev(q, "bf16")
+    say("fp8 prefill nan codes outside the visible keys")
+    ref = F.prefill(qt, W.to_torch(k, "fp8", "cuda"), W.to_torch(v, "fp8", "cuda"), scale=scale, causal=True, window=w,
+                    k_scale=0.5, v_scale=0.25)
+    kbig = np.full((1, Skv + 70, 1, 128), 0x7F, np.uint8)
+    vbig = kbig.copy()
+    first_visible = (Skv - Sq) - w + 1  # no query sees keys below this
+    kbig[:, first_visible:Skv] = k[:, first_visible:]
+    vbig[:, first_visible:Skv] = v[:, first_visible:]
+    kt, vt = W.to_torch(kbig, "fp8", "cuda"), W.to_torch(vbig, "fp8", "cuda")
+    o = F.prefill(qt, kt[:, :Skv], vt[:, :Skv], scale=scale, causal=True, window=w, k_scale=0.5, v_scale=0.25)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
