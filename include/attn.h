@@ -8,10 +8,14 @@
  * with the online-softmax recurrence (running row max m, running sum l,
  * rescale alpha = exp(m_old - m_new) of O and l, final O * (1/l)):
  *   - attn_prefill_fwd     long Q against K/V of the same sequence (compute bound),
- *                          with _ex (lse output, sinks) and _varlen (packed sequences);
+ *                          with _ex (lse output, sinks), _varlen (packed sequences)
+ *                          and _fp8kv (K and V stored as FP8 E4M3);
  *   - attn_decode_fwd      a few query tokens against a long, optionally paged,
- *                          KV cache, split along the cache into partial results;
- *   - attn_decode_combine  the log-sum-exp merge of those partials.
+ *                          KV cache, split along the cache into partial results
+ *                          (_fp8kv: an FP8 E4M3 cache);
+ *   - attn_decode_combine  the log-sum-exp merge of those partials (_ex: lse, sinks).
+ * Helpers: attn_decode_workspace_size, attn_decode_validate_pages (a device-side
+ * check of a page table) and attn_status_string.
  *
  * The recurrence and its final normalisation are the ones described on the
  * "Flash-Attention: Context (CTE)" page (section "The online-softmax
