@@ -153,3 +153,19 @@ def test_fp8_prefill_nan_codes_outside_the_visible_keys_never_leak():
     o = F.prefill(qt, kt[:, :Skv], vt[:, :Skv], scale=scale, causal=True, window=w, k_scale=0.5, v_scale=0.25)
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
+
+
+def test_fp8_prefill_repeated_runs_bit_identical():
+    """The same launch repeated gives bit-identical outputs (eight-wave launch, window masks)."""
+    import flash_attention_forward_amd as F
+
+    torch = torch_cuda()
+    case = (2, 16, 2, 4096, 4096, 128, "bf16", True, 700, 0.5, 0.25)  # 16 tiles x 2 x 16 heads: the eight-wave launch
+    q, k, v = make(case, 13)
+    qt, kt, vt = dev(q, "bf16"), W.to_torch(k, "fp8", "cuda"), W.to_torch(v, "fp8", "cuda")
+    say("fp8 prefill repeated runs")
+    first = F.prefill(qt, kt, vt, causal=True, window=700, k_scale=0.5, v_scale=0.25)
+    for _ in range(20):
+        again = F.prefill(qt, kt, vt, causal=True, window=700, k_scale=0.5, v_scale=0.25)
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int16), first.view(torch.int16))
