@@ -59,6 +59,36 @@ __device__ __forceinline__ int pf_vswz(int row) {
     return D == 64 ? 4 * ((row >> 1) & 1) : 4 * (row & 3);
 }
 
+// Q fragments of one lane (B operand of S^T = K Q^T: row l32, d = 16s + 8hf
+// .. +8), read from qrow (already offset by 8 hf); zeros when the row is
+// outside the sequence. qflip flips the sign bits when the scale is negative.
+template <int D>
+__device__ __forceinline__ void pf_load_q(s16x8 (&qf)[D / 16], const uint16_t* qrow, bool valid, uint32_t qflip) {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (valid) x = *(const uint4*)(qrow + 16 * s);
+        x.x ^= qflip; x.y ^= qflip; x.z ^= qflip; x.w ^= qflip;
+        qf[s] = __builtin_bit_cast(s16x8, x);
+    }
+}
+
+// One lane's half of an output row: O^T tile dt holds d = 32 dt + 8 rq + 4 hf
+// .. +4 in registers 4 rq .. 4 rq + 3, each multiplied by inv and rounded.
+template <bool BF16, int NDT>
+__device__ __forceinline__ void pf_store_o(const f32x16 (&o)[NDT], float inv, uint16_t* orow, int hf) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            const int d = 32 * dt + 8 * rq + 4 * hf;
+            uint2 pk;
+            pk.x = pack2_16<BF16>(o[dt][4 * rq + 0] * inv, o[dt][4 * rq + 1] * inv);
+            pk.y = pack2_16<BF16>(o[dt][4 * rq + 2] * inv, o[dt][4 * rq + 3] * inv);
+            *(uint2*)(orow + d) = pk;
+        }
+}
+
 // NW waves per workgroup: 4 (two workgroups per CU for D <= 128) or 8 (one
 // workgroup per CU, twice the query rows per K/V tile: half the L2-to-LDS
 // traffic per FLOP).
@@ -157,19 +187,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     const int my_pos = pos_of(my_q);
     const int wpos0 = pos_of(wq0), wpos1 = pos_of(wq1);  // positions of the wave's first and last rows
 
-    // Q fragments: B operand of S^T = K Q^T (lane: row l32, d = 16s + 8hf .. +8).
     s16x8 qf[D / 16];
-    {
-        const uint16_t* qrow = (const uint16_t*)p.q + q_at + (int64_t)my_q * p.qs.seq +
-                               (int64_t)h * p.qs.head + 8 * hf;
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (my_q < sq) x = *(const uint4*)(qrow + 16 * s);
-            x.x ^= p.qflip; x.y ^= p.qflip; x.z ^= p.qflip; x.w ^= p.qflip;
-            qf[s] = __builtin_bit_cast(s16x8, x);
-        }
-    }
+    pf_load_q<D>(qf, (const uint16_t*)p.q + q_at + (int64_t)my_q * p.qs.seq + (int64_t)h * p.qs.head + 8 * hf,
+                 my_q < sq, p.qflip);
 
     const uint16_t* kbase = (const uint16_t*)p.k + k_at + (int64_t)hk * p.ks.head;
     const uint16_t* vbase = (const uint16_t*)p.v + v_at + (int64_t)hk * p.vs.head;
@@ -538,20 +558,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     if (p.lse && hf == 0 && wave_live && my_q < sq)
         p.lse[(lse_at + my_q) * p.n_q_heads + h] =
             l_tot > 0.f ? (m_fin + __log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
-    if (wave_live && my_q < sq) {
-        uint16_t* orow = (uint16_t*)p.o + o_at + (int64_t)my_q * p.os.seq +
-                         (int64_t)h * p.os.head;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const int d = 32 * dt + 8 * rq + 4 * hf;
-                uint2 pk;
-                pk.x = pack2_16<BF16>(o[dt][4 * rq + 0] * inv, o[dt][4 * rq + 1] * inv);
-                pk.y = pack2_16<BF16>(o[dt][4 * rq + 2] * inv, o[dt][4 * rq + 3] * inv);
-                *(uint2*)(orow + d) = pk;
-            }
-    }
+    if (wave_live && my_q < sq)
+        pf_store_o<BF16, NDT>(o, inv, (uint16_t*)p.o + o_at + (int64_t)my_q * p.os.seq + (int64_t)h * p.os.head, hf);
 }
 
 // ---------------------------------------------------------------------------- FP8 K/V
@@ -612,19 +620,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     const int my_pos = my_q + off;
     const int wpos0 = wq0 + off, wpos1 = wq1 + off;
 
-    // Q fragments: B operand of S^T = K Q^T (lane: row l32, d = 16s + 8hf .. +8).
     s16x8 qf[D / 16];
-    {
-        const uint16_t* qrow = (const uint16_t*)p.q + (int64_t)b * p.qs.batch + (int64_t)my_q * p.qs.seq +
-                               (int64_t)h * p.qs.head + 8 * hf;
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (my_q < sq) x = *(const uint4*)(qrow + 16 * s);
-            x.x ^= p.qflip; x.y ^= p.qflip; x.z ^= p.qflip; x.w ^= p.qflip;
-            qf[s] = __builtin_bit_cast(s16x8, x);
-        }
-    }
+    pf_load_q<D>(qf, (const uint16_t*)p.q + (int64_t)b * p.qs.batch + (int64_t)my_q * p.qs.seq + (int64_t)h * p.qs.head + 8 * hf,
+                 my_q < sq, p.qflip);
 
     // Tile staging. Thread chunk c = tid + NT i covers codes 16 (c % CH8) ..
     // +16 of tile row c / CH8; rows outside [kv_lo, skv) read the nearest valid
@@ -795,19 +793,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     if (p.lse && hf == 0 && wave_live && my_q < sq)
         p.lse[((int64_t)b * p.seqlen_q + my_q) * p.n_q_heads + h] =
             l_tot > 0.f ? (m_fin + __log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
-    if (wave_live && my_q < sq) {
-        uint16_t* orow = (uint16_t*)p.o + (int64_t)b * p.os.batch + (int64_t)my_q * p.os.seq + (int64_t)h * p.os.head;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const int d = 32 * dt + 8 * rq + 4 * hf;
-                uint2 pk;
-                pk.x = pack2_16<BF16>(o[dt][4 * rq + 0] * inv, o[dt][4 * rq + 1] * inv);
-                pk.y = pack2_16<BF16>(o[dt][4 * rq + 2] * inv, o[dt][4 * rq + 3] * inv);
-                *(uint2*)(orow + d) = pk;
-            }
-    }
+    if (wave_live && my_q < sq)
+        pf_store_o<BF16, NDT>(o, inv,
+                              (uint16_t*)p.o + (int64_t)b * p.os.batch + (int64_t)my_q * p.os.seq + (int64_t)h * p.os.head, hf);
 }
 
 // ---------------------------------------------------------------------------- f32
