@@ -23,3 +23,16 @@ def test_prefill_flops_count_visible_pairs():
     # window w: row i sees min(i + 1, w) keys
     s = W.PrefillSpec(2, 1, 1, 50, 50, 128, "bf16", causal=True, window=7)
     assert bench.prefill_flops(s) == 4 * 128 * 2 * sum(min(i + 1, 7) for i in range(50))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """One GPU only: --gpus 2 exits non-zero with a message, before touching any device."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
