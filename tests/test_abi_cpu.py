@@ -73,6 +73,8 @@ def prefill(**kw):
     (dict(sq=-5), INVALID),
     (dict(scale=float("nan")), INVALID),
     (dict(scale=float("inf")), INVALID),
+    (dict(ks=st(0, 1 << 25, 128)), UNSUPPORTED),               # a 64-row tile would span more than 2^31 elements
+    (dict(batch=1 << 20, hq=1 << 12, hkv=1 << 12), UNSUPPORTED),  # more than 2^31 workgroups
 ])
 def test_prefill_rejects(kw, status):
     assert prefill(**kw) == status
@@ -108,6 +110,8 @@ def decode(**kw):
     (dict(po=0), INVALID),
     (dict(k=FAKE + 8), INVALID),
     (dict(scale=float("nan")), INVALID),
+    (dict(split=16, ms=70000), UNSUPPORTED),   # more splits than a grid dimension holds
+    (dict(batch=70000), UNSUPPORTED),          # more sequences than a grid dimension holds
 ])
 def test_decode_rejects(kw, status):
     assert decode(**kw) == status
