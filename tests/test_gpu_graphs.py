@@ -155,3 +155,40 @@ def test_varlen_graph_serves_new_length_mixes():
             f64 = lambda t: W.as_f64(W.from_torch(t[:n], "bf16"), "bf16")
             ref64 = oracle.attention_varlen(f64(q), f64(k), f64(v), cu_h, cu_h, scale, True, 0)
             check(host64(got, "bf16")[:n], ref64, "bf16", "graph replay vs oracle")
+
+
+def test_fp8_prefill_graph_replays_match_eager():
+    """attn_prefill_fwd_fp8kv in a graph: new FP8 codes written in place between replays."""
+    import flash_attention_forward_amd as F
+
+    torch = torch_cuda()
+    B, Hq, Hkv, S, D, ks, vs = 2, 4, 2, 300, 128, 0.5, 0.25
+    rng = np.random.default_rng(9)
+    q = dev(W.normal_rounded(rng, (B, S, Hq, D), "bf16"), "bf16")
+    k = W.to_torch(W.normal_rounded(rng, (B, S, Hkv, D), "fp8", divide_by=ks), "fp8", "cuda")
+    v = W.to_torch(W.normal_rounded(rng, (B, S, Hkv, D), "fp8", divide_by=vs), "fp8", "cuda")
+    out = torch.empty_like(q)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+
+    def call(o):
+        F.prefill(q, k, v, scale=scale, causal=True, window=90, out=o, k_scale=ks, v_scale=vs)
+
+    say("fp8 prefill graph")
+    g = capture(lambda: call(out))
+    for it in range(REPLAYS):
+        k8 = W.normal_rounded(rng, (B, S, Hkv, D), "fp8", divide_by=ks)
+        v8 = W.normal_rounded(rng, (B, S, Hkv, D), "fp8", divide_by=vs)
+        k.copy_(W.to_torch(k8, "fp8", "cuda"))
+        v.copy_(W.to_torch(v8, "fp8", "cuda"))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref = torch.empty_like(out)
+        call(ref)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {it}"
+        if it == REPLAYS - 1:
+            q64 = W.as_f64(W.from_torch(q, "bf16"), "bf16")
+            ref64 = oracle.attention(q64, np.float64(ks) * W.as_f64(k8, "fp8"), np.float64(vs) * W.as_f64(v8, "fp8"),
+                                     scale, True, 90)
+            check(host64(got, "bf16"), ref64, "bf16", "graph replay vs oracle")
