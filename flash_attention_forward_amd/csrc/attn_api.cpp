@@ -93,8 +93,8 @@ int prefill_impl(const void* q, attn_strides q_st, const void* k, attn_strides k
     if ((cu_seqlens_q == nullptr) != (cu_seqlens_kv == nullptr)) return ATTN_ERR_INVALID;
     if (cu_seqlens_q && (!aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_kv))) return ATTN_ERR_INVALID;
     if (!aligned4(positions)) return ATTN_ERR_INVALID;
-    // lane offsets inside one 64-row K/V tile are kept in 32 bits
-    if (k_st.seq * 64 + head_dim >= ((int64_t)1 << 31) || v_st.seq * 64 + head_dim >= ((int64_t)1 << 31))
+    // byte offsets inside one 64-row K/V tile (buffer records and lane offsets) are kept in 31 bits
+    if ((k_st.seq * 64 + head_dim) * kvb >= ((int64_t)1 << 31) || (v_st.seq * 64 + head_dim) * kvb >= ((int64_t)1 << 31))
         return ATTN_ERR_UNSUPPORTED;
     const int64_t tiles = (seqlen_q + 63) / 64;
     if (tiles * batch * n_q_heads >= (int64_t)1 << 31) return ATTN_ERR_UNSUPPORTED;

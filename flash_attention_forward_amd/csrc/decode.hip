@@ -273,9 +273,11 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
     };
 
     // Every load is issued unconditionally with its row clamped to a valid
-    // token: rows past the end (and whole blocks past the last one) re-read
-    // finite cache data, get probability exactly 0 in the softmax and so add
-    // exactly nothing to P V. Nothing at or beyond cache_len is ever read. With
+    // token: rows past the end (and whole blocks past the last one), and rows
+    // of the first block below the earliest query's window, re-read cache
+    // data that some query row sees, get probability exactly 0 in the softmax
+    // and so add exactly nothing to P V. Nothing at or beyond cache_len and
+    // nothing before that window is ever read. With
     // no conditional loads, each lane has exactly 2 * VLD loads per block in
     // flight and the wait counts below hold on every path.
     const int tlast = t1 - 1;
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
     const int t_from = p.window > 0 ? len - p.window : 0;
     // FAST: offset of the 16-aligned group holding token t, plus the row within it
     auto fast_off = [&](int t) -> int64_t {
-        const int tc = min(t, tlast);
+        const int tc = min(max(t, tlo), tlast);
         const int tg = tc & ~15;
         return row_off(tg) + (int64_t)(tc - tg) * seq;
     };
@@ -311,7 +313,7 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
     // within the group, swizzled chunk), so its loads cost no vector ALU work.
     const bool lane_addr = MODE != kDecodeGeneric && p.lane_addr32;
     auto load_rows = [&](uint16_t* dst, const uint16_t* base, int tb, bool is_k) __attribute__((always_inline)) {
-        if (lane_addr && tb + DC_KB <= t1) {
+        if (lane_addr && tb >= tlo && tb + DC_KB <= t1) {
             const int64_t g0 = group_off(tb), g1 = group_off(tb + 16);
 #pragma unroll
             for (int i = 0; i < VLD; ++i) {
@@ -331,7 +333,7 @@ __global__ __launch_bounds__(64 * HW) void decode_split(DecodeParams p) {
             const int row = i * RPL + lane / CPR;
             const int t = tb + row;
             const int c = cs ^ (is_k ? dc_kswz<D>(row) : dc_vswz<D>(row));
-            const int64_t off = MODE == kDecodeGeneric ? row_off(min(t, tlast)) : fast_off(t);
+            const int64_t off = MODE == kDecodeGeneric ? row_off(min(max(t, tlo), tlast)) : fast_off(t);
             __builtin_amdgcn_global_load_lds(base + off + 8 * c, (__attribute__((address_space(3))) void*)(dst + 512 * i),
                                              16, 0, kStreamPolicy);
         }
@@ -566,14 +568,15 @@ __global__ __launch_bounds__(64 * HW) void decode_split_f8(DecodeParams p) {
             return (int64_t)pages[pi] * p.kvs.batch + (int64_t)slot * seq;
         }
     };
-    // Rows are clamped to the last valid token (see decode_split): rows past
-    // the end re-read finite cache data and get probability exactly 0.
+    // Rows are clamped to [tlo, t1) (see decode_split): rows past the end and
+    // below the earliest query's window re-read visible cache data and get
+    // probability exactly 0.
     const int tlast = t1 - 1;
     // Keys in [t_from, t_full) are visible to every query row of the wave.
     const int t_full = min(t1, len - p.s_active + 1);
     const int t_from = p.window > 0 ? len - p.window : 0;
     auto tok_off = [&](int t) -> int64_t {
-        const int tc = min(t, tlast);
+        const int tc = min(max(t, tlo), tlast);
         if constexpr (MODE == kDecodeFast) {
             const int tg = tc & ~15;
             return row_off(tg) + (int64_t)(tc - tg) * seq;
@@ -598,7 +601,7 @@ __global__ __launch_bounds__(64 * HW) void decode_split_f8(DecodeParams p) {
     // work; other blocks clamp row by row.
     const bool lane_addr = MODE != kDecodeGeneric && p.lane_addr32;
     auto load_block = [&](uint4 (&kr)[NI], uint4 (&vr)[NI], int tb) __attribute__((always_inline)) {
-        if (lane_addr && tb + DC_KB <= t1) {
+        if (lane_addr && tb >= tlo && tb + DC_KB <= t1) {
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int64_t go = group_off(tb + ((RPI * i) & ~15));
@@ -796,10 +799,13 @@ __global__ __launch_bounds__(64) void decode_combine(CombineParams p) {
     // Attention sink: one more logit of the row, with no value (the decode
     // page's per-q-head sink), merged like a split with O = 0. The partial
     // LSEs are natural-log, so the sink enters in the same units.
+    // A NaN or +inf sink makes the row NaN (written as NaN bits).
     float osc = 1.f;
+    bool nan_row = false;
     if (p.sinks) {
         const float sk = p.sinks[h];
-        if (sk > -__builtin_inff()) {
+        nan_row = sink_gives_nan(sk);
+        if (sk > -__builtin_inff() && !nan_row) {
             const float mn = fmaxf(M, sk);
             osc = fast_exp2((M - mn) * kLog2e);  // 0 when no split was visible (M = -inf)
             wsum = wsum * osc + fast_exp2((sk - mn) * kLog2e);
@@ -807,12 +813,14 @@ __global__ __launch_bounds__(64) void decode_combine(CombineParams p) {
         }
     }
     const float inv = wsum > 0.f ? osc / wsum : 0.f;
-    if (p.lse && lane == 0) p.lse[row] = wsum > 0.f ? M + __logf(wsum) : -__builtin_inff();
+    if (p.lse && lane == 0)
+        *(uint32_t*)&p.lse[row] = nan_row ? kNaN32 : __float_as_uint(wsum > 0.f ? M + __logf(wsum) : -__builtin_inff());
     if (r == 0) {
         uint16_t* orow = (uint16_t*)p.o + (int64_t)b * p.os.batch + (int64_t)i * p.os.seq + (int64_t)h * p.os.head;
         uint2 pk;
         pk.x = pack2_16<BF16>(acc.x * inv, acc.y * inv);
         pk.y = pack2_16<BF16>(acc.z * inv, acc.w * inv);
+        if (nan_row) pk = make_uint2(kNaN16x2<BF16>, kNaN16x2<BF16>);
         *(uint2*)(orow + 4 * c) = pk;
     }
 }

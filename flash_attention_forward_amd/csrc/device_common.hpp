@@ -106,6 +106,18 @@ __device__ __forceinline__ float fold_sink(float s2, float& m, float& l) {
     return a;
 }
 
+// A sink logit that is NaN or +inf (any non-finite value but -inf), tested on
+// its bits: the kernels are built without NaN semantics for float compares.
+// Such a sink makes every row of its head NaN (its exp is NaN or makes the
+// sum infinite), so the epilogues then write NaN bit patterns directly.
+__device__ __forceinline__ bool sink_gives_nan(float s) {
+    const uint32_t bits = __float_as_uint(s);
+    return (bits & 0x7f800000u) == 0x7f800000u && bits != 0xff800000u;
+}
+constexpr uint32_t kNaN32 = 0x7fc00000u;                // quiet f32 NaN
+template <bool BF16>
+constexpr uint32_t kNaN16x2 = BF16 ? 0x7fc07fc0u : 0x7e007e00u;  // two quiet bf16 / f16 NaNs
+
 // Round-to-nearest-even conversions of f32 to 16-bit floats, returned as raw bits.
 template <bool BF16>
 __device__ __forceinline__ uint16_t f32_to_16(float x) {

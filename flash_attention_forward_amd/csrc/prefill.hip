@@ -74,9 +74,10 @@ __device__ __forceinline__ void pf_load_q(s16x8 (&qf)[D / 16], const uint16_t* q
 }
 
 // One lane's half of an output row: O^T tile dt holds d = 32 dt + 8 rq + 4 hf
-// .. +4 in registers 4 rq .. 4 rq + 3, each multiplied by inv and rounded.
+// .. +4 in registers 4 rq .. 4 rq + 3, each multiplied by inv and rounded
+// (NaN throughout when nan_row: a NaN or +inf sink).
 template <bool BF16, int NDT>
-__device__ __forceinline__ void pf_store_o(const f32x16 (&o)[NDT], float inv, uint16_t* orow, int hf) {
+__device__ __forceinline__ void pf_store_o(const f32x16 (&o)[NDT], float inv, uint16_t* orow, int hf, bool nan_row) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -85,8 +86,17 @@ __device__ __forceinline__ void pf_store_o(const f32x16 (&o)[NDT], float inv, ui
             uint2 pk;
             pk.x = pack2_16<BF16>(o[dt][4 * rq + 0] * inv, o[dt][4 * rq + 1] * inv);
             pk.y = pack2_16<BF16>(o[dt][4 * rq + 2] * inv, o[dt][4 * rq + 3] * inv);
+            if (nan_row) pk = make_uint2(kNaN16x2<BF16>, kNaN16x2<BF16>);
             *(uint2*)(orow + d) = pk;
         }
+}
+
+// The row's log-sum-exp (natural log) from m and l in scaled log2 units: -inf
+// without any visible key or sink, NaN bits with a NaN or +inf sink.
+__device__ __forceinline__ void pf_store_lse(float* dst, float m, float l, bool nan_row) {
+    const uint32_t bits = nan_row ? kNaN32
+                                  : __float_as_uint(l > 0.f ? (m + __log2f(l)) * 0.69314718055994531f : -__builtin_inff());
+    *(uint32_t*)dst = bits;
 }
 
 // NW waves per workgroup: 4 (two workgroups per CU for D <= 128) or 8 (one
@@ -203,7 +213,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     // .. RPL*i + RPL-1; lane l takes row RPL*i + l/CPR and the swizzled chunk
     // (l%CPR ^ g(l/CPR)) ^ U(i) (the K or V swizzle factored into a lane part
     // and a uniform part), so a lane keeps two offsets per tensor. A tile
-    // spans fewer than 64 * seq elements, which the host keeps below 2^31.
+    // spans fewer than 64 * seq + D elements, whose bytes the host keeps below 2^31.
     // Edge tiles clamp row by row.
     constexpr int RPL = 64 / CPR;
     const int lrow = lane / CPR, lcs = lane % CPR;
@@ -266,7 +276,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     }
     auto tile_rsrc = [&](const uint16_t* base, int64_t seq, int j) __attribute__((always_inline)) {
         const int kv0 = j * PF_BN;
-        const int nrec = kv0 + PF_BN - 1 <= key_max ? 0x7fffffff : 2 * ((key_max - kv0) * (int)seq + D);
+        const uint32_t nrec =
+            kv0 + PF_BN - 1 <= key_max ? 0x7fffffffu : 2u * ((uint32_t)(key_max - kv0) * (uint32_t)seq + (uint32_t)D);
         return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kv0 * seq), (short)0, nrec, 0x00020000);
     };
     auto load_part = [&](uint16_t* dst, __amdgpu_buffer_rsrc_t rs, uint32_t voff, int ii) __attribute__((always_inline)) {
@@ -553,13 +564,15 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     // key are written as zeros. The log-sum-exp (natural log) goes to lse.
     float l_tot = sum_with_other_half(l_i);
     float m_fin = m_i;
-    const float osc = p.sinks ? fold_sink(p.sinks[h] * kLog2e, m_fin, l_tot) : 1.f;
+    const float sink = p.sinks ? p.sinks[h] : -__builtin_inff();
+    const bool nan_row = sink_gives_nan(sink);
+    const float osc = p.sinks ? fold_sink(sink * kLog2e, m_fin, l_tot) : 1.f;
     const float inv = l_tot > 0.f ? osc / l_tot : 0.f;
     if (p.lse && hf == 0 && wave_live && my_q < sq)
-        p.lse[(lse_at + my_q) * p.n_q_heads + h] =
-            l_tot > 0.f ? (m_fin + __log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
+        pf_store_lse(&p.lse[(lse_at + my_q) * p.n_q_heads + h], m_fin, l_tot, nan_row);
     if (wave_live && my_q < sq)
-        pf_store_o<BF16, NDT>(o, inv, (uint16_t*)p.o + o_at + (int64_t)my_q * p.os.seq + (int64_t)h * p.os.head, hf);
+        pf_store_o<BF16, NDT>(o, inv, (uint16_t*)p.o + o_at + (int64_t)my_q * p.os.seq + (int64_t)h * p.os.head, hf,
+                              nan_row);
 }
 
 // ---------------------------------------------------------------------------- FP8 K/V
@@ -788,14 +801,16 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     // no key are written as zeros. The log-sum-exp (natural log) goes to lse.
     float l_tot = sum_with_other_half(l_i);
     float m_fin = m_i;
-    const float osc = p.sinks ? fold_sink(p.sinks[h] * kLog2e, m_fin, l_tot) : 1.f;
+    const float sink = p.sinks ? p.sinks[h] : -__builtin_inff();
+    const bool nan_row = sink_gives_nan(sink);
+    const float osc = p.sinks ? fold_sink(sink * kLog2e, m_fin, l_tot) : 1.f;
     const float inv = l_tot > 0.f ? osc * p.v_scale / l_tot : 0.f;
     if (p.lse && hf == 0 && wave_live && my_q < sq)
-        p.lse[((int64_t)b * p.seqlen_q + my_q) * p.n_q_heads + h] =
-            l_tot > 0.f ? (m_fin + __log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
+        pf_store_lse(&p.lse[((int64_t)b * p.seqlen_q + my_q) * p.n_q_heads + h], m_fin, l_tot, nan_row);
     if (wave_live && my_q < sq)
         pf_store_o<BF16, NDT>(o, inv,
-                              (uint16_t*)p.o + (int64_t)b * p.os.batch + (int64_t)my_q * p.os.seq + (int64_t)h * p.os.head, hf);
+                              (uint16_t*)p.o + (int64_t)b * p.os.batch + (int64_t)my_q * p.os.seq + (int64_t)h * p.os.head, hf,
+                              nan_row);
 }
 
 // ---------------------------------------------------------------------------- f32
@@ -911,16 +926,20 @@ __global__ __launch_bounds__(256) void prefill_f32(PrefillParams p) {
     }
     if (live) {
         float m_fin = m_i;
-        const float osc = p.sinks ? fold_sink(p.sinks[h] * kLog2e, m_fin, l_i) : 1.f;
+        const float sink = p.sinks ? p.sinks[h] : -__builtin_inff();
+        const bool nan_row = sink_gives_nan(sink);
+        const float osc = p.sinks ? fold_sink(sink * kLog2e, m_fin, l_i) : 1.f;
         const float inv = l_i > 0.f ? osc / l_i : 0.f;
-        if (p.lse && qd == 0)
-            p.lse[(lse_at + my_q) * p.n_q_heads + h] =
-                l_i > 0.f ? (m_fin + __log2f(l_i)) * 0.69314718055994531f : -__builtin_inff();
+        if (p.lse && qd == 0) pf_store_lse(&p.lse[(lse_at + my_q) * p.n_q_heads + h], m_fin, l_i, nan_row);
         float* orow = (float*)p.o + o_at + (int64_t)my_q * p.os.seq + (int64_t)h * p.os.head +
                       qd * DQ;
 #pragma unroll
-        for (int e = 0; e < DQ; e += 4)
-            *(float4*)(orow + e) = make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+        for (int e = 0; e < DQ; e += 4) {
+            uint4 bits = make_uint4(__float_as_uint(acc[e] * inv), __float_as_uint(acc[e + 1] * inv),
+                                    __float_as_uint(acc[e + 2] * inv), __float_as_uint(acc[e + 3] * inv));
+            if (nan_row) bits = make_uint4(kNaN32, kNaN32, kNaN32, kNaN32);
+            *(uint4*)(orow + e) = bits;
+        }
     }
 }
 

@@ -39,6 +39,16 @@
  * key outputs zeros. `scale` multiplies the scores (CTE page, section
  * "Scale"); the library never divides by sqrt(head_dim) itself.
  *
+ * Finite inputs: Q, and K and V at every key some query row of the call
+ * sees, must be finite. Masked keys add exactly nothing for finite data,
+ * bit for bit, also inside the tiles that straddle the diagonal or the
+ * window edge; but a masked key's value row still enters the P*V product of
+ * its tile with probability 0, so a NaN or Inf value there can turn rows of
+ * the same query tile NaN that the plain definition leaves finite. Keys at
+ * or past seqlen_kv (cache_len), keys before the window of the call's
+ * earliest query row and cache pages the table does not reference are never
+ * read, so any bits there are harmless.
+ *
  * Supported: head_dim in {64, 128, 256}; dtype f32, f16 or bf16 for Q, K, V
  * and O alike (f32 accumulation throughout; probabilities are rounded to
  * the input dtype before the P*V product for f16/bf16).

@@ -74,6 +74,8 @@ def prefill(**kw):
     (dict(scale=float("nan")), INVALID),
     (dict(scale=float("inf")), INVALID),
     (dict(ks=st(0, 1 << 25, 128)), UNSUPPORTED),               # a 64-row tile would span more than 2^31 elements
+    (dict(ks=st(0, 3 << 23, 128)), UNSUPPORTED),               # ... or more than 2^31 bytes of 16-bit values
+    (dict(vs=st(0, 3 << 23, 128)), UNSUPPORTED),
     (dict(batch=1 << 20, hq=1 << 12, hkv=1 << 12), UNSUPPORTED),  # more than 2^31 workgroups
 ])
 def test_prefill_rejects(kw, status):

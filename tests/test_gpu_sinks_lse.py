@@ -150,3 +150,75 @@ def test_decode_without_sinks_lse_matches_oracle_and_neg_inf_is_none():
     _, rl = oracle.decode(f64(inp.q), inp.k_pool, inp.v_pool, inp.block_table, inp.cache_len, spec.scale_f32,
                           to_f64=f64, return_lse=True)
     check_lse(l1.cpu().numpy().astype(np.float64), rl, "bf16", "decode lse")
+
+
+def mixed_sinks(hq):
+    """A finite sink, no sink (-inf), NaN and +inf, repeated over the q-heads."""
+    return np.resize(np.array([1.5, -np.inf, np.nan, np.inf], np.float32), hq)
+
+
+@pytest.mark.parametrize("name", ["bf16_causal_ragged", "f32_d64_causal", "wide_bf16_causal",
+                                  "bf16_d64_rows_without_keys"])
+def test_prefill_nan_and_inf_sinks_give_nan_rows(name):
+    """A NaN or +inf sink gives NaN output rows and NaN lse for its head (every row, also those
+    that see no key), as the oracle does; finite and -inf sinks are unaffected."""
+    import flash_attention_forward_amd as F
+
+    torch = torch_cuda()
+    s = PREFILL[name]
+    inp = W.make_prefill(s, seed=310 + len(name))
+    sinks = mixed_sinks(s.n_q_heads)
+    q, k, v = dev(inp.q, s.dtype), dev(inp.k, s.dtype), dev(inp.v, s.dtype)
+    say("prefill NaN/inf sinks", name)
+    o, lse = F.prefill(q, k, v, scale=s.scale_f32, causal=s.causal, window=s.window,
+                       sinks=torch.from_numpy(sinks).cuda(), return_lse=True)
+    torch.cuda.synchronize()
+    f64 = lambda a: W.as_f64(a, s.dtype)
+    ro, rl = oracle.attention(f64(inp.q), f64(inp.k), f64(inp.v), s.scale_f32, s.causal, s.window,
+                              return_lse=True, sinks=sinks.astype(np.float64))
+    got, gl = host64(o, s.dtype), lse.cpu().numpy().astype(np.float64)
+    bad = ~np.isfinite(sinks) & ~np.isneginf(sinks)
+    assert np.isnan(ro[:, :, bad]).all() and np.isnan(rl[:, :, bad]).all()  # the oracle's reading
+    assert np.isnan(got[:, :, bad]).all() and np.isnan(gl[:, :, bad]).all()
+    check(got[:, :, ~bad], ro[:, :, ~bad], s.dtype, name)
+    check_lse(gl[:, :, ~bad], rl[:, :, ~bad], s.dtype, name)
+
+
+def test_fp8_prefill_and_decode_combine_nan_and_inf_sinks():
+    """The same for attn_prefill_fwd_fp8kv and for the decode merge (attn_decode_combine_ex)."""
+    import flash_attention_forward_amd as F
+
+    torch = torch_cuda()
+    rng = np.random.default_rng(3)
+    B, Sq, Hq, Hkv, D = 1, 200, 4, 2, 128
+    q = W.normal_rounded(rng, (B, Sq, Hq, D), "bf16")
+    k8 = W.normal_rounded(rng, (B, Sq, Hkv, D), "fp8")
+    v8 = W.normal_rounded(rng, (B, Sq, Hkv, D), "fp8")
+    sinks = mixed_sinks(Hq)
+    bad = ~np.isfinite(sinks) & ~np.isneginf(sinks)
+    say("fp8 prefill NaN/inf sinks")
+    o, lse = F.prefill(dev(q, "bf16"), W.to_torch(k8, "fp8", "cuda"), W.to_torch(v8, "fp8", "cuda"),
+                       scale=float(np.float32(D ** -0.5)), causal=True, sinks=torch.from_numpy(sinks).cuda(),
+                       return_lse=True)
+    torch.cuda.synchronize()
+    got, gl = host64(o, "bf16"), lse.cpu().numpy()
+    assert np.isnan(got[:, :, bad]).all() and np.isnan(gl[:, :, bad]).all()
+    assert np.isfinite(got[:, :, ~bad]).all() and not np.isnan(gl[:, :, ~bad]).any()
+
+    spec = W.shrink(W.WORKLOADS["paged_decode_b32_d128"], batch=4, n_q_heads=8, n_kv_heads=2, len_lo=1, len_hi=900)
+    inp = W.make_decode(spec, seed=13)
+    dsinks = mixed_sinks(spec.n_q_heads)
+    dbad = ~np.isfinite(dsinks) & ~np.isneginf(dsinks)
+    t = decode_tensors(inp)
+    say("decode combine NaN/inf sinks")
+    o, lse = F.decode(t["q"], t["k"], t["v"], t["cache_len"], block_table=t["block_table"], scale=spec.scale_f32,
+                      split_len=128, max_len=spec.max_pages_per_seq * spec.page_size,
+                      sinks=torch.from_numpy(dsinks).cuda(), return_lse=True)
+    torch.cuda.synchronize()
+    f64 = lambda a: W.as_f64(a, spec.dtype)
+    ro, rl = oracle.decode(f64(inp.q), inp.k_pool, inp.v_pool, inp.block_table, inp.cache_len, spec.scale_f32,
+                           to_f64=f64, return_lse=True, sinks=dsinks.astype(np.float64))
+    got, gl = host64(o, spec.dtype), lse.cpu().numpy().astype(np.float64)
+    assert np.isnan(ro[:, :, dbad]).all() and np.isnan(got[:, :, dbad]).all() and np.isnan(gl[:, :, dbad]).all()
+    check(got[:, :, ~dbad], ro[:, :, ~dbad], spec.dtype, "decode finite sinks")
+    check_lse(gl[:, :, ~dbad], rl[:, :, ~dbad], spec.dtype, "decode finite sinks")

@@ -488,6 +488,19 @@ def test_sinks_rescale_the_plain_result():
     np.testing.assert_array_equal(l2, l0)
 
 
+def test_nan_and_inf_sinks_give_nan_rows():
+    """A NaN sink logit has a NaN exponential, and a +inf one makes the max +inf and its own
+    exponential exp(inf - inf) = NaN (IEEE 754), so the normaliser is NaN in both cases: every row
+    of that head, also one that sees no key, is NaN (output and lse); other heads are untouched."""
+    q, k, v = rand((1, 9, 4, 8), 94), rand((1, 5, 2, 8), 95), rand((1, 5, 2, 8), 96)
+    sinks = np.array([np.nan, 0.5, np.inf, -np.inf])
+    o, l = oracle.attention(q, k, v, 0.6, True, 0, return_lse=True, sinks=sinks)
+    assert np.isnan(o[:, :, [0, 2]]).all() and np.isnan(l[:, :, [0, 2]]).all()
+    o1, l1 = oracle.attention(q, k, v, 0.6, True, 0, return_lse=True, sinks=np.array([0.0, 0.5, 0.0, -np.inf]))
+    np.testing.assert_array_equal(o[:, :, [1, 3]], o1[:, :, [1, 3]])
+    np.testing.assert_array_equal(l[:, :, [1, 3]], l1[:, :, [1, 3]])
+
+
 # ----------------------------------------------------------------------------- FP8 E4M3 storage of the inputs
 def test_e4m3_decode_table_matches_torch():
     """The generator's value of every code equals torch's float8_e4m3fn widening (a library routine)."""
