@@ -9,7 +9,7 @@ import pytest
 import oracle
 from flash_attention_forward_amd import workloads as W
 
-from gpu_common import check, dev, host64, say, torch_cuda
+from gpu_common import attention_with_bound, check, dev, host64, say, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -65,8 +65,12 @@ def test_fp8_prefill_parity(name):
     q, k, v = make(case, 70 + len(name))
     say("fp8 prefill", name)
     got, _ = run(case, q, k, v)
-    ref, _ = reference(case, q, k, v)
-    check(got, ref, case[6], name)
+    B, Hq, Hkv, Sq, Skv, D, dtype, causal, window, ks, vs = case
+    k64 = np.float64(np.float32(ks)) * W.as_f64(k, "fp8")
+    v64 = np.float64(np.float32(vs)) * W.as_f64(v, "fp8")
+    ref, bound = attention_with_bound(W.as_f64(q, dtype), k64, v64, float(np.float32(1.0 / np.sqrt(D))), causal,
+                                      window, dtype)
+    check(got, ref, dtype, name, bound=bound)
 
 
 @pytest.mark.parametrize("name", ["bf16_causal_gqa", "bf16_d256_window", "bf16_more_queries_than_keys"])
