@@ -11,6 +11,7 @@ from .attn import (  # noqa: F401
     attn_decode_combine_ex,
     attn_decode_fwd,
     attn_decode_fwd_fp8kv,
+    attn_decode_fwd_noalloc,
     attn_decode_validate_pages,
     attn_prefill_fwd,
     attn_prefill_fwd_ex,

@@ -23,7 +23,9 @@ ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "kernel launch failed"}
 SYMBOLS = ("attn_prefill_fwd", "attn_prefill_fwd_ex", "attn_prefill_fwd_fp8kv", "attn_prefill_varlen_fwd", "attn_decode_fwd", "attn_decode_fwd_fp8kv",
            "attn_decode_combine", "attn_decode_combine_ex", "attn_decode_validate_pages", "attn_decode_workspace_size",
-           "attn_status_string")
+           "attn_decode_fwd_noalloc", "attn_status_string")
+# Bytes of the library's device array for attn_decode_fwd_noalloc's partials (ATTN_DECODE_NOALLOC_MAX_BYTES).
+DECODE_NOALLOC_MAX_BYTES = 32 << 20
 
 
 class AttnError(RuntimeError):
@@ -75,6 +77,9 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t),
                                              ctypes.POINTER(ctypes.c_size_t)]
     L.attn_decode_workspace_size.restype = i32
+    L.attn_decode_fwd_noalloc.argtypes = [vp, Strides, vp, vp, Strides, vp, i32, i32, vp, i32, i32, i32, i32, i32,
+                                          i32, f32, i32, i32, i32, vp, Strides, vp]
+    L.attn_decode_fwd_noalloc.restype = i32
     L.attn_status_string.argtypes = [i32]
     L.attn_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -277,6 +282,35 @@ def _decode_fwd(q, k_cache, v_cache, cache_len, part_o, part_lse, split_len, max
         if k_cache.dtype not in (torch.float8_e4m3fn, torch.uint8) or v_cache.dtype != k_cache.dtype:
             raise TypeError("FP8 caches must be torch.float8_e4m3fn (or uint8 codes)")
         _check("attn_decode_fwd_fp8kv", lib().attn_decode_fwd_fp8kv(*head, *fp8_scales, *tail))
+
+
+def attn_decode_fwd_noalloc(q, k_cache, v_cache, cache_len, split_len: int, max_splits: int, scale: float, o,
+                            block_table=None, window: int = 0, stream=None) -> None:
+    """attn_decode_fwd + attn_decode_combine in one call, o [B, s_active, Hq, D] written, with the partials in
+    the library's own device array: nothing is allocated (16-bit cache; see DECODE_NOALLOC_MAX_BYTES)."""
+    import torch
+
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (cache_len, "cache_len"), (o, "o")):
+        _gpu(t, n)
+    if cache_len.dtype != torch.int32:
+        raise TypeError("cache_len must be int32")
+    if k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
+        raise ValueError("k_cache and v_cache must have the same shape and strides")
+    if k_cache.dtype != q.dtype or o.dtype != q.dtype or o.shape != q.shape:
+        raise TypeError("k_cache, v_cache and o must have q's dtype, o q's shape")
+    B, sa, Hq, D = q.shape
+    if block_table is not None:
+        _gpu(block_table, "block_table")
+        if block_table.dtype not in (torch.int32, torch.uint32) or not block_table.is_contiguous():
+            raise TypeError("block_table must be a contiguous 32-bit tensor")
+        maxp, ps = block_table.shape[1], k_cache.shape[1]
+    else:
+        maxp, ps = 0, 0
+    rc = lib().attn_decode_fwd_noalloc(_ptr(q), _strides4(q, "q"), _ptr(k_cache), _ptr(v_cache),
+                                       _strides4(k_cache, "k_cache"), _ptr(block_table), maxp, ps, _ptr(cache_len),
+                                       _dtype_code(q), B, sa, Hq, k_cache.shape[2], D, float(scale), int(window),
+                                       int(split_len), int(max_splits), _ptr(o), _strides4(o, "o"), _stream(stream))
+    _check("attn_decode_fwd_noalloc", rc)
 
 
 def attn_decode_combine(part_o, part_lse, cache_len, split_len: int, max_splits: int, o, stream=None) -> None:

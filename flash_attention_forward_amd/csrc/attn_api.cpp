@@ -183,16 +183,23 @@ int attn_decode_workspace_size(int batch, int s_active, int n_q_heads, int head_
 }
 
 namespace {
-// Shared by attn_decode_fwd and attn_decode_fwd_fp8kv: kv_bytes is the cache's element size.
-int decode_fwd_impl(const void* q, attn_strides q_st, const void* k_cache, const void* v_cache, attn_strides kv_st,
-                    const uint32_t* block_table, int max_pages_per_seq, int page_size, const int32_t* cache_len,
-                    attn_dtype dtype, int batch, int s_active, int n_q_heads, int n_kv_heads, int head_dim,
-                    float scale, int window, float* part_o, float* part_lse, int split_len, int max_splits,
-                    int kv_bytes, float v_scale, void* hip_stream) {
+// Validation and parameters shared by attn_decode_fwd, attn_decode_fwd_fp8kv
+// and attn_decode_fwd_noalloc (kv_bytes is the cache's element size). Sets
+// `empty` for a problem with nothing to compute. With workspace = false the
+// partials' pointers are not checked (the caller supplies them later).
+int decode_setup(const void* q, attn_strides q_st, const void* k_cache, const void* v_cache, attn_strides kv_st,
+                 const uint32_t* block_table, int max_pages_per_seq, int page_size, const int32_t* cache_len,
+                 attn_dtype dtype, int batch, int s_active, int n_q_heads, int n_kv_heads, int head_dim, float scale,
+                 int window, float* part_o, float* part_lse, int split_len, int max_splits, int kv_bytes,
+                 float v_scale, bool workspace, attn::DecodeParams& p, bool& empty) {
+    empty = false;
     if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
     if (batch < 0 || s_active < 0 || n_q_heads < 0 || n_kv_heads < 0 || head_dim <= 0) return ATTN_ERR_INVALID;
     if (!std::isfinite(scale)) return ATTN_ERR_INVALID;
-    if (batch == 0 || s_active == 0 || n_q_heads == 0) return ATTN_OK;
+    if (batch == 0 || s_active == 0 || n_q_heads == 0) {
+        empty = true;
+        return ATTN_OK;
+    }
     if (n_kv_heads == 0 || n_q_heads % n_kv_heads != 0) return ATTN_ERR_INVALID;
     if (split_len <= 0 || split_len % 16 != 0 || max_splits <= 0) return ATTN_ERR_INVALID;
     if (block_table) {
@@ -205,11 +212,12 @@ int decode_fwd_impl(const void* q, attn_strides q_st, const void* k_cache, const
     if ((int64_t)(n_q_heads / n_kv_heads) * s_active > (head_dim <= 128 ? 32 : 16)) return ATTN_ERR_UNSUPPORTED;
     if (max_splits > 65535 || batch > 65535) return ATTN_ERR_UNSUPPORTED;
     const int eb = elem_bytes(dtype);
-    if (!q || !k_cache || !v_cache || !cache_len || !part_o || !part_lse) return ATTN_ERR_INVALID;
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(part_o)) return ATTN_ERR_INVALID;
+    if (!q || !k_cache || !v_cache || !cache_len) return ATTN_ERR_INVALID;
+    if (workspace && (!part_o || !part_lse || !aligned16(part_o))) return ATTN_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return ATTN_ERR_INVALID;
     if (!strides_ok(q_st, eb) || !strides_ok(kv_st, kv_bytes)) return ATTN_ERR_INVALID;
 
-    attn::DecodeParams p{};
+    p = attn::DecodeParams{};
     p.q = q; p.k = k_cache; p.v = v_cache;
     p.qs = conv(q_st); p.kvs = conv(kv_st);
     p.block_table = block_table; p.cache_len = cache_len;
@@ -228,7 +236,49 @@ int decode_fwd_impl(const void* q, attn_strides q_st, const void* k_cache, const
     p.kv_fp8 = kv_bytes == 1;
     p.v_scale = v_scale;
     p.lane_addr32 = (int64_t)16 * (kv_st.seq + head_dim) * kv_bytes < ((int64_t)1 << 31);
+    return ATTN_OK;
+}
+
+int decode_fwd_impl(const void* q, attn_strides q_st, const void* k_cache, const void* v_cache, attn_strides kv_st,
+                    const uint32_t* block_table, int max_pages_per_seq, int page_size, const int32_t* cache_len,
+                    attn_dtype dtype, int batch, int s_active, int n_q_heads, int n_kv_heads, int head_dim,
+                    float scale, int window, float* part_o, float* part_lse, int split_len, int max_splits,
+                    int kv_bytes, float v_scale, void* hip_stream) {
+    attn::DecodeParams p;
+    bool empty;
+    const int st = decode_setup(q, q_st, k_cache, v_cache, kv_st, block_table, max_pages_per_seq, page_size, cache_len,
+                                dtype, batch, s_active, n_q_heads, n_kv_heads, head_dim, scale, window, part_o,
+                                part_lse, split_len, max_splits, kv_bytes, v_scale, true, p, empty);
+    if (st != ATTN_OK || empty) return st;
     return status_of(attn::launch_decode(p, (int)dtype, head_dim, (hipStream_t)hip_stream));
+}
+
+// Validation and parameters of the combine (shared by attn_decode_combine_ex
+// and attn_decode_fwd_noalloc); the partials' pointers are checked by the caller.
+int combine_setup(const int32_t* cache_len, int split_len, int max_splits, int batch, int s_active, int n_q_heads,
+                  int head_dim, void* o, attn_strides o_st, attn_dtype dtype, float* lse, const float* sinks,
+                  attn::CombineParams& p, bool& empty) {
+    empty = false;
+    if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
+    if (batch < 0 || s_active < 0 || n_q_heads < 0 || head_dim <= 0) return ATTN_ERR_INVALID;
+    if (batch == 0 || s_active == 0 || n_q_heads == 0) {
+        empty = true;
+        return ATTN_OK;
+    }
+    if (split_len <= 0 || max_splits <= 0) return ATTN_ERR_INVALID;
+    if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+    if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
+    if ((int64_t)batch * s_active * n_q_heads >= (int64_t)1 << 31) return ATTN_ERR_UNSUPPORTED;
+    if (!cache_len || !o || !aligned16(o)) return ATTN_ERR_INVALID;
+    if (!strides_ok(o_st, elem_bytes(dtype))) return ATTN_ERR_INVALID;
+    if (!aligned4(lse) || !aligned4(sinks)) return ATTN_ERR_INVALID;
+
+    p = attn::CombineParams{};
+    p.cache_len = cache_len; p.o = o; p.os = conv(o_st);
+    p.batch = batch; p.s_active = s_active; p.n_q_heads = n_q_heads;
+    p.split_len = split_len; p.max_splits = max_splits;
+    p.lse = lse; p.sinks = sinks;
+    return ATTN_OK;
 }
 }  // namespace
 
@@ -257,22 +307,13 @@ int attn_decode_fwd_fp8kv(const void* q, attn_strides q_st, const uint8_t* k_cac
 int attn_decode_combine_ex(const float* part_o, const float* part_lse, const int32_t* cache_len, int split_len,
                            int max_splits, int batch, int s_active, int n_q_heads, int head_dim, void* o,
                            attn_strides o_st, attn_dtype dtype, float* lse, const float* sinks, void* hip_stream) {
-    if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
-    if (batch < 0 || s_active < 0 || n_q_heads < 0 || head_dim <= 0) return ATTN_ERR_INVALID;
-    if (batch == 0 || s_active == 0 || n_q_heads == 0) return ATTN_OK;
-    if (split_len <= 0 || max_splits <= 0) return ATTN_ERR_INVALID;
-    if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
-    if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
-    if ((int64_t)batch * s_active * n_q_heads >= (int64_t)1 << 31) return ATTN_ERR_UNSUPPORTED;
-    if (!part_o || !part_lse || !cache_len || !o || !aligned16(o)) return ATTN_ERR_INVALID;
-    if (!strides_ok(o_st, elem_bytes(dtype))) return ATTN_ERR_INVALID;
-    if (!aligned4(lse) || !aligned4(sinks)) return ATTN_ERR_INVALID;
-
-    attn::CombineParams p{};
-    p.part_o = part_o; p.part_lse = part_lse; p.cache_len = cache_len; p.o = o; p.os = conv(o_st);
-    p.batch = batch; p.s_active = s_active; p.n_q_heads = n_q_heads;
-    p.split_len = split_len; p.max_splits = max_splits;
-    p.lse = lse; p.sinks = sinks;
+    attn::CombineParams p;
+    bool empty;
+    const int st = combine_setup(cache_len, split_len, max_splits, batch, s_active, n_q_heads, head_dim, o, o_st,
+                                 dtype, lse, sinks, p, empty);
+    if (st != ATTN_OK || empty) return st;
+    if (!part_o || !part_lse) return ATTN_ERR_INVALID;
+    p.part_o = part_o; p.part_lse = part_lse;
     return status_of(attn::launch_combine(p, (int)dtype, head_dim, (hipStream_t)hip_stream));
 }
 
@@ -281,6 +322,38 @@ int attn_decode_combine(const float* part_o, const float* part_lse, const int32_
                         attn_strides o_st, attn_dtype dtype, void* hip_stream) {
     return attn_decode_combine_ex(part_o, part_lse, cache_len, split_len, max_splits, batch, s_active, n_q_heads,
                                   head_dim, o, o_st, dtype, nullptr, nullptr, hip_stream);
+}
+
+int attn_decode_fwd_noalloc(const void* q, attn_strides q_st, const void* k_cache, const void* v_cache,
+                            attn_strides kv_st, const uint32_t* block_table, int max_pages_per_seq, int page_size,
+                            const int32_t* cache_len, attn_dtype dtype, int batch, int s_active, int n_q_heads,
+                            int n_kv_heads, int head_dim, float scale, int window, int split_len, int max_splits,
+                            void* o, attn_strides o_st, void* hip_stream) {
+    attn::DecodeParams dp;
+    attn::CombineParams cp;
+    bool empty;
+    int st = decode_setup(q, q_st, k_cache, v_cache, kv_st, block_table, max_pages_per_seq, page_size, cache_len,
+                          dtype, batch, s_active, n_q_heads, n_kv_heads, head_dim, scale, window, nullptr, nullptr,
+                          split_len, max_splits, elem_bytes(dtype), 1.f, false, dp, empty);
+    if (st != ATTN_OK || empty) return st;
+    st = combine_setup(cache_len, split_len, max_splits, batch, s_active, n_q_heads, head_dim, o, o_st, dtype,
+                       nullptr, nullptr, cp, empty);
+    if (st != ATTN_OK || empty) return st;
+    // the partials, [rows, max_splits, head_dim] then [rows, max_splits] f32, must fit the device array
+    const uint64_t slots = (uint64_t)batch * (uint64_t)s_active * (uint64_t)n_q_heads * (uint64_t)max_splits;
+    if (slots * ((uint64_t)head_dim + 1) * sizeof(float) > ATTN_DECODE_NOALLOC_MAX_BYTES) return ATTN_ERR_UNSUPPORTED;
+    void* scratch = nullptr;
+    if (attn::decode_scratch(&scratch) != hipSuccess) return ATTN_ERR_LAUNCH;
+    float* const part_o = (float*)scratch;
+    float* const part_lse = part_o + slots * (uint64_t)head_dim;
+    dp.part_o = part_o;
+    dp.part_lse = part_lse;
+    cp.part_o = part_o;
+    cp.part_lse = part_lse;
+    const hipStream_t s = (hipStream_t)hip_stream;
+    st = status_of(attn::launch_decode(dp, (int)dtype, head_dim, s));
+    if (st != ATTN_OK) return st;
+    return status_of(attn::launch_combine(cp, (int)dtype, head_dim, s));
 }
 
 }  // extern "C"

@@ -32,7 +32,9 @@
 // cross-section merge (section "Algorithm — running-sum update, reciprocal,
 // output accumulate") over any number of splits.
 #include <algorithm>
+#include <mutex>
 
+#include "attn.h"
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -900,6 +902,40 @@ static hipError_t launch_combine_t(const CombineParams& p, int head_dim, hipStre
 
 hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim, hipStream_t s) {
     return dtype == kBF16 ? launch_combine_t<true>(p, head_dim, s) : launch_combine_t<false>(p, head_dim, s);
+}
+
+// ---------------------------------------------------------------------------- allocation-free decode
+// The split partials of attn_decode_fwd_noalloc live in this file-scope
+// device array: one copy per GPU, held until the process ends, shared by
+// every such call on that GPU (calls that overlap on one GPU race on it).
+// Host code never uses the array's name as an address (in host code it is a
+// stand-in, not device memory): its device address is looked up once per
+// device, with that device current, and passed to the kernels as the
+// partials' pointers, exactly as a caller's workspace would be. Nothing in it
+// needs clearing: the combine reads only the splits the split kernel has just
+// written (those that start below cache_len).
+static __device__ __align__(256) unsigned char scratch[ATTN_DECODE_NOALLOC_MAX_BYTES];
+
+namespace {
+constexpr int kScratchMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kScratchMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** addr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_addr[dev]) {
+        void* a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_addr[dev] = a;
+    }
+    *addr = g_scratch_addr[dev];
+    return hipSuccess;
 }
 
 // Page-table validation (the device-side range check of the page indices).

@@ -79,6 +79,9 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int m
 hipError_t launch_prefill_f8kv(const PrefillParams& p, int dtype, int head_dim, int mask, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim, hipStream_t s);
+// Device address of the allocation-free decode's partials on the current
+// device (ATTN_DECODE_NOALLOC_MAX_BYTES, looked up once per device).
+hipError_t decode_scratch(void** addr);
 hipError_t launch_validate_pages(const uint32_t* block_table, const int32_t* cache_len, int batch,
                                  int max_pages_per_seq, int page_size, int64_t num_pages, int32_t* result,
                                  hipStream_t s);

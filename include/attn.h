@@ -315,6 +315,34 @@ int attn_decode_validate_pages(const uint32_t* block_table, int max_pages_per_se
                                const int32_t* cache_len, int batch, int64_t num_pages, int32_t* result,
                                void* hip_stream);
 
+/*
+ * Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): attn_decode_fwd followed by attn_decode_combine in one call,
+ * writing o [batch, s_active, n_q_heads, head_dim] (`dtype`, o_st strides)
+ * with the same kernels and bit-identical results, but with the split
+ * partials in a device array of the library (ATTN_DECODE_NOALLOC_MAX_BYTES
+ * per GPU, held until the process ends) instead of a caller's workspace.
+ * Arguments are those of attn_decode_fwd (16-bit cache) and
+ * attn_decode_combine. The partials need batch * s_active * n_q_heads *
+ * max_splits * (head_dim + 1) * 4 bytes; more than the maximum returns
+ * ATTN_ERR_UNSUPPORTED before any HIP call (use longer splits, or the
+ * workspace entry points). No call allocates, frees or memsets anything; the
+ * first call on a device looks up the array's address there (the device of
+ * hip_stream must be current). Every call on a GPU shares that GPU's array:
+ * calls that overlap on one GPU (concurrent streams or threads) race and
+ * must be serialised by the caller.
+ */
+#define ATTN_DECODE_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+
+int attn_decode_fwd_noalloc(const void* q, attn_strides q_st,
+                            const void* k_cache, const void* v_cache, attn_strides kv_st,
+                            const uint32_t* block_table, int max_pages_per_seq, int page_size,
+                            const int32_t* cache_len, attn_dtype dtype, int batch, int s_active,
+                            int n_q_heads, int n_kv_heads, int head_dim, float scale, int window,
+                            int split_len, int max_splits, void* o, attn_strides o_st,
+                            void* hip_stream);
+
 /* Bytes of part_o and part_lse that attn_decode_fwd needs. Returns ATTN_OK or ATTN_ERR_INVALID. */
 int attn_decode_workspace_size(int batch, int s_active, int n_q_heads, int head_dim, int max_splits,
                                size_t* part_o_bytes, size_t* part_lse_bytes);

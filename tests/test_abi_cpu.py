@@ -129,6 +129,45 @@ def test_decode_empty_is_noop(kw):
     assert decode(**kw) == 0
 
 
+def decode_noalloc(**kw):
+    a = dict(q=FAKE, qs=st(32 * 128, 32 * 128, 128), k=FAKE, v=FAKE, kvs=st(16 * 8 * 128, 8 * 128, 128), bt=FAKE,
+             maxp=2048, ps=16, cl=FAKE, dtype=A.ATTN_BF16, batch=32, sa=1, hq=32, hkv=8, d=128, scale=0.088, window=0,
+             split=4096, ms=8, o=FAKE, os=st(32 * 128, 32 * 128, 128))
+    a.update(kw)
+    return A.lib().attn_decode_fwd_noalloc(a["q"], a["qs"], a["k"], a["v"], a["kvs"], a["bt"], a["maxp"], a["ps"],
+                                           a["cl"], a["dtype"], a["batch"], a["sa"], a["hq"], a["hkv"], a["d"],
+                                           a["scale"], a["window"], a["split"], a["ms"], a["o"], a["os"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    # the partials of 32 x 32 rows x 64 splits x 129 floats exceed the 32 MiB device array
+    (dict(split=512, ms=64), UNSUPPORTED),
+    (dict(split=4096, ms=8, batch=256), UNSUPPORTED),
+    (dict(split=500), INVALID),
+    (dict(ms=7), INVALID),               # splits do not cover max_pages * page_size
+    (dict(dtype=A.ATTN_F32), UNSUPPORTED),
+    (dict(sa=9), UNSUPPORTED),
+    (dict(o=0), INVALID),
+    (dict(o=FAKE + 4), INVALID),
+    (dict(os=st(3, 128, 128)), INVALID),
+    (dict(cl=0), INVALID),
+    (dict(scale=float("inf")), INVALID),
+])
+def test_decode_noalloc_rejects_before_any_hip_call(kw, status):
+    assert decode_noalloc(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(sa=0), dict(hq=0)])
+def test_decode_noalloc_empty_is_noop(kw):
+    assert decode_noalloc(**kw) == 0
+
+
+def test_decode_noalloc_limit_matches_the_header():
+    hdr = open(os.path.join(ROOT, "include", "attn.h")).read()
+    assert "#define ATTN_DECODE_NOALLOC_MAX_BYTES ((size_t)32 << 20)" in hdr
+    assert A.DECODE_NOALLOC_MAX_BYTES == 32 << 20
+
+
 def combine(**kw):
     a = dict(po=FAKE, pl=FAKE, cl=FAKE, split=512, ms=64, batch=32, sa=1, hq=32, d=128, o=FAKE,
              os=st(32 * 128, 32 * 128, 128), dtype=A.ATTN_BF16)
