@@ -60,15 +60,20 @@ __device__ __forceinline__ int pf_vswz(int row) {
 }
 
 // Q fragments of one lane (B operand of S^T = K Q^T: row l32, d = 16s + 8hf
-// .. +8), read from qrow (already offset by 8 hf); zeros when the row is
-// outside the sequence. qflip flips the sign bits when the scale is negative.
+// .. +8), read from qrow (already offset by 8 hf), which must point at a row
+// of the sequence (callers clamp it); the fragments are zeros when the lane's
+// own row is outside the sequence (valid = false). The loads are unconditional
+// and the zeroing is a mask applied afterwards, so no branch separates the
+// loads and nothing waits for them before the caller's next loads are issued.
+// qflip flips the sign bits when the scale is negative.
 template <int D>
 __device__ __forceinline__ void pf_load_q(s16x8 (&qf)[D / 16], const uint16_t* qrow, bool valid, uint32_t qflip) {
+    const uint32_t keep = valid ? 0xffffffffu : 0u;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (valid) x = *(const uint4*)(qrow + 16 * s);
-        x.x ^= qflip; x.y ^= qflip; x.z ^= qflip; x.w ^= qflip;
+        uint4 x = *(const uint4*)(qrow + 16 * s);
+        x.x = (x.x & keep) ^ qflip; x.y = (x.y & keep) ^ qflip;
+        x.z = (x.z & keep) ^ qflip; x.w = (x.w & keep) ^ qflip;
         qf[s] = __builtin_bit_cast(s16x8, x);
     }
 }
@@ -197,9 +202,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     const int my_pos = pos_of(my_q);
     const int wpos0 = pos_of(wq0), wpos1 = pos_of(wq1);  // positions of the wave's first and last rows
 
+    // Q stays in VGPRs; it is loaded in the prologue, after the first K/V
+    // tiles have been requested, so that both latencies overlap.
     s16x8 qf[D / 16];
-    pf_load_q<D>(qf, (const uint16_t*)p.q + q_at + (int64_t)my_q * p.qs.seq + (int64_t)h * p.qs.head + 8 * hf,
-                 my_q < sq, p.qflip);
+    const uint16_t* qrow = (const uint16_t*)p.q + q_at + (int64_t)min(my_q, sq - 1) * p.qs.seq +
+                           (int64_t)h * p.qs.head + 8 * hf;
 
     const uint16_t* kbase = (const uint16_t*)p.k + k_at + (int64_t)hk * p.ks.head;
     const uint16_t* vbase = (const uint16_t*)p.v + v_at + (int64_t)hk * p.vs.head;
@@ -540,6 +547,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
         load_k_tile(Ks0, j_begin);
         load_v_tile(Vs0, j_begin);
         load_k_tile(Ks1, min(j_begin + 1, j_last));
+        pf_load_q<D>(qf, qrow, my_q < sq, p.qflip);
         wait_vmcnt<0>();
         __syncthreads();
         qk_tile(sa0, sa1, Ks0);
@@ -572,6 +580,363 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
         pf_store_lse(&p.lse[(lse_at + my_q) * p.n_q_heads + h], m_fin, l_tot, nan_row);
     if (wave_live && my_q < sq)
         pf_store_o<BF16, NDT>(o, inv, (uint16_t*)p.o + o_at + (int64_t)my_q * p.os.seq + (int64_t)h * p.os.head, hf,
+                              nan_row);
+}
+
+// ---------------------------------------------------------------------------- D = 256, paired waves
+// prefill_pair: head_dim 256 at two waves per SIMD. A 32-row wave holding all
+// of Q and O for 256 dims needs about 460 registers, which leaves one wave per
+// SIMD and every stall exposed. Here the two waves of a pair share 32 query
+// rows and split the work of each 64-key tile: wave half h computes the scores
+// of keys 32h .. 32h+31 over all 256 dims (Q resident in full) and the output
+// for dims 128h .. 128h+127 (that half of O resident). The pair exchanges its
+// rows' tile maxima and its probabilities through LDS, so both waves run the
+// same online softmax (the same m, the same rescale decisions, the same row
+// sums over all 64 keys, in prefill_mfma's order) and each multiplies the
+// tile's 64 probabilities into its half of V. Each wave needs about 230
+// registers: eight waves (four pairs, 128 rows) per workgroup, two per SIMD.
+// The arithmetic per row is prefill_mfma's, step for step, so the results are
+// the same bits.
+template <bool BF16, int MASK>
+__global__ __launch_bounds__(512, 1) void prefill_pair(PrefillParams p) {
+    constexpr int D = 256;
+    constexpr int NW = 8;
+    constexpr int PF_BM = 128;              // four pairs of 32 rows
+    constexpr int PF_THREADS = 64 * NW;
+    constexpr int CPR = D / 8;              // 16-byte chunks per row
+    constexpr int TILE = PF_BN * D;
+    constexpr int LPW = TILE / 512 / NW;    // 1 KB direct loads per wave per tile
+    constexpr int NS = D / 16;              // k-steps of the score MFMAs
+    constexpr int NDH = 4;                  // 32-wide d tiles in a wave's half of O^T
+    constexpr int NPV = 4 * NDH;            // P V MFMAs per tile
+    constexpr int VPRE = 4;                 // P V MFMAs whose fragments are in flight
+    static_assert(LPW == 4 && NS % LPW == 0 && NPV % LPW == 0, "four direct loads per wave and tile");
+    __shared__ __attribute__((aligned(16))) uint16_t Ks0[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks1[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs0[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs1[TILE];
+    // Exchange between the waves of a pair: probabilities [pair][half][two
+    // 16-byte chunks][lane] (a lane's 8 packed pairs), row maxima [pair][half][row].
+    __shared__ __attribute__((aligned(16))) uint4 Xp[4][2][2][64];
+    __shared__ float Xm[4][2][32];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pr = w & 3;       // pair: rows 32 pr .. 32 pr + 31 of the tile
+    const int hh = w >> 2;      // half: keys 32 hh .. of each tile, dims 128 hh .. of O
+    const int l32 = lane & 31;
+    const int hf = lane >> 5;
+    const int g = lane >> 4;
+    const int r16 = lane & 15;
+
+    // Workgroup -> (q tile, batch, q-head) as in prefill_mfma.
+    const int nbh = p.batch * p.n_q_heads;
+    int wid = (int)blockIdx.x;
+    if (p.xcd_chunks) {
+        const int G = p.group, round = 8 * G;
+        const int full = ((int)gridDim.x / round) * round;
+        if (wid < full) {
+            const int xcd = wid & 7, k = wid >> 3;
+            wid = ((k / G) * 8 + xcd) * G + k % G;
+        }
+    }
+    const int qt = p.n_q_tiles - 1 - wid / nbh;
+    const int bh = wid % nbh;
+    const int b = bh / p.n_q_heads;
+    const int h = bh % p.n_q_heads;
+    const int hk = h / p.group;
+
+    int sq = p.seqlen_q, skv = p.seqlen_kv;
+    int64_t q_at = (int64_t)b * p.qs.batch, k_at = (int64_t)b * p.ks.batch, v_at = (int64_t)b * p.vs.batch,
+            o_at = (int64_t)b * p.os.batch, lse_at = (int64_t)b * p.seqlen_q;
+    if (p.cu_seqlens_q) {
+        const int qs0 = p.cu_seqlens_q[b], ks0 = p.cu_seqlens_kv[b];
+        sq = min(p.cu_seqlens_q[b + 1] - qs0, p.seqlen_q);
+        skv = p.cu_seqlens_kv[b + 1] - ks0;
+        q_at = (int64_t)qs0 * p.qs.seq;
+        o_at = (int64_t)qs0 * p.os.seq;
+        lse_at = qs0;
+        k_at = (int64_t)ks0 * p.ks.seq;
+        v_at = (int64_t)ks0 * p.vs.seq;
+    }
+    const int off = skv - sq;
+    const int q0 = qt * PF_BM;
+    if (q0 >= sq) return;  // a tile past this sequence's end (packed sequences only; uniform)
+    const int qlast = min(q0 + PF_BM, sq) - 1;
+    auto pos_of = [&](int i) -> int { return p.positions ? p.positions[lse_at + min(i, sq - 1)] : i + off; };
+    int kv_lo = 0, kv_hi = skv;
+    if (MASK >= kMaskCausal) kv_hi = min(kv_hi, pos_of(qlast) + 1);
+    if (MASK == kMaskCausalWindow) kv_lo = max(0, pos_of(q0) - p.window + 1);
+    const int j_begin = kv_lo / PF_BN;
+    const int j_end = kv_hi > kv_lo ? (kv_hi + PF_BN - 1) / PF_BN : j_begin;
+
+    const int wq0 = q0 + 32 * pr;
+    const int wq1 = min(wq0 + 31, sq - 1);
+    const bool wave_live = wq0 < sq;
+    const int my_q = wq0 + l32;
+    const int my_pos = pos_of(my_q);
+    const int wpos0 = pos_of(wq0), wpos1 = pos_of(wq1);
+
+    // Q (loaded in the prologue, after the first K/V tiles have been requested)
+    s16x8 qf[NS];
+    const uint16_t* qrow = (const uint16_t*)p.q + q_at + (int64_t)min(my_q, sq - 1) * p.qs.seq +
+                           (int64_t)h * p.qs.head + 8 * hf;
+
+    const uint16_t* kbase = (const uint16_t*)p.k + k_at + (int64_t)hk * p.ks.head;
+    const uint16_t* vbase = (const uint16_t*)p.v + v_at + (int64_t)hk * p.vs.head;
+    // K/V tiles: the direct-to-LDS staging of prefill_mfma (eight waves load a
+    // tile together; rows outside [kv_lo, seqlen_kv) are clamped copies).
+    const int key_min = kv_lo, key_max = skv - 1;
+    constexpr int RPL = 64 / CPR;
+    const int lrow = lane / CPR, lcs = lane % CPR;
+    const uint32_t kx = 16u * (uint32_t)(lcs ^ lrow);
+    const uint32_t vx = 16u * (uint32_t)(lcs ^ (4 * lrow));
+    const uint32_t kl = 2u * (uint32_t)lrow * (uint32_t)p.ks.seq, vl = 2u * (uint32_t)lrow * (uint32_t)p.vs.seq;
+    auto load_tile_impl = [&](uint16_t* dst, const uint16_t* base, int64_t seq, int j, uint32_t lane_row_off,
+                              uint32_t lane_chunk_off, bool is_k) __attribute__((always_inline)) {
+        const int kv0 = j * PF_BN;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kv0 * seq), (short)0, 0x7fffffff, 0x00020000);
+        if (kv0 >= key_min && kv0 + PF_BN - 1 <= key_max) {
+#pragma unroll
+            for (int ii = 0; ii < LPW; ++ii) {
+                const int i = w * LPW + ii;
+                const uint32_t u = is_k ? (2 * i) & 15 : 4 * ((2 * i) & 3);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 512 * i), 16,
+                                                         lane_row_off + (lane_chunk_off ^ (16u * u)),
+                                                         (uint32_t)(2 * RPL * i) * (uint32_t)seq, 0, 0);
+            }
+        } else {
+            int lr = lrow;
+            asm volatile("" : "+v"(lr));
+#pragma unroll
+            for (int ii = 0; ii < LPW; ++ii) {
+                const int i = w * LPW + ii;
+                const int row = RPL * i + lr, cs = lcs;
+                const int key = min(max(kv0 + row, key_min), key_max);
+                const int c = cs ^ (is_k ? pf_kswz<D>(row) : pf_vswz<D>(row));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 512 * i), 16,
+                                                         2u * ((uint32_t)(key - kv0) * (uint32_t)seq + 8u * c), 0, 0, 0);
+            }
+        }
+    };
+    auto load_k_tile = [&](uint16_t* dst, int j) __attribute__((always_inline)) { load_tile_impl(dst, kbase, p.ks.seq, j, kl, kx, true); };
+    auto load_v_tile = [&](uint16_t* dst, int j) __attribute__((always_inline)) { load_tile_impl(dst, vbase, p.vs.seq, j, vl, vx, false); };
+    uint32_t kvo[LPW], vvo[LPW];
+#pragma unroll
+    for (int ii = 0; ii < LPW; ++ii) {
+        const int i = w * LPW + ii;
+        const uint32_t uk = (2 * i) & 15;
+        const uint32_t uv = 4 * ((2 * i) & 3);
+        uint32_t ko = kl + (kx ^ (16u * uk)) + (uint32_t)(2 * RPL * i) * (uint32_t)p.ks.seq;
+        uint32_t vo = vl + (vx ^ (16u * uv)) + (uint32_t)(2 * RPL * i) * (uint32_t)p.vs.seq;
+        asm volatile("" : "+v"(ko), "+v"(vo));
+        kvo[ii] = ko;
+        vvo[ii] = vo;
+    }
+    auto tile_rsrc = [&](const uint16_t* base, int64_t seq, int j) __attribute__((always_inline)) {
+        const int kv0 = j * PF_BN;
+        const uint32_t nrec =
+            kv0 + PF_BN - 1 <= key_max ? 0x7fffffffu : 2u * ((uint32_t)(key_max - kv0) * (uint32_t)seq + (uint32_t)D);
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kv0 * seq), (short)0, nrec, 0x00020000);
+    };
+    auto load_part = [&](uint16_t* dst, __amdgpu_buffer_rsrc_t rs, uint32_t voff, int ii) __attribute__((always_inline)) {
+        const int i = w * LPW + ii;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 512 * i), 16, voff, 0, 0, 0);
+    };
+
+    constexpr float kLazyRescale = 8.0f;
+    float m_i = kMaxInit, l_i = 0.f;
+    f32x16 o[NDH];
+#pragma unroll
+    for (int dt = 0; dt < NDH; ++dt) o[dt] = f32x16{};
+    const uint32_t one2 = BF16 ? 0x3F803F80u : 0x3C003C00u;
+
+    auto tile_full = [&](int j) __attribute__((always_inline)) {
+        const int kv0 = j * PF_BN;
+        bool f = kv0 + PF_BN <= skv;
+        if (MASK >= kMaskCausal) f &= kv0 + PF_BN - 1 <= wpos0;
+        if (MASK == kMaskCausalWindow) f &= kv0 >= wpos1 - p.window + 1;
+        return f;
+    };
+    // Fragment offsets: this wave's 32-key block of K starts 32 rows into the
+    // tile; its half of V^T is d tiles 4 hh .. 4 hh + 3 (chunk XOR 16 hh).
+    const uint32_t kfrag = ((uint32_t)(l32 * D * 2) | (16u * (uint32_t)(hf ^ pf_kswz<D>(l32)))) + (uint32_t)hh * (32u * D * 2);
+    const int vr0 = 4 * hf + (r16 >> 2);
+    const int vcl = 2 * (g & 1) + ((r16 & 3) >> 1);
+    const uint32_t vfrag = ((uint32_t)(vr0 * D * 2) | (16u * (uint32_t)(vcl ^ pf_vswz<D>(vr0))) | (8u * (r16 & 1))) ^
+                           (256u * (uint32_t)hh);
+    auto opaque = [](uint32_t x) __attribute__((always_inline)) {
+        asm volatile("" : "+v"(x));
+        return x;
+    };
+    auto lds_frag8 = [](const uint16_t* base, uint32_t byte_off) __attribute__((always_inline)) {
+        return *(const s16x8*)((const char*)base + byte_off);
+    };
+    int key_hi = skv - 1, key_lo = 0;
+    if (MASK >= kMaskCausal) key_hi = min(key_hi, my_pos);
+    if (MASK == kMaskCausalWindow) key_lo = max(key_lo, my_pos - p.window + 1);
+    const bool none_visible = key_hi < key_lo;
+    const uint32_t key_span = none_visible ? 0u : (uint32_t)(key_hi - key_lo);
+    if (none_visible) key_lo = INT_MIN / 2;
+    // this wave's block of a tile: keys kv0 + 32 hh + 8 (r / 4) + 4 hf + r % 4 in register r
+    auto mask_block = [&](f32x16& sacc, int kv0) __attribute__((always_inline)) {
+        const int base = kv0 + 32 * hh + 4 * hf - key_lo;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint32_t d = (uint32_t)(base + 8 * (r >> 2) + (r & 3));
+            sacc[r] = d <= key_span ? sacc[r] : kMaskedScore;
+        }
+    };
+    auto max_block = [&](const f32x16& s) __attribute__((always_inline)) {
+        float mx = kMaskedScore;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[r], s[r + 1]);
+        return max_with_other_half(mx);
+    };
+    auto rescale = [&](float mx) __attribute__((always_inline)) {
+        const float m_cand = mx * p.c;
+        const bool grow = m_cand > m_i + kLazyRescale;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float m_new = grow ? m_cand : m_i;
+            const float alpha = fast_exp2(m_i - m_new);
+            m_i = m_new;
+            l_i *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDH; ++dt) o[dt] *= alpha;
+        }
+    };
+    // The pair's tile max: this wave's (masked) block max against its partner's.
+    auto exchange_max = [&](float mx) __attribute__((always_inline)) {
+        if (hf == 0) Xm[pr][hh][l32] = mx;
+        return mx;
+    };
+
+    // Step j (as prefill_mfma's): the score MFMAs of tile j+1 (this wave's
+    // block) beside the exponentials of tile j; this wave's probabilities go to
+    // LDS; a barrier (which also publishes V(j)); both halves' probabilities
+    // are read back in order; the P V MFMAs of tile j into this wave's half of
+    // O beside the raw row max of tile j+1; the row sums of all 64
+    // probabilities; the tile max of j+1 goes to LDS; a barrier (K(j+2) in);
+    // the partner's max settles m for tile j+1. Loads: V(j+1) in the first
+    // part, K(j+3) in the second, as in prefill_mfma.
+    const int j_last = j_end - 1;
+    auto step = [&](int j, f32x16& c, f32x16& n, uint16_t* Kn, uint16_t* Vc, uint16_t* Vl) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(vbase, p.vs.seq, min(j + 1, j_last));
+        const uint32_t kf = opaque(kfrag);
+        const uint32_t vf = opaque(vfrag);
+        s16x8 ka[NS];
+        s16x8 vb[NPV];
+        uint32_t pk[8];
+        auto kread = [&](int s) __attribute__((always_inline)) { ka[s] = lds_frag8(Kn, kf ^ (32u * s)); };
+        auto vread = [&](int i) __attribute__((always_inline)) {
+            const int u = i / NDH, dt = i % NDH;
+            const char* vb0 = (const char*)Vc + (vf ^ (64u * dt));
+            vb[i] = concat4(lds_read_tr16((const uint16_t*)(vb0 + 2 * D * (16 * u))),
+                            lds_read_tr16((const uint16_t*)(vb0 + 2 * D * (16 * u + 8))));
+        };
+        const float neg_m = -m_i;
+        auto prob_pair = [&](int i) __attribute__((always_inline)) {
+            pk[i] = pack2_16<BF16>(fast_exp2(fmaf(c[2 * i], p.c, neg_m)), fast_exp2(fmaf(c[2 * i + 1], p.c, neg_m)));
+            asm volatile("" ::"v"(pk[i]));
+        };
+        kread(0);
+        kread(1);
+        sched_fence();
+        n = f32x16{};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            n = mfma32x32x16<BF16>(ka[s], qf[s], n);
+            if (s % (NS / LPW) == 0) load_part(Vl, vrs, vvo[s / (NS / LPW)], s / (NS / LPW));
+            if (s + 2 < NS) kread(s + 2);
+            if (s % 2 == 1) prob_pair(s / 2);
+            sched_fence();
+        }
+        Xp[pr][hh][0][lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        Xp[pr][hh][1][lane] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+        // V(j) in; both halves' P(j) written; every wave is past its reads of K(j+1).
+        wait_vmcnt<2 * LPW>();
+        barrier_lds();
+        const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kbase, p.ks.seq, min(j + 3, j_last));
+        uint4 pq[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pq[e] = Xp[pr][e >> 1][e & 1][lane];
+#pragma unroll
+        for (int i = 0; i < VPRE; ++i) vread(i);
+        sched_fence();
+        float mx = kMaskedScore;
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            const int u = i / NDH, dt = i % NDH;
+            o[dt] = mfma32x32x16<BF16>(vb[i], __builtin_bit_cast(s16x8, pq[u]), o[dt]);
+            if (i % (NPV / LPW) == 0) load_part(Kn, krs, kvo[i / (NPV / LPW)], i / (NPV / LPW));
+            if (i + VPRE < NPV) vread(i + VPRE);
+            if (i % 2 == 0) mx = max3f(mx, n[i], n[i + 1]);
+            sched_fence();
+        }
+        // row sums of the tile's 64 probabilities, in prefill_mfma's order
+        const uint32_t* pw = (const uint32_t*)pq;
+        float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+            ps0 = dot2_16<BF16>(pw[e], one2, ps0);
+            ps1 = dot2_16<BF16>(pw[e + 1], one2, ps1);
+        }
+        l_i += ps0 + ps1;
+        mx = max_with_other_half(mx);
+        if (!(wave_live && tile_full(j + 1))) {
+            mask_block(n, (j + 1) * PF_BN);
+            mx = fminf(mx, max_block(n));
+        }
+        exchange_max(mx);
+        // K(j+2) in; both halves' tile maxima written; every wave is past its reads of V(j).
+        wait_vmcnt<2 * LPW>();
+        barrier_lds();
+        rescale(fmaxf(mx, Xm[pr][hh ^ 1][l32]));
+    };
+
+    f32x16 sa, sb;
+    const int nt = j_end - j_begin;
+    if (nt > 0) {
+        // The first refill of Vs1 may be range-limited: start it from zeros.
+#pragma unroll
+        for (int c = tid; c < TILE / 8; c += PF_THREADS) *(uint4*)(Vs1 + 8 * c) = make_uint4(0, 0, 0, 0);
+        load_k_tile(Ks0, j_begin);
+        load_v_tile(Vs0, j_begin);
+        load_k_tile(Ks1, min(j_begin + 1, j_last));
+        pf_load_q<D>(qf, qrow, my_q < sq, p.qflip);
+        wait_vmcnt<0>();
+        __syncthreads();
+        {
+            const uint32_t kf = opaque(kfrag);
+            sa = f32x16{};
+#pragma unroll
+            for (int s = 0; s < NS; ++s) sa = mfma32x32x16<BF16>(lds_frag8(Ks0, kf ^ (32u * s)), qf[s], sa);
+        }
+        if (!(wave_live && tile_full(j_begin))) mask_block(sa, j_begin * PF_BN);
+        const float mx = exchange_max(max_block(sa));
+        __syncthreads();  // the tile maxima are written; every wave is past its reads of K(j_begin)
+        rescale(fmaxf(mx, Xm[pr][hh ^ 1][l32]));
+        load_k_tile(Ks0, min(j_begin + 2, j_last));
+    }
+    for (int r = 0; r < nt; r += 2) {
+        step(j_begin + r, sa, sb, Ks1, Vs0, Vs1);
+        if (r + 1 < nt) step(j_begin + r + 1, sb, sa, Ks0, Vs1, Vs0);
+    }
+    wait_vmcnt<0>();
+
+    float l_tot = sum_with_other_half(l_i);
+    float m_fin = m_i;
+    const float sink = p.sinks ? p.sinks[h] : -__builtin_inff();
+    const bool nan_row = sink_gives_nan(sink);
+    const float osc = p.sinks ? fold_sink(sink * kLog2e, m_fin, l_tot) : 1.f;
+    const float inv = l_tot > 0.f ? osc / l_tot : 0.f;
+    if (p.lse && hh == 0 && hf == 0 && wave_live && my_q < sq)
+        pf_store_lse(&p.lse[(lse_at + my_q) * p.n_q_heads + h], m_fin, l_tot, nan_row);
+    if (wave_live && my_q < sq)
+        pf_store_o<BF16, NDH>(o, inv,
+                              (uint16_t*)p.o + o_at + (int64_t)my_q * p.os.seq + (int64_t)h * p.os.head + 128 * hh, hf,
                               nan_row);
 }
 
@@ -633,9 +998,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     const int my_pos = my_q + off;
     const int wpos0 = wq0 + off, wpos1 = wq1 + off;
 
+    // Q: loaded after the first K/V tile has been requested (the row is clamped
+    // into the sequence; rows past it are zeroed)
     s16x8 qf[D / 16];
-    pf_load_q<D>(qf, (const uint16_t*)p.q + (int64_t)b * p.qs.batch + (int64_t)my_q * p.qs.seq + (int64_t)h * p.qs.head + 8 * hf,
-                 my_q < sq, p.qflip);
+    const uint16_t* qrow = (const uint16_t*)p.q + (int64_t)b * p.qs.batch + (int64_t)min(my_q, sq - 1) * p.qs.seq +
+                           (int64_t)h * p.qs.head + 8 * hf;
 
     // Tile staging. Thread chunk c = tid + NT i covers codes 16 (c % CH8) ..
     // +16 of tile row c / CH8; rows outside [kv_lo, skv) read the nearest valid
@@ -784,6 +1151,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
 
     if (j_end > j_begin) {
         fetch(j_begin);
+        pf_load_q<D>(qf, qrow, my_q < sq, p.qflip);
         store(0);
         __syncthreads();
         for (int j = j_begin; j < j_end; ++j) {
@@ -964,8 +1332,21 @@ static hipError_t launch_mfma_nw(PrefillParams p, int mask, hipStream_t s) {
 // halve that waste (measured 8% faster on 16 prompts of 256..4096 tokens).
 constexpr int kPrefillWideMinWorkgroups = 512;
 
+template <bool BF16>
+static hipError_t launch_pair(PrefillParams p, int mask, hipStream_t s) {
+    p.n_q_tiles = (p.seqlen_q + 127) / 128;
+    const dim3 grid((unsigned)p.n_q_tiles * p.batch * p.n_q_heads), block(512);
+    switch (mask) {
+        case kMaskNone: hipLaunchKernelGGL((prefill_pair<BF16, kMaskNone>), grid, block, 0, s, p); break;
+        case kMaskCausal: hipLaunchKernelGGL((prefill_pair<BF16, kMaskCausal>), grid, block, 0, s, p); break;
+        default: hipLaunchKernelGGL((prefill_pair<BF16, kMaskCausalWindow>), grid, block, 0, s, p); break;
+    }
+    return hipGetLastError();
+}
+
 template <bool BF16, int D>
 static hipError_t launch_mfma_mask(PrefillParams p, int mask, hipStream_t s) {
+    if constexpr (D == 256) return launch_pair<BF16>(p, mask, s);
     if constexpr (D <= 128) {
         if (p.cu_seqlens_q) return launch_mfma_nw<BF16, D, 4>(p, mask, s);
         const long wide = (long)((p.seqlen_q + 255) / 256) * p.batch * p.n_q_heads;
