@@ -181,30 +181,107 @@ def calibrate_copy():
     print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
 
 
-def cpu_baseline(inp, seconds_target: float = 15.0):
-    """The fp64 oracle, timed on a bounded random sample of the prefill's rows."""
+def cpu_threads() -> int:
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo) and its logical CPU count."""
+    name = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                name = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return f"{name}, {os.cpu_count()} logical CPUs"
+
+
+def row_pairs(spec, rows) -> float:
+    """Visible (query, key) pairs of the given rows (b, i, h) under the spec's mask."""
+    pos = rows[:, 1] + (spec.seqlen_kv - spec.seqlen_q)
+    hi = np.minimum(spec.seqlen_kv - 1, pos) if spec.causal else np.full_like(pos, spec.seqlen_kv - 1)
+    lo = np.maximum(0, pos - spec.window + 1) if spec.window > 0 else np.zeros_like(pos)
+    return float(np.maximum(0, hi - lo + 1).sum())
+
+
+def cpu_baseline(inp, seconds_target: float = 15.0, what: str = "the 32768-token causal prefill"):
+    """The fp64 oracle, timed on a bounded random sample of a prefill workload's query rows
+    (the whole workload when it takes less than the target)."""
     import oracle
     from flash_attention_forward_amd import workloads as W
 
     s = inp.spec
     q, k, v = W.as_f64(inp.q, s.dtype), W.as_f64(inp.k, s.dtype), W.as_f64(inp.v, s.dtype)
     rng = np.random.default_rng(0)
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    total = s.batch * s.seqlen_q * s.n_q_heads
 
     def run(n):
-        rows = np.stack([np.zeros(n, np.int64), rng.integers(0, s.seqlen_q, n), rng.integers(0, s.n_q_heads, n)], 1)
+        if n >= total:
+            rows = oracle.all_rows(s.batch, s.seqlen_q, s.n_q_heads)
+        else:
+            rows = np.stack([rng.integers(0, s.batch, n), rng.integers(0, s.seqlen_q, n),
+                             rng.integers(0, s.n_q_heads, n)], 1)
         t = time.perf_counter()
         oracle.attention_rows(q, k, v, s.scale_f32, s.causal, s.window, rows)
         dt = time.perf_counter() - t
-        pairs = (rows[:, 1] + 1 + (s.seqlen_kv - s.seqlen_q)).clip(0, s.seqlen_kv).sum()  # causal rows, no window
-        return n, dt, 4.0 * s.head_dim * float(pairs)
+        return len(rows), dt, 4.0 * s.head_dim * row_pairs(s, rows)
 
-    n, dt, fl = run(256)
-    n2 = int(min(200000, max(256, n * seconds_target / max(dt, 1e-3))))
-    n, dt, fl = run(n2)
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} random query rows of the 32768-token causal prefill (all keys each row sees), "
-                      f"{dt:.1f} s wall, fp64, OpenMP over rows"}
+    n, dt, fl = run(min(256, total))
+    if n < total:
+        n, dt, fl = run(int(min(total, 200000, max(256, n * seconds_target / max(dt, 1e-3)))))
+    sample = "all" if n >= total else f"{n} random"
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cpu_threads(), "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{sample} query rows of {what} (all keys each row sees), {dt:.1f} s wall, fp64, OpenMP over rows"}
+
+
+def parity_prefill(spec, inp, got_t, n_random: int = 240) -> dict:
+    """The timed prefill output against the fp64 oracle on sampled rows (tile and sequence edges of
+    every head plus random rows; every row for the fp32 workload): the benchmark spec's tolerances, the
+    per-row normwise relative error and the ratio to the per-element error bound of the kernels'
+    arithmetic (tests/gpu_common.derived_bound)."""
+    import oracle
+    from flash_attention_forward_amd import workloads as W
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import gpu_common as G
+
+    got = W.as_f64(W.from_torch(got_t, spec.dtype), spec.dtype)
+    q, k, v = W.as_f64(inp.q, spec.dtype), W.as_f64(inp.k, spec.dtype), W.as_f64(inp.v, spec.dtype)
+    if spec.dtype == "f32":
+        ref = oracle.attention(q, k, v, spec.scale_f32, spec.causal, spec.window)
+        err = np.abs(got - ref).max() / np.abs(ref).max()
+        return {"rows": int(np.prod(got.shape[:3])), "normwise_rel": float(err), "gate": G.F32_NORMWISE,
+                "pass": bool(err <= G.F32_NORMWISE)}
+    rows = G.sample_rows(spec, n_random=n_random, seed=3)
+    ref, bound = G.attention_with_bound(q, k, v, spec.scale_f32, spec.causal, spec.window, spec.dtype, rows=rows)
+    sel = got[rows[:, 0], rows[:, 1], rows[:, 2]]
+    return parity_record(sel, ref, bound, len(rows))
+
+
+def parity_record(sel, ref, bound, nrows) -> dict:
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import gpu_common as G
+
+    err = np.abs(sel - ref)
+    ratio = float(np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0)).max())
+    mx, mean = float(err.max()), float(err.mean())
+    ok = bool(np.isfinite(sel).all() and mx <= G.LOWP_MAX_ABS and mean <= G.LOWP_MEAN_ABS and ratio <= 1.0)
+    return {"rows": int(nrows), "max_abs": mx, "mean_abs": mean,
+            "row_normwise_max": float(G.row_normwise(sel, ref).max()), "bound_ratio_max": ratio, "pass": ok}
+
+
+def parity_decode(inp, got_t, batches) -> dict:
+    """The timed decode output against the fp64 oracle on the given sequences (as parity_prefill)."""
+    from flash_attention_forward_amd import workloads as W
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import gpu_common as G
+
+    got = W.as_f64(W.from_torch(got_t, inp.spec.dtype), inp.spec.dtype)[batches]
+    ref, bound = G.decode_with_bound(inp, batches=batches)
+    return dict(parity_record(got, ref, bound, got.shape[0] * got.shape[1] * got.shape[2]), sequences=list(batches))
 
 
 def cpu_baseline_decode(inp):
@@ -220,8 +297,8 @@ def cpu_baseline_decode(inp):
                   batches=batches, to_f64=f64)
     dt = time.perf_counter() - t
     nbytes = int(inp.cache_len[batches].astype(np.int64).sum()) * s.n_kv_heads * s.head_dim * 2 * 2
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
-            "kind": "oracle", "sample": f"sequences {batches} of the paged decode (gather + fp64 attention), {dt:.1f} s"}
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cpu_threads(), "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"sequences {batches} of the paged decode (gather + fp64 attention), {dt:.1f} s"}
 
 
 def main():
@@ -327,6 +404,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # the outputs of the last timed step, checked against the oracle in the CPU leg below
+    o_timed, do_timed = o.cpu(), do.cpu()
     pre_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     split_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     comb_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
@@ -342,6 +421,7 @@ def main():
         e[1].record(stream)
     torch.cuda.synchronize()
     ctx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in cev]))
+    co_timed = co.cpu()
 
     # sliding window over D = 256 (bf16, B2, 16/8 heads, 8192 tokens, window 1024): 20 back-to-back launches
     wspec = W.WORKLOADS[SWA]
@@ -358,7 +438,8 @@ def main():
     torch.cuda.synchronize()
     swa_ms = wev[0].elapsed_time(wev[1]) / 20
     swa_flops = prefill_flops(wspec)
-    del wq, wk, wv, wo, win
+    wo_timed = wo.cpu()
+    del wq, wk, wv, wo
 
     # the 32K causal workload with K and V stored as FP8 E4M3 (attn_prefill_fwd_fp8kv): 10 back-to-back launches
     fks, fvs = W.FP8_PREFILL_SCALES
@@ -621,9 +702,40 @@ def main():
         "kernel_source_digest": kernel_source_digest(),
     }
     if not args.no_cpu_baseline:
+        # the fp32 workload (correctness only: 1.7e7 FLOP), run once for its parity line
+        fspec = W.WORKLOADS["fp32_d64_s256"]
+        fin = W.make_prefill(fspec, W.WORKLOAD_SEEDS["fp32_d64_s256"])
+        fo = F.prefill(*(W.to_torch(a, "f32", dev) for a in (fin.q, fin.k, fin.v)), scale=fspec.scale_f32,
+                       causal=fspec.causal)
+        fo_timed = fo.cpu()
         log("cpu baseline (oracle)")
-        line["cpu_baseline"] = cpu_baseline(pin)
+        line["cpu_model"] = cpu_model()
+        line["cpu_baseline"] = cpu_baseline(pin, seconds_target=10.0)
         line["cpu_baseline_decode"] = cpu_baseline_decode(din)
+        line["cpu_baselines"] = {
+            "fp32_d64_s256": cpu_baseline(fin, 3.0, "the fp32 256-token workload"),
+            CONTEXT: cpu_baseline(cin, 3.0, "the 7B-shaped 2K f16 causal prefill"),
+            PREFILL: line["cpu_baseline"],
+            SWA: cpu_baseline(win, 3.0, "the D = 256 window-1024 prefill"),
+            DECODE: line["cpu_baseline_decode"],
+            "note": "the fp64 oracle on the box's host cores; value in each workload's unit (TFLOP/s over the "
+                    "sampled rows' visible pairs, GB/s over the sampled sequences' K/V bytes)",
+        }
+        log("parity of the timed outputs (oracle)")
+        order = np.argsort(din.cache_len)
+        dec_rows = sorted({int(order[0]), int(order[1]), int(order[-1]), int(order[-2]), int(order[len(order) // 2]),
+                           3, 17, 29})
+        line["parity"] = {
+            "fp32_d64_s256": parity_prefill(fspec, fin, fo_timed),
+            CONTEXT: parity_prefill(cspec, cin, co_timed),
+            PREFILL: parity_prefill(pspec, pin, o_timed),
+            SWA: parity_prefill(wspec, win, wo_timed),
+            DECODE: parity_decode(din, do_timed, dec_rows),
+            "note": "outputs of the timed launches against the fp64 oracle on sampled rows (tile and sequence "
+                    "edges of every head plus random rows; every row of the fp32 workload; 8 whole sequences of "
+                    "the decode): north-star tolerances (max-abs 2e-2, mean-abs 2e-3; fp32 normwise 1e-5) and "
+                    "the per-element bound of the kernels' arithmetic (bound_ratio_max <= 1)",
+        }
     print(json.dumps(line), flush=True)
 
 

@@ -1,6 +1,7 @@
 """Mask index logic of the prefill, bit-exact, on the launch shapes the full-size
 workloads take: the eight-wave 256-row launch (D = 64 and 128, with and without
-the kv-head chunking across XCDs), the four-wave launch at D = 64, 128 and 256,
+the kv-head chunking across XCDs), the four-wave launch at D = 64 and 128, the
+paired-wave D = 256 launch,
 causal and sliding-window masks, Sq < Skv, packed sequences and FP8 K/V.
 
 * Masked-key poison inside loaded tiles. Keys above a cut (causal) and below a
@@ -38,11 +39,14 @@ LAUNCHES = {
     "wave8_d128_gqa_xcd_4k": W.PrefillSpec(4, 8, 2, 4096, 4096, 128, "bf16", causal=True),
     "wave8_d128_f16_window_4k": W.PrefillSpec(2, 16, 4, 4096, 4096, 128, "f16", causal=True, window=1000),
     "wave8_d64_f16_window_4k": W.PrefillSpec(2, 16, 2, 4096, 4096, 64, "f16", causal=True, window=300),
-    # the D = 256 sliding-window launch (four waves, one workgroup per CU)
+    # the D = 256 sliding-window launch (paired waves, one workgroup per CU)
     "wave4_d256_window": W.PrefillSpec(2, 4, 2, 1500, 1500, 256, "bf16", causal=True, window=333),
     "wave4_d256_f16_causal": W.PrefillSpec(1, 2, 1, 900, 900, 256, "f16", causal=True),
     "wave4_d64_f16_causal": W.PrefillSpec(1, 4, 1, 700, 700, 64, "f16", causal=True),
     "wave4_d128_window_sq_lt_skv": W.PrefillSpec(2, 4, 2, 400, 900, 128, "bf16", causal=True, window=200),
+    # the four-wave launch of the 2K f16 prefill (one round of causal row tiles), and D64 with a window
+    "wave4_f16_gqa_causal_2k": W.PrefillSpec(1, 8, 2, 2048, 2048, 128, "f16", causal=True),
+    "wave4_bf16_d64_window_1k": W.PrefillSpec(2, 4, 2, 1200, 1200, 64, "bf16", causal=True, window=400),
 }
 
 

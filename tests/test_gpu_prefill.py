@@ -34,6 +34,11 @@ SMALL = {
     "wide_f16_d64_window": W.PrefillSpec(32, 8, 4, 290, 290, 64, "f16", causal=True, window=100),
     "wide_bf16_nocausal_sq_lt_skv": W.PrefillSpec(128, 4, 1, 200, 330, 128, "bf16", causal=False),
     "wide_bf16_sq_lt_skv_window": W.PrefillSpec(64, 8, 8, 130, 400, 128, "bf16", causal=True, window=90),
+    # longer rows (9 to 12 row tiles, up to 24 key tiles per row tile)
+    "long_f16_gqa_causal_ragged": W.PrefillSpec(1, 8, 2, 1100, 1100, 128, "f16", causal=True),
+    "long_bf16_d64_window": W.PrefillSpec(2, 4, 1, 1500, 1500, 64, "bf16", causal=True, window=700),
+    "long_bf16_sq_lt_skv": W.PrefillSpec(1, 4, 2, 1030, 1300, 128, "bf16", causal=True),
+    "long_bf16_sq_gt_skv": W.PrefillSpec(1, 2, 1, 1100, 700, 128, "bf16", causal=True),  # first rows see nothing
 }
 
 
