@@ -116,12 +116,17 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     constexpr int LPW = TILE / 512 / NW;    // 1 KB direct loads per wave per tile
     static_assert(LPW >= 1, "every wave loads part of each tile");
     constexpr int NDT = D / 32;             // 32-wide d tiles of O^T
-    // Two K and two V tiles, separate objects so waits on one buffer's refill
-    // never cover reads of the other.
+    // K and V tiles, separate objects so waits on one buffer's refill never
+    // cover reads of the other: two of each (two barriers per key tile) for
+    // four waves, three of each (one barrier per key tile) for eight, whose
+    // one workgroup per CU has the LDS for them.
+    constexpr int NB = NW == 8 ? 3 : 2;
     __shared__ __attribute__((aligned(16))) uint16_t Ks0[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Ks1[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks2[NB == 3 ? TILE : 8];
     __shared__ __attribute__((aligned(16))) uint16_t Vs0[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Vs1[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs2[NB == 3 ? TILE : 8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -134,22 +139,26 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     // Workgroup -> (q tile, batch, q-head). In the logical order, consecutive
     // workgroups are the heads of one q tile and causal tiles come heaviest
     // first. The hardware deals workgroups to the 8 XCDs round robin
-    // (workgroup i to XCD i % 8) and each XCD has its own L2. When batch *
-    // n_kv_heads is a multiple of 8 (p.xcd_chunks), the logical order is dealt
-    // out in chunks of `group` workgroups — the q-heads that share one kv-head
-    // — with a whole chunk on one XCD; all chunks of one (sequence, kv-head)
-    // then land on the same XCD, so each K/V stream is fetched into one L2
-    // only (measured 8% faster on 16 packed prompts; on one long sequence
-    // with one kv-head the plain order is 3% faster). The last partial round
-    // keeps the plain order.
+    // (workgroup i to XCD i % 8) and each XCD has its own L2. With
+    // p.xcd_chunks the logical order is dealt out in chunks of `group`
+    // workgroups — the q-heads that share one kv-head — with a whole chunk on
+    // one XCD. When batch * n_kv_heads is a multiple of 8 all chunks of one
+    // (sequence, kv-head) then land on the same XCD, so each K/V stream is
+    // fetched into one L2 only (measured 8% faster on 16 packed prompts). The
+    // host also asks for chunks on eight-wave grids whose q-heads share
+    // kv-heads, where the heads of one q tile then share one L2 (32K causal,
+    // 8 q-heads over 1 kv-head: 2% faster together with the three-buffer
+    // pipeline). Successive rounds of chunks are dealt in opposite XCD order,
+    // so that with causal tiles (heaviest first) every XCD gets the same
+    // work. The last partial round keeps the plain order.
     const int nbh = p.batch * p.n_q_heads;
     int wid = (int)blockIdx.x;
     if (p.xcd_chunks) {
         const int G = p.group, round = 8 * G;
         const int full = ((int)gridDim.x / round) * round;
         if (wid < full) {
-            const int xcd = wid & 7, k = wid >> 3;
-            wid = ((k / G) * 8 + xcd) * G + k % G;
+            const int xcd = wid & 7, k = wid >> 3, r = k / G;
+            wid = (r * 8 + ((r & 1) ? 7 - xcd : xcd)) * G + k % G;
         }
     }
     // A grid that fits on the chip in one go (256 < workgroups <= 512, two
@@ -434,11 +443,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     // their use. The row sums of P(j) (v_dot2c, which stalls when mixed with
     // MFMAs) come after the last MFMA, in two independent chains.
     //
-    // Loads and barriers: step j issues V(j+1) at its start (into the buffer
-    // of V(j-1)) and K(j+3) after a mid-step barrier that follows the QK part
-    // (into the buffer of K(j+1), which that part has just read). The
-    // mid-step barrier also publishes V(j), the end-of-step barrier K(j+2):
-    // every tile has about one and a half steps to arrive. Tile indices past
+    // Loads and barriers (two buffers): step j issues V(j+1) at its start
+    // (into the buffer of V(j-1)) and K(j+3) after a mid-step barrier that
+    // follows the QK part (into the buffer of K(j+1), which that part has just
+    // read). The mid-step barrier also publishes V(j), the end-of-step barrier
+    // K(j+2): every tile has about one and a half steps to arrive. With three
+    // buffers there is no mid-step barrier: step j issues V(j+2) at its start
+    // and K(j+3) in its P V part, and the end-of-step barrier publishes K(j+2)
+    // and V(j+1), whose buffers no wave reads in step j. Tile indices past
     // the last tile are clamped to it, so every step issues the same loads
     // and each wait is a fixed count: loads complete in issue order (V(j),
     // K(j+2), V(j+1), K(j+3), ...), and each barrier waits with vmcnt = the
@@ -449,9 +461,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     constexpr int NPV_EARLY = NPV - NDT;  // P V MFMAs before the last key chunk's
     static_assert(NS >= 4, "the V prefetch is issued in the last two QK stages");
     const int j_last = j_end - 1;
-    auto step = [&](int j, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1, uint16_t* Kn, uint16_t* Vc,
+    auto step = [&](int j, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1, uint16_t* Kn, uint16_t* Kl, uint16_t* Vc,
                     uint16_t* Vl) __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(vbase, p.vs.seq, min(j + 1, j_last));
+        const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(vbase, p.vs.seq, min(j + NB - 1, j_last));
         const uint32_t kf = PRE ? 0u : opaque(kfrag);
         const uint32_t vf = PRE ? 0u : opaque(vfrag);
         s16x8 ka[NS][2];
@@ -494,9 +506,12 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             for (int i = s * PQ / NS; i < (s + 1) * PQ / NS; ++i) prob_pair(i);
             sched_fence();
         }
-        // V(j) in; every wave is past its reads of K(j+1).
-        wait_vmcnt<2 * LPW>();
-        barrier_lds();
+        if constexpr (NB == 2) {
+            // V(j) in; every wave is past its reads of K(j+1) (with three
+            // buffers both hold at the end-of-step barrier of step j-1).
+            wait_vmcnt<2 * LPW>();
+            barrier_lds();
+        }
         const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kbase, p.ks.seq, min(j + 3, j_last));
 #pragma unroll
         for (int i = 0; i < VPRE; ++i) vread(i);
@@ -507,7 +522,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             const int u = i / NDT, dt = i % NDT;
             const s16x8 pb = __builtin_bit_cast(s16x8, make_uint4(pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]));
             o[dt] = mfma32x32x16<BF16>(vb[i], pb, o[dt]);
-            if (i % (NPV / LPW) == 0) load_part(Kn, krs, kvo[i / (NPV / LPW)], i / (NPV / LPW));
+            if (i % (NPV / LPW) == 0) load_part(Kl, krs, kvo[i / (NPV / LPW)], i / (NPV / LPW));
             if (i + VPRE < NPV) vread(i + VPRE);
             if (i < NPV_EARLY) {
 #pragma unroll
@@ -541,9 +556,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     f32x16 sa0, sa1, sb0, sb1;
     const int nt = j_end - j_begin;
     if (nt > 0) {
-        // The first refill of Vs1 may be range-limited: start it from zeros.
+        // The first refill of a V buffer in the loop may be range-limited: start it from zeros.
+        uint16_t* const vz = NB == 3 ? Vs2 : Vs1;
 #pragma unroll
-        for (int c = tid; c < TILE / 8; c += PF_THREADS) *(uint4*)(Vs1 + 8 * c) = make_uint4(0, 0, 0, 0);
+        for (int c = tid; c < TILE / 8; c += PF_THREADS) *(uint4*)(vz + 8 * c) = make_uint4(0, 0, 0, 0);
         load_k_tile(Ks0, j_begin);
         load_v_tile(Vs0, j_begin);
         load_k_tile(Ks1, min(j_begin + 1, j_last));
@@ -556,15 +572,39 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             mask_half(sa1, j_begin * PF_BN, 1);
         }
         rescale(max_tile(sa0, sa1));
-        __syncthreads();  // every wave is past its reads of K(j_begin)
-        load_k_tile(Ks0, min(j_begin + 2, j_last));
+        if constexpr (NB == 3) {
+            // K(j_begin + 2) and V(j_begin + 1) into buffers no wave has read yet
+            load_k_tile(Ks2, min(j_begin + 2, j_last));
+            load_v_tile(Vs1, min(j_begin + 1, j_last));
+        } else {
+            __syncthreads();  // every wave is past its reads of K(j_begin)
+            load_k_tile(Ks0, min(j_begin + 2, j_last));
+        }
     }
     // Step r = j - j_begin: K(j+1) sits in buffer (r+1)%2, V(j) in buffer r%2.
     // Unrolled by two so that every LDS access names its buffer (the compiler
     // then waits on a refill only before reads of the buffer being refilled).
-    for (int r = 0; r < nt; r += 2) {
-        step(j_begin + r, sa0, sa1, sb0, sb1, Ks1, Vs0, Vs1);
-        if (r + 1 < nt) step(j_begin + r + 1, sb0, sb1, sa0, sa1, Ks0, Vs1, Vs0);
+    if constexpr (NB == 3) {
+        // Step r = j - j_begin: K(j+1) sits in buffer (r+1)%3, V(j) in buffer
+        // r%3; the step refills K buffer r%3 with K(j+3) and V buffer (r+2)%3
+        // with V(j+2). Unrolled by six (the buffers cycle by three, the score
+        // registers by two) so that every LDS access names its buffer.
+        for (int r = 0; r < nt; r += 6) {
+            step(j_begin + r, sa0, sa1, sb0, sb1, Ks1, Ks0, Vs0, Vs2);
+            if (r + 1 < nt) step(j_begin + r + 1, sb0, sb1, sa0, sa1, Ks2, Ks1, Vs1, Vs0);
+            if (r + 2 < nt) step(j_begin + r + 2, sa0, sa1, sb0, sb1, Ks0, Ks2, Vs2, Vs1);
+            if (r + 3 < nt) step(j_begin + r + 3, sb0, sb1, sa0, sa1, Ks1, Ks0, Vs0, Vs2);
+            if (r + 4 < nt) step(j_begin + r + 4, sa0, sa1, sb0, sb1, Ks2, Ks1, Vs1, Vs0);
+            if (r + 5 < nt) step(j_begin + r + 5, sb0, sb1, sa0, sa1, Ks0, Ks2, Vs2, Vs1);
+        }
+    } else {
+        // Step r = j - j_begin: K(j+1) sits in buffer (r+1)%2, V(j) in buffer r%2.
+        // Unrolled by two so that every LDS access names its buffer (the compiler
+        // then waits on a refill only before reads of the buffer being refilled).
+        for (int r = 0; r < nt; r += 2) {
+            step(j_begin + r, sa0, sa1, sb0, sb1, Ks1, Ks1, Vs0, Vs1);
+            if (r + 1 < nt) step(j_begin + r + 1, sb0, sb1, sa0, sa1, Ks0, Ks0, Vs1, Vs0);
+        }
     }
     wait_vmcnt<0>();  // nothing is left in flight when the wave ends
 
