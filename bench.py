@@ -634,6 +634,10 @@ def main():
             "workload": CONTEXT,
             "ms_per_layer": round(ctx_ms, 4),
             "tflops": round(prefill_flops(cspec) / (ctx_ms * 1e-3) / 1e12, 2),
+            "roofline": {"bound": "mfma", "achieved": round(prefill_flops(cspec) / (ctx_ms * 1e-3) / 1e12, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(prefill_flops(cspec) / (ctx_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "traffic": traffic_from_profiles("prefill_ctx_2k")},
             "pages_ms_per_layer": PAGES_CONTEXT_MS_PER_LAYER,
             "pages_hardware": "unnamed NVIDIA GPU (minfer 8n page); context only",
         },
