@@ -30,8 +30,10 @@
 // f32: prefill_f32 — the same recurrence on the vector ALUs (no f32 MFMA
 // shortcut is used): 64 rows per workgroup, four lanes per row.
 //
-// FP8 K/V: prefill_f8kv — K and V stored as E4M3 codes, widened into the
-// same LDS tiles, then prefill_mfma's per-tile math without the pipeline.
+// FP8 K/V: K and V stored as E4M3 codes, widened exactly into the same LDS
+// tiles. On the wide grids that take eight waves (D = 128) prefill_mfma
+// itself stages the codes (KV8) and keeps its whole pipeline; elsewhere
+// prefill_f8kv runs prefill_mfma's per-tile math without the pipeline.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -104,11 +106,45 @@ __device__ __forceinline__ void pf_store_lse(float* dst, float m, float l, bool 
     *(uint32_t*)dst = bits;
 }
 
+// 16 FP8 E4M3 codes -> two 16-byte chunks of 16-bit floats (codes 0..7, 8..15),
+// widened exactly (gfx950's v_cvt_scalef32_pk_*_fp8 with scale 1: every E4M3
+// value is representable in bf16 and f16).
+template <bool BF16>
+__device__ __forceinline__ void widen_e4m3x16(uint4 x, uint4& lo, uint4& hi) {
+    uint32_t wv[8];
+    const uint32_t src[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (BF16) {
+            wv[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[e], 1.0f, false));
+            wv[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[e], 1.0f, true));
+        } else {
+            wv[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src[e], 1.0f, false));
+            wv[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src[e], 1.0f, true));
+        }
+    }
+    lo = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    hi = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+}
+
 // NW waves per workgroup: 4 (two workgroups per CU for D <= 128) or 8 (one
 // workgroup per CU, twice the query rows per K/V tile: half the L2-to-LDS
 // traffic per FLOP).
-template <bool BF16, int D, int MASK, int NW>
+//
+// KV8: K and V hold FP8 E4M3 codes with one scale per tensor (a code stands
+// for scale times its value; the host folds K's scale into c, V's scale
+// multiplies the output) -- the decode page's quantised cache read by a
+// prefill. Eight waves and D = 128 only. The codes of each tile go HBM->LDS
+// into a staging area with the same direct loads, each lane's 16 bytes to its
+// own 16-byte slot; at the end of the step before the tile is needed the same
+// lane widens them (exactly) and writes them into the 16-bit tile layout
+// below, and the end-of-step barrier publishes them. A lane only reads back
+// what its own load wrote, so the staging needs no barrier of its own, and
+// the 16-bit tiles, the fragment reads and all of the math are the 16-bit
+// path's.
+template <bool BF16, int D, int MASK, int NW, bool KV8 = false>
 __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefill_mfma(PrefillParams p) {
+    static_assert(!KV8 || (NW == 8 && D == 128), "FP8 K/V: eight waves, D = 128");
     constexpr int PF_BM = PF_ROWS_PER_WAVE * NW;  // query rows per workgroup
     constexpr int PF_THREADS = 64 * NW;
     constexpr int CPR = D / 8;              // 16-byte chunks per row
@@ -127,6 +163,12 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     __shared__ __attribute__((aligned(16))) uint16_t Vs0[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Vs1[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Vs2[NB == 3 ? TILE : 8];
+    // FP8 staging: two tiles of codes per tensor (separate objects, as above)
+    constexpr int TILE8 = KV8 ? TILE : 16;
+    __shared__ __attribute__((aligned(16))) uint8_t Sk0[TILE8];
+    __shared__ __attribute__((aligned(16))) uint8_t Sk1[TILE8];
+    __shared__ __attribute__((aligned(16))) uint8_t Sv0[TILE8];
+    __shared__ __attribute__((aligned(16))) uint8_t Sv1[TILE8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -280,7 +322,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     // (computed once), so the range check covers the whole offset.
     uint32_t kvo[LPW], vvo[LPW];
 #pragma unroll
-    for (int ii = 0; ii < LPW; ++ii) {
+    for (int ii = 0; ii < (KV8 ? 0 : LPW); ++ii) {
         const int i = w * LPW + ii;
         const uint32_t uk = D == 64 ? (4 * i) & 7 : (D == 128 ? (4 * i) & 15 : (2 * i) & 15);
         const uint32_t uv = D <= 128 ? 0 : 4 * ((2 * i) & 3);
@@ -299,6 +341,53 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     auto load_part = [&](uint16_t* dst, __amdgpu_buffer_rsrc_t rs, uint32_t voff, int ii) __attribute__((always_inline)) {
         const int i = w * LPW + ii;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 512 * i), 16, voff, 0, 0, 0);
+    };
+
+    // FP8 codes (KV8): one direct load per wave, tensor and tile; lane
+    // c8 = 64 w + lane takes codes 16 (c8 % 8) .. +16 of tile row c8 / 8 into
+    // staging bytes 16 c8 .. +16, and later widens exactly those into the
+    // swizzled 16-bit tile. Range-limited loads of the last tile drop the rows
+    // past key_max, whose staging bytes keep the codes of an earlier tile
+    // (visible keys: finite), masked like every row past the end.
+    const int c8 = 64 * w + lane, row8 = c8 >> 3, col8 = 16 * (c8 & 7);
+    const uint8_t* const kbase8 = (const uint8_t*)p.k + k_at + (int64_t)hk * p.ks.head;
+    const uint8_t* const vbase8 = (const uint8_t*)p.v + v_at + (int64_t)hk * p.vs.head;
+    uint32_t k8o = 0, v8o = 0;
+    if constexpr (KV8) {
+        k8o = (uint32_t)row8 * (uint32_t)p.ks.seq + (uint32_t)col8;
+        v8o = (uint32_t)row8 * (uint32_t)p.vs.seq + (uint32_t)col8;
+        asm volatile("" : "+v"(k8o), "+v"(v8o));
+    }
+    auto tile_rsrc8 = [&](const uint8_t* base, int64_t seq, int j) __attribute__((always_inline)) {
+        const int kv0 = j * PF_BN;
+        const uint32_t nrec =
+            kv0 + PF_BN - 1 <= key_max ? 0x7fffffffu : (uint32_t)(key_max - kv0) * (uint32_t)seq + (uint32_t)D;
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kv0 * seq), (short)0, nrec, 0x00020000);
+    };
+    auto stage_part = [&](uint8_t* dst, __amdgpu_buffer_rsrc_t rs, uint32_t voff) __attribute__((always_inline)) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 1024 * w), 16, voff, 0, 0, 0);
+    };
+    // A whole tile with its rows clamped one by one into [key_min, key_max] (the prologue's tiles).
+    auto stage_clamped = [&](uint8_t* dst, const uint8_t* base, int64_t seq, int j) __attribute__((always_inline)) {
+        const int kv0 = j * PF_BN;
+        const int key = min(max(kv0 + row8, key_min), key_max);  // kv0 <= key <= kv0 + 63
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kv0 * seq), (short)0, 0x7fffffff, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 1024 * w), 16,
+                                                 (uint32_t)(key - kv0) * (uint32_t)seq + (uint32_t)col8, 0, 0, 0);
+    };
+    auto stage_read = [&](const uint8_t* src) __attribute__((always_inline)) { return *(const uint4*)(src + 16 * c8); };
+    auto widen_store = [&](uint16_t* dst, uint4 x, bool is_k) __attribute__((always_inline)) {
+        uint4 lo, hi;
+        widen_e4m3x16<BF16>(x, lo, hi);
+        char* drow = (char*)dst + row8 * D * 2;
+        const int sw = is_k ? pf_kswz<D>(row8) : pf_vswz<D>(row8);
+        const int cc = c8 & 7;
+        *(uint4*)(drow + 16 * ((2 * cc) ^ sw)) = lo;
+        *(uint4*)(drow + 16 * ((2 * cc + 1) ^ sw)) = hi;
+    };
+    auto widen_tile = [&](uint16_t* dst, const uint8_t* src, bool is_k) __attribute__((always_inline)) {
+        widen_store(dst, stage_read(src), is_k);
     };
 
     // Running max in scaled log2 units. It only moves when a row's tile max
@@ -461,14 +550,27 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     constexpr int NPV_EARLY = NPV - NDT;  // P V MFMAs before the last key chunk's
     static_assert(NS >= 4, "the V prefetch is issued in the last two QK stages");
     const int j_last = j_end - 1;
+    // KV8 (three buffers): step j stages the codes of V(j+2) (into Svb) and
+    // K(j+3) (into Skb) where the 16-bit path loads those tiles, and widens
+    // V(j+1) (from Sva) in its QK part and K(j+2) (from Ska) in its P V part,
+    // both staged in step j-1, into the third V and K buffers V3, K3, which no
+    // wave has read since step j-2; the end-of-step barrier then publishes
+    // them as it publishes the direct loads of the 16-bit path. Loads complete
+    // in issue order (V(j+1), K(j+2), V(j+2), K(j+3)), so each widening waits
+    // with vmcnt = the two loads issued after the one it reads. The codes are
+    // read three MFMA stages before they are widened and written (QK stages 2
+    // and 5, P V MFMAs 4 and 8: measured best of five placements on the 32K
+    // causal workload: 3% faster than widening both at the end of the step).
     auto step = [&](int j, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1, uint16_t* Kn, uint16_t* Kl, uint16_t* Vc,
-                    uint16_t* Vl) __attribute__((always_inline)) {
+                    uint16_t* Vl, uint16_t* K3, uint16_t* V3, uint8_t* Ska, uint8_t* Skb, uint8_t* Sva,
+                    uint8_t* Svb) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(vbase, p.vs.seq, min(j + NB - 1, j_last));
         const uint32_t kf = PRE ? 0u : opaque(kfrag);
         const uint32_t vf = PRE ? 0u : opaque(vfrag);
         s16x8 ka[NS][2];
         s16x8 vb[NPV];
         uint32_t pk[16];
+        uint4 x8;  // KV8: one lane's staged codes between their read and their widening
         auto kread = [&](int s) __attribute__((always_inline)) {
             uint32_t off;
             if constexpr (PRE) off = koff[s]; else off = kf ^ (32u * s);
@@ -500,7 +602,16 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
         for (int s = 0; s < NS; ++s) {
             n0 = mfma32x32x16<BF16>(ka[s][0], qf[s], n0);
             n1 = mfma32x32x16<BF16>(ka[s][1], qf[s], n1);
-            if (s % (NS / LPW) == 0) load_part(Vl, vrs, vvo[s / (NS / LPW)], s / (NS / LPW));
+            if constexpr (KV8) {
+                if (s == 0) stage_part(Svb, tile_rsrc8(vbase8, p.vs.seq, min(j + 2, j_last)), v8o);
+                if (s == 2) {
+                    wait_vmcnt<2>();  // V(j+1) in
+                    x8 = stage_read(Sva);
+                }
+                if (s == 5) widen_store(V3, x8, false);
+            } else if (s % (NS / LPW) == 0) {
+                load_part(Vl, vrs, vvo[s / (NS / LPW)], s / (NS / LPW));
+            }
             if (s + 2 < NS) kread(s + 2);
 #pragma unroll
             for (int i = s * PQ / NS; i < (s + 1) * PQ / NS; ++i) prob_pair(i);
@@ -522,7 +633,16 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             const int u = i / NDT, dt = i % NDT;
             const s16x8 pb = __builtin_bit_cast(s16x8, make_uint4(pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]));
             o[dt] = mfma32x32x16<BF16>(vb[i], pb, o[dt]);
-            if (i % (NPV / LPW) == 0) load_part(Kl, krs, kvo[i / (NPV / LPW)], i / (NPV / LPW));
+            if constexpr (KV8) {
+                if (i == 0) stage_part(Skb, tile_rsrc8(kbase8, p.ks.seq, min(j + 3, j_last)), k8o);
+                if (i == 4) {
+                    wait_vmcnt<2>();  // K(j+2) in
+                    x8 = stage_read(Ska);
+                }
+                if (i == 8) widen_store(K3, x8, true);
+            } else if (i % (NPV / LPW) == 0) {
+                load_part(Kl, krs, kvo[i / (NPV / LPW)], i / (NPV / LPW));
+            }
             if (i + VPRE < NPV) vread(i + VPRE);
             if (i < NPV_EARLY) {
 #pragma unroll
@@ -547,7 +667,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
         }
         rescale(mx);
         // K(j+2) in; every wave is past its reads of V(j).
-        wait_vmcnt<2 * LPW>();
+        if constexpr (!KV8) wait_vmcnt<2 * LPW>();
         barrier_lds();
     };
 
@@ -556,15 +676,26 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     f32x16 sa0, sa1, sb0, sb1;
     const int nt = j_end - j_begin;
     if (nt > 0) {
-        // The first refill of a V buffer in the loop may be range-limited: start it from zeros.
-        uint16_t* const vz = NB == 3 ? Vs2 : Vs1;
+        if constexpr (KV8) {
+            stage_clamped(Sk0, kbase8, p.ks.seq, j_begin);
+            stage_clamped(Sv0, vbase8, p.vs.seq, j_begin);
+            stage_clamped(Sk1, kbase8, p.ks.seq, min(j_begin + 1, j_last));
+            pf_load_q<D>(qf, qrow, my_q < sq, p.qflip);
+            wait_vmcnt<0>();
+            widen_tile(Ks0, Sk0, true);
+            widen_tile(Vs0, Sv0, false);
+            widen_tile(Ks1, Sk1, true);
+        } else {
+            // The first refill of a V buffer in the loop may be range-limited: start it from zeros.
+            uint16_t* const vz = NB == 3 ? Vs2 : Vs1;
 #pragma unroll
-        for (int c = tid; c < TILE / 8; c += PF_THREADS) *(uint4*)(vz + 8 * c) = make_uint4(0, 0, 0, 0);
-        load_k_tile(Ks0, j_begin);
-        load_v_tile(Vs0, j_begin);
-        load_k_tile(Ks1, min(j_begin + 1, j_last));
-        pf_load_q<D>(qf, qrow, my_q < sq, p.qflip);
-        wait_vmcnt<0>();
+            for (int c = tid; c < TILE / 8; c += PF_THREADS) *(uint4*)(vz + 8 * c) = make_uint4(0, 0, 0, 0);
+            load_k_tile(Ks0, j_begin);
+            load_v_tile(Vs0, j_begin);
+            load_k_tile(Ks1, min(j_begin + 1, j_last));
+            pf_load_q<D>(qf, qrow, my_q < sq, p.qflip);
+            wait_vmcnt<0>();
+        }
         __syncthreads();
         qk_tile(sa0, sa1, Ks0);
         if (!(wave_live && tile_full(j_begin))) {
@@ -572,7 +703,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             mask_half(sa1, j_begin * PF_BN, 1);
         }
         rescale(max_tile(sa0, sa1));
-        if constexpr (NB == 3) {
+        if constexpr (KV8) {
+            // codes of V(j_begin + 1) and K(j_begin + 2) (in the loop's order), widened in the first step
+            stage_clamped(Sv1, vbase8, p.vs.seq, min(j_begin + 1, j_last));
+            stage_clamped(Sk0, kbase8, p.ks.seq, min(j_begin + 2, j_last));
+        } else if constexpr (NB == 3) {
             // K(j_begin + 2) and V(j_begin + 1) into buffers no wave has read yet
             load_k_tile(Ks2, min(j_begin + 2, j_last));
             load_v_tile(Vs1, min(j_begin + 1, j_last));
@@ -589,21 +724,25 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
         // r%3; the step refills K buffer r%3 with K(j+3) and V buffer (r+2)%3
         // with V(j+2). Unrolled by six (the buffers cycle by three, the score
         // registers by two) so that every LDS access names its buffer.
+        // KV8 staging cycles by two: even steps widen from Sk0 / Sv1 and stage
+        // into Sk1 / Sv0, odd steps the other way round.
         for (int r = 0; r < nt; r += 6) {
-            step(j_begin + r, sa0, sa1, sb0, sb1, Ks1, Ks0, Vs0, Vs2);
-            if (r + 1 < nt) step(j_begin + r + 1, sb0, sb1, sa0, sa1, Ks2, Ks1, Vs1, Vs0);
-            if (r + 2 < nt) step(j_begin + r + 2, sa0, sa1, sb0, sb1, Ks0, Ks2, Vs2, Vs1);
-            if (r + 3 < nt) step(j_begin + r + 3, sb0, sb1, sa0, sa1, Ks1, Ks0, Vs0, Vs2);
-            if (r + 4 < nt) step(j_begin + r + 4, sa0, sa1, sb0, sb1, Ks2, Ks1, Vs1, Vs0);
-            if (r + 5 < nt) step(j_begin + r + 5, sb0, sb1, sa0, sa1, Ks0, Ks2, Vs2, Vs1);
+            step(j_begin + r, sa0, sa1, sb0, sb1, Ks1, Ks0, Vs0, Vs2, Ks2, Vs1, Sk0, Sk1, Sv1, Sv0);
+            if (r + 1 < nt) step(j_begin + r + 1, sb0, sb1, sa0, sa1, Ks2, Ks1, Vs1, Vs0, Ks0, Vs2, Sk1, Sk0, Sv0, Sv1);
+            if (r + 2 < nt) step(j_begin + r + 2, sa0, sa1, sb0, sb1, Ks0, Ks2, Vs2, Vs1, Ks1, Vs0, Sk0, Sk1, Sv1, Sv0);
+            if (r + 3 < nt) step(j_begin + r + 3, sb0, sb1, sa0, sa1, Ks1, Ks0, Vs0, Vs2, Ks2, Vs1, Sk1, Sk0, Sv0, Sv1);
+            if (r + 4 < nt) step(j_begin + r + 4, sa0, sa1, sb0, sb1, Ks2, Ks1, Vs1, Vs0, Ks0, Vs2, Sk0, Sk1, Sv1, Sv0);
+            if (r + 5 < nt) step(j_begin + r + 5, sb0, sb1, sa0, sa1, Ks0, Ks2, Vs2, Vs1, Ks1, Vs0, Sk1, Sk0, Sv0, Sv1);
         }
     } else {
         // Step r = j - j_begin: K(j+1) sits in buffer (r+1)%2, V(j) in buffer r%2.
         // Unrolled by two so that every LDS access names its buffer (the compiler
         // then waits on a refill only before reads of the buffer being refilled).
         for (int r = 0; r < nt; r += 2) {
-            step(j_begin + r, sa0, sa1, sb0, sb1, Ks1, Ks1, Vs0, Vs1);
-            if (r + 1 < nt) step(j_begin + r + 1, sb0, sb1, sa0, sa1, Ks0, Ks0, Vs1, Vs0);
+            step(j_begin + r, sa0, sa1, sb0, sb1, Ks1, Ks1, Vs0, Vs1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+            if (r + 1 < nt)
+                step(j_begin + r + 1, sb0, sb1, sa0, sa1, Ks0, Ks0, Vs1, Vs0, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     nullptr);
         }
     }
     wait_vmcnt<0>();  // nothing is left in flight when the wave ends
@@ -615,7 +754,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     const float sink = p.sinks ? p.sinks[h] : -__builtin_inff();
     const bool nan_row = sink_gives_nan(sink);
     const float osc = p.sinks ? fold_sink(sink * kLog2e, m_fin, l_tot) : 1.f;
-    const float inv = l_tot > 0.f ? osc / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? (KV8 ? osc * p.v_scale : osc) / l_tot : 0.f;
     if (p.lse && hf == 0 && wave_live && my_q < sq)
         pf_store_lse(&p.lse[(lse_at + my_q) * p.n_q_heads + h], m_fin, l_tot, nan_row);
     if (wave_live && my_q < sq)
@@ -991,8 +1130,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pair(PrefillParams p) {
 // masks, the online softmax with its lazy rescale and the epilogue are
 // prefill_mfma's. Two LDS buffers per tensor: tile j+1 is requested before
 // the MFMAs of tile j and written after them, with one barrier per tile.
-// NW waves of 32 query rows (as prefill_mfma: 8 for D = 128 on wide grids);
-// no software pipelining across tiles.
+// Four waves of 32 query rows; no software pipelining across tiles. (The wide
+// D = 128 grids go to prefill_mfma with FP8 staging instead.)
 template <bool BF16, int D, int MASK, int NW>
 __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefill_f8kv(PrefillParams p) {
     constexpr int PF_BM = PF_ROWS_PER_WAVE * NW;
@@ -1062,23 +1201,6 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             vr[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(vb8 + (int64_t)key * p.vs.seq + col)));
         }
     };
-    // 16 codes -> two 16-byte chunks of 16-bit floats (codes 0..7, 8..15)
-    auto widen = [](uint4 x, uint4& lo, uint4& hi) __attribute__((always_inline)) {
-        uint32_t wv[8];
-        const uint32_t src[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if constexpr (BF16) {
-                wv[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[e], 1.0f, false));
-                wv[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[e], 1.0f, true));
-            } else {
-                wv[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src[e], 1.0f, false));
-                wv[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src[e], 1.0f, true));
-            }
-        }
-        lo = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-        hi = make_uint4(wv[4], wv[5], wv[6], wv[7]);
-    };
     auto store = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
@@ -1086,11 +1208,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             const int row = c / CH8, cc = c % CH8;
             uint4 lo, hi;
             char* krow = (char*)Ks[buf] + row * D * 2;
-            widen(kr[i], lo, hi);
+            widen_e4m3x16<BF16>(kr[i], lo, hi);
             *(uint4*)(krow + 16 * ((2 * cc) ^ pf_kswz<D>(row))) = lo;
             *(uint4*)(krow + 16 * ((2 * cc + 1) ^ pf_kswz<D>(row))) = hi;
             char* vrow = (char*)Vs[buf] + row * D * 2;
-            widen(vr[i], lo, hi);
+            widen_e4m3x16<BF16>(vr[i], lo, hi);
             *(uint4*)(vrow + 16 * ((2 * cc) ^ pf_vswz<D>(row))) = lo;
             *(uint4*)(vrow + 16 * ((2 * cc + 1) ^ pf_vswz<D>(row))) = hi;
         }
@@ -1352,14 +1474,14 @@ __global__ __launch_bounds__(256) void prefill_f32(PrefillParams p) {
 }
 
 // ---------------------------------------------------------------------------- dispatch
-template <bool BF16, int D, int NW>
+template <bool BF16, int D, int NW, bool KV8 = false>
 static hipError_t launch_mfma_nw(PrefillParams p, int mask, hipStream_t s) {
     p.n_q_tiles = (p.seqlen_q + PF_ROWS_PER_WAVE * NW - 1) / (PF_ROWS_PER_WAVE * NW);
     const dim3 grid((unsigned)p.n_q_tiles * p.batch * p.n_q_heads), block(64 * NW);
     switch (mask) {
-        case kMaskNone: hipLaunchKernelGGL((prefill_mfma<BF16, D, kMaskNone, NW>), grid, block, 0, s, p); break;
-        case kMaskCausal: hipLaunchKernelGGL((prefill_mfma<BF16, D, kMaskCausal, NW>), grid, block, 0, s, p); break;
-        default: hipLaunchKernelGGL((prefill_mfma<BF16, D, kMaskCausalWindow, NW>), grid, block, 0, s, p); break;
+        case kMaskNone: hipLaunchKernelGGL((prefill_mfma<BF16, D, kMaskNone, NW, KV8>), grid, block, 0, s, p); break;
+        case kMaskCausal: hipLaunchKernelGGL((prefill_mfma<BF16, D, kMaskCausal, NW, KV8>), grid, block, 0, s, p); break;
+        default: hipLaunchKernelGGL((prefill_mfma<BF16, D, kMaskCausalWindow, NW, KV8>), grid, block, 0, s, p); break;
     }
     return hipGetLastError();
 }
@@ -1419,12 +1541,13 @@ static hipError_t launch_f8kv_nw(PrefillParams p, int mask, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Eight waves for D = 128 on the grids where prefill_mfma takes them.
+// On the grids where the 16-bit prefill takes eight waves (D = 128), its
+// pipelined kernel with FP8 staging; prefill_f8kv otherwise.
 template <bool BF16, int D>
 static hipError_t launch_f8kv_mask(PrefillParams p, int mask, hipStream_t s) {
     if constexpr (D == 128) {
         const long wide = (long)((p.seqlen_q + 255) / 256) * p.batch * p.n_q_heads;
-        if (wide >= kPrefillWideMinWorkgroups) return launch_f8kv_nw<BF16, D, 8>(p, mask, s);
+        if (wide >= kPrefillWideMinWorkgroups) return launch_mfma_nw<BF16, D, 8, true>(p, mask, s);
     }
     return launch_f8kv_nw<BF16, D, 4>(p, mask, s);
 }

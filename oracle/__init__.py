@@ -96,6 +96,8 @@ def attention_rows(q, k, v, scale: float, causal: bool, window: int, rows, sinks
     assert v.shape == k.shape and Dk == D and Bk == B
     rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
     n = rows.shape[0]
+    if n and ((rows < 0).any() or (rows[:, 0] >= B).any() or (rows[:, 1] >= Sq).any() or (rows[:, 2] >= Hq).any()):
+        raise ValueError("oracle_attention_rows: a row index lies outside [B, Sq, Hq]")
     o = np.zeros((n, D), dtype=np.float64)
     lse = np.zeros(n, dtype=np.float64)
     qs, ks, vs = _strides3(q), _strides3(k), _strides3(v)

@@ -1,8 +1,8 @@
 """GPU parity of attn_prefill_fwd_fp8kv (K and V as FP8 E4M3 codes with per-tensor scales,
 f16/bf16 queries) against the fp64 oracle applied to scale * value(code), with the
 tolerances of gpu_common; plus a bitwise comparison with attn_prefill_fwd fed the same
-codes widened to the 16-bit type (the widening is exact, and both kernels use 128-row
-tiles at these sizes)."""
+codes widened to the 16-bit type (the widening is exact, and both take the same launch
+shape: 128-row tiles at the small sizes, the pipelined 256-row kernel on the wide grids)."""
 import numpy as np
 import pytest
 
@@ -24,6 +24,18 @@ CASES = {
     "bf16_more_queries_than_keys": (1, 2, 1, 300, 100, 128, "bf16", True, 0, 1.0, 1.0),
     "f16_window_1": (1, 4, 2, 130, 130, 128, "f16", True, 1, 0.9, 1.1),
     "bf16_d64_window": (2, 6, 3, 190, 190, 64, "bf16", True, 33, 1.0, 0.8),
+}
+
+
+# Grids of at least 512 workgroups of 256 rows (D = 128): the pipelined eight-wave kernel
+# with FP8 staging. Ragged key tails, a cached prefix (Sq < Skv), and more queries than
+# keys (the first Sq - Skv rows see no key).
+WAVE8 = {
+    "bf16_wave8_gqa": (4, 8, 2, 4096, 4096, 128, "bf16", True, 0, 0.75, 1.25),
+    "f16_wave8_window": (2, 16, 4, 4096, 4096, 128, "f16", True, 1000, 0.5, 2.0),
+    "bf16_wave8_prefix_ragged": (8, 16, 4, 1024, 3000, 128, "bf16", True, 0, 1.5, 0.625),
+    "bf16_wave8_more_queries": (2, 16, 2, 4000, 1500, 128, "bf16", True, 0, 1.0, 1.0),
+    "f16_wave8_nomask_ragged": (4, 8, 8, 4096, 1000, 128, "f16", False, 0, 1.0, 0.5),
 }
 
 
@@ -105,6 +117,45 @@ def test_fp8_prefill_equals_the_16bit_kernel_on_widened_codes(name):
                   window=case[8])
     torch.cuda.synchronize()
     assert np.array_equal(got, host64(o, dtype))
+
+
+@pytest.mark.parametrize("name", list(WAVE8))
+def test_fp8_prefill_eight_wave_equals_the_16bit_kernel_on_widened_codes(name):
+    """Unit scales, eight-wave launches: bitwise equal to attn_prefill_fwd on the widened codes."""
+    import flash_attention_forward_amd as F
+
+    torch = torch_cuda()
+    case = WAVE8[name][:9] + (1.0, 1.0)
+    q, k, v = make(case, 150 + len(name))
+    dtype = case[6]
+    say("fp8 prefill vs widened, eight waves", name)
+    got, _ = run(case, q, k, v)
+    kw = W.to_torch(W.round_to(W.as_f32(k, "fp8"), dtype), dtype, "cuda")
+    vw = W.to_torch(W.round_to(W.as_f32(v, "fp8"), dtype), dtype, "cuda")
+    o = F.prefill(dev(q, dtype), kw, vw, scale=float(np.float32(1.0 / np.sqrt(case[5]))), causal=case[7],
+                  window=case[8])
+    torch.cuda.synchronize()
+    assert np.array_equal(got, host64(o, dtype))
+
+
+@pytest.mark.parametrize("name", list(WAVE8))
+def test_fp8_prefill_eight_wave_parity_sampled(name):
+    """Eight-wave launches with per-tensor scales against the oracle on rows spread over every
+    batch, head and query tile (first, last and ragged rows included)."""
+    case = WAVE8[name]
+    B, Hq, Hkv, Sq, Skv, D, dtype, causal, window, ks, vs = case
+    q, k, v = make(case, 170 + len(name))
+    say("fp8 prefill eight waves", name)
+    got, _ = run(case, q, k, v)
+    rng = np.random.default_rng(9)
+    edge = [0, 1, 255, 256, Sq // 2, Sq - 257, Sq - 1, Sq - Skv - 1, Sq - Skv, Sq - Skv + 1]  # last rows with no key
+    ii = np.concatenate([np.array([e for e in edge if 0 <= e < Sq]), rng.integers(0, Sq, 120)])
+    rows = np.stack([rng.integers(0, B, len(ii)), ii, rng.integers(0, Hq, len(ii))], axis=1).astype(np.int64)
+    k64 = np.float64(np.float32(ks)) * W.as_f64(k, "fp8")
+    v64 = np.float64(np.float32(vs)) * W.as_f64(v, "fp8")
+    ref, bound = attention_with_bound(W.as_f64(q, dtype), k64, v64, float(np.float32(1.0 / np.sqrt(D))), causal,
+                                      window, dtype, rows=rows)
+    check(got[rows[:, 0], rows[:, 1], rows[:, 2]], ref, dtype, name, bound=bound)
 
 
 def test_fp8_prefill_full_size_sampled():

@@ -657,3 +657,15 @@ def test_varlen_positions_match_sdpa_with_a_position_mask():
     ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(mask), scale=0.5,
                                                            enable_gqa=True)[0].permute(1, 0, 2).numpy()
     np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_rows_rejects_rows_outside_the_tensors():
+    """A row index outside [B, Sq, Hq] raises instead of reading out of bounds."""
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((2, 5, 3, 8))
+    k = rng.standard_normal((2, 7, 1, 8))
+    for bad in ((0, -1, 0), (2, 0, 0), (0, 5, 0), (0, 0, 3)):
+        with pytest.raises(ValueError):
+            oracle.attention_rows(q, k, k, 0.3, True, 0, np.array([bad]))
+    o, _ = oracle.attention_rows(q, k, k, 0.3, True, 0, np.array([(1, 4, 2)]))
+    assert o.shape == (1, 8)
