@@ -441,19 +441,42 @@ def main():
     wo_timed = wo.cpu()
     del wq, wk, wv, wo
 
-    # the 32K causal workload with K and V stored as FP8 E4M3 (attn_prefill_fwd_fp8kv): 10 back-to-back launches
+    # the 32K causal workload with K and V stored as FP8 E4M3 (attn_prefill_fwd_fp8kv), timed as the
+    # main loop times the 16-bit prefill: each launch followed by the paged decode (split + combine),
+    # events around the prefill only, 10 steps. Then 10 back-to-back launches of each prefill, which
+    # draw more power and run at a lower clock than the alternating steps.
     fks, fvs = W.FP8_PREFILL_SCALES
     k8 = W.to_torch(W.f32_to_e4m3_bits(W.as_f32(pin.k, pspec.dtype) / np.float32(fks)), "fp8", dev)
     v8 = W.to_torch(W.f32_to_e4m3_bits(W.as_f32(pin.v, pspec.dtype) / np.float32(fvs)), "fp8", dev)
+
+    def decode_step():
+        F.attn_decode_fwd(dq, kc, vc, cl, ws.part_o, ws.part_lse, args.split_len, ms, dspec.scale_f32, bt)
+        F.attn_decode_combine(ws.part_o, ws.part_lse, cl, args.split_len, ms, do)
+
     for _ in range(5):
         F.attn_prefill_fwd_fp8kv(q, k8, v8, o, pspec.scale_f32, True, 0, fks, fvs)
-    f8ev = [ev(), ev()]
-    f8ev[0].record(stream)
-    for _ in range(10):
+        decode_step()
+    f8ev = [[ev(), ev()] for _ in range(10)]
+    for e in f8ev:
+        e[0].record(stream)
         F.attn_prefill_fwd_fp8kv(q, k8, v8, o, pspec.scale_f32, True, 0, fks, fvs)
-    f8ev[1].record(stream)
+        e[1].record(stream)
+        decode_step()
     torch.cuda.synchronize()
-    pf8_ms = f8ev[0].elapsed_time(f8ev[1]) / 10
+    pf8_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in f8ev]))
+
+    def back_to_back(launch, n=10):
+        launch()
+        e = [ev(), ev()]
+        e[0].record(stream)
+        for _ in range(n):
+            launch()
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / n
+
+    pf8_b2b_ms = back_to_back(lambda: F.attn_prefill_fwd_fp8kv(q, k8, v8, o, pspec.scale_f32, True, 0, fks, fvs))
+    pre_b2b_ms = back_to_back(lambda: F.attn_prefill_fwd(q, k, v, o, pspec.scale_f32, True, 0))
     del k8, v8
 
     # packed prompts of different lengths (attn_prefill_varlen_fwd): 10 back-to-back launches
@@ -656,9 +679,13 @@ def main():
             "workload": PREFILL,
             "ms": round(pf8_ms, 4),
             "tflops": round(prefill_flops(pspec) / (pf8_ms * 1e-3) / 1e12, 2),
+            "ms_back_to_back": round(pf8_b2b_ms, 4),
+            "bf16_ms_back_to_back": round(pre_b2b_ms, 4),
             "k_scale": fks,
             "v_scale": fvs,
-            "note": "the 32K causal prefill with K and V stored as FP8 E4M3 (per-tensor scales), q and o bf16",
+            "note": "the 32K causal prefill with K and V stored as FP8 E4M3 (per-tensor scales), q and o bf16; "
+                    "ms is timed as prefill_ms (each launch followed by the paged decode), the back-to-back "
+                    "pair times 10 launches of each kernel in a row",
             "roofline": {"bound": "mfma", "achieved": round(prefill_flops(pspec) / (pf8_ms * 1e-3) / 1e12, 2),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(prefill_flops(pspec) / (pf8_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),

@@ -112,12 +112,13 @@ int prefill_impl(const void* q, attn_strides q_st, const void* k, attn_strides k
     p.cu_seqlens_q = cu_seqlens_q;
     p.cu_seqlens_kv = cu_seqlens_kv;
     p.positions = positions;
-    // Deal workgroups to XCDs in chunks of the q-heads sharing a kv-head: when every
-    // (sequence, kv-head) then stays on one XCD, and on the eight-wave grids (the same
-    // rule as the prefill dispatch's) whose q-heads share kv-heads.
-    p.xcd_chunks = ((int64_t)batch * n_kv_heads) % 8 == 0 ||
-                   (!cu_seqlens_q && head_dim <= 128 && n_q_heads / n_kv_heads >= 2 &&
-                    (int64_t)((seqlen_q + 255) / 256) * batch * n_q_heads >= 512);
+    // Deal workgroups to XCDs in chunks of the q-heads sharing a kv-head: in one
+    // fixed order when every (sequence, kv-head) then stays on one XCD (1), and in
+    // rounds of alternating XCD order on the eight-wave grids (the same rule as the
+    // prefill dispatch's) whose q-heads share kv-heads (2).
+    p.xcd_chunks = ((int64_t)batch * n_kv_heads) % 8 == 0 ? 1
+                   : (!cu_seqlens_q && head_dim <= 128 && n_q_heads / n_kv_heads >= 2 &&
+                      (int64_t)((seqlen_q + 255) / 256) * batch * n_q_heads >= 512) ? 2 : 0;
     p.v_scale = v_scale;
     const int mask = !causal ? attn::kMaskNone : (p.window > 0 ? attn::kMaskCausalWindow : attn::kMaskCausal);
     if (fp8) return status_of(attn::launch_prefill_f8kv(p, (int)dtype, head_dim, mask, (hipStream_t)hip_stream));

@@ -33,7 +33,9 @@ struct PrefillParams {
     // lse row order); key j is visible to a row at position P iff j <= P (causal)
     // and j >= P - window + 1. Nondecreasing within a sequence.
     const int32_t* positions;
-    int xcd_chunks;   // deal workgroups to XCDs in kv-head groups (batch * n_kv_heads % 8 == 0)
+    // Deal workgroups to XCDs in kv-head groups: 0 no, 1 in one order (batch * n_kv_heads
+    // % 8 == 0: each K/V stream on one XCD), 2 in rounds of alternating XCD order.
+    int xcd_chunks;
     float v_scale;    // FP8 K/V (prefill_f8kv): V row = v_scale * its codes (K's scale is folded into c)
 };
 

@@ -184,15 +184,16 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     // (workgroup i to XCD i % 8) and each XCD has its own L2. With
     // p.xcd_chunks the logical order is dealt out in chunks of `group`
     // workgroups — the q-heads that share one kv-head — with a whole chunk on
-    // one XCD. When batch * n_kv_heads is a multiple of 8 all chunks of one
+    // one XCD. Mode 1 (batch * n_kv_heads a multiple of 8): all chunks of one
     // (sequence, kv-head) then land on the same XCD, so each K/V stream is
-    // fetched into one L2 only (measured 8% faster on 16 packed prompts). The
-    // host also asks for chunks on eight-wave grids whose q-heads share
-    // kv-heads, where the heads of one q tile then share one L2 (32K causal,
-    // 8 q-heads over 1 kv-head: 2% faster together with the three-buffer
-    // pipeline). Successive rounds of chunks are dealt in opposite XCD order,
-    // so that with causal tiles (heaviest first) every XCD gets the same
-    // work. The last partial round keeps the plain order.
+    // fetched into one L2 only (measured 8% faster on 16 packed prompts).
+    // Mode 2 (eight-wave grids whose q-heads share kv-heads, fewer than 8
+    // streams): the heads of one q tile then share one L2, and successive
+    // rounds of chunks are dealt in opposite XCD order, so that with causal
+    // tiles (heaviest first) every XCD gets the same work (32K causal, 8
+    // q-heads over 1 kv-head: 2% faster together with the three-buffer
+    // pipeline). Mode 1 keeps one order, which alternating would break. The
+    // last partial round keeps the plain order.
     const int nbh = p.batch * p.n_q_heads;
     int wid = (int)blockIdx.x;
     if (p.xcd_chunks) {
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
         const int full = ((int)gridDim.x / round) * round;
         if (wid < full) {
             const int xcd = wid & 7, k = wid >> 3, r = k / G;
-            wid = (r * 8 + ((r & 1) ? 7 - xcd : xcd)) * G + k % G;
+            wid = (r * 8 + ((p.xcd_chunks == 2 && (r & 1)) ? 7 - xcd : xcd)) * G + k % G;
         }
     }
     // A grid that fits on the chip in one go (256 < workgroups <= 512, two
