@@ -691,19 +691,26 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             uint16_t* const vz = NB == 3 ? Vs2 : Vs1;
 #pragma unroll
             for (int c = tid; c < TILE / 8; c += PF_THREADS) *(uint4*)(vz + 8 * c) = make_uint4(0, 0, 0, 0);
+            // K(j_begin) and Q first: the first scores wait for those only, while
+            // V(j_begin) and K(j_begin + 1) arrive behind them.
             load_k_tile(Ks0, j_begin);
+            pf_load_q<D>(qf, qrow, my_q < sq, p.qflip);
             load_v_tile(Vs0, j_begin);
             load_k_tile(Ks1, min(j_begin + 1, j_last));
-            pf_load_q<D>(qf, qrow, my_q < sq, p.qflip);
-            wait_vmcnt<0>();
+            wait_vmcnt<2 * LPW>();
         }
-        __syncthreads();
+        barrier_lds();
         qk_tile(sa0, sa1, Ks0);
         if (!(wave_live && tile_full(j_begin))) {
             mask_half(sa0, j_begin * PF_BN, 0);
             mask_half(sa1, j_begin * PF_BN, 1);
         }
         rescale(max_tile(sa0, sa1));
+        if constexpr (!KV8) {
+            // V(j_begin) and K(j_begin + 1) in; every wave is past its reads of K(j_begin)
+            wait_vmcnt<0>();
+            barrier_lds();
+        }
         if constexpr (KV8) {
             // codes of V(j_begin + 1) and K(j_begin + 2) (in the loop's order), widened in the first step
             stage_clamped(Sv1, vbase8, p.vs.seq, min(j_begin + 1, j_last));
@@ -713,7 +720,6 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             load_k_tile(Ks2, min(j_begin + 2, j_last));
             load_v_tile(Vs1, min(j_begin + 1, j_last));
         } else {
-            __syncthreads();  // every wave is past its reads of K(j_begin)
             load_k_tile(Ks0, min(j_begin + 2, j_last));
         }
     }
@@ -1082,12 +1088,14 @@ __global__ __launch_bounds__(512, 1) void prefill_pair(PrefillParams p) {
         // The first refill of Vs1 may be range-limited: start it from zeros.
 #pragma unroll
         for (int c = tid; c < TILE / 8; c += PF_THREADS) *(uint4*)(Vs1 + 8 * c) = make_uint4(0, 0, 0, 0);
+        // K(j_begin) and Q first: the first scores wait for those only, while
+        // V(j_begin) and K(j_begin + 1) arrive behind them.
         load_k_tile(Ks0, j_begin);
+        pf_load_q<D>(qf, qrow, my_q < sq, p.qflip);
         load_v_tile(Vs0, j_begin);
         load_k_tile(Ks1, min(j_begin + 1, j_last));
-        pf_load_q<D>(qf, qrow, my_q < sq, p.qflip);
-        wait_vmcnt<0>();
-        __syncthreads();
+        wait_vmcnt<2 * LPW>();
+        barrier_lds();
         {
             const uint32_t kf = opaque(kfrag);
             sa = f32x16{};
@@ -1096,7 +1104,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pair(PrefillParams p) {
         }
         if (!(wave_live && tile_full(j_begin))) mask_block(sa, j_begin * PF_BN);
         const float mx = exchange_max(max_block(sa));
-        __syncthreads();  // the tile maxima are written; every wave is past its reads of K(j_begin)
+        // V(j_begin) and K(j_begin + 1) in; the tile maxima are written; every wave is past its reads of K(j_begin)
+        wait_vmcnt<0>();
+        barrier_lds();
         rescale(fmaxf(mx, Xm[pr][hh ^ 1][l32]));
         load_k_tile(Ks0, min(j_begin + 2, j_last));
     }
