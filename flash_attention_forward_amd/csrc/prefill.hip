@@ -80,6 +80,27 @@ __device__ __forceinline__ void pf_load_q(s16x8 (&qf)[D / 16], const uint16_t* q
     }
 }
 
+// The same in two parts, for a caller that issues the loads, then more loads,
+// and applies the mask only after a wait that covers them: the raw fragments,
+// then the mask and the sign flip. (pf_load_q's loads and masks in one place
+// can be compiled as a load, a wait and a mask per fragment.)
+template <int D>
+__device__ __forceinline__ void pf_load_q_raw(uint4 (&x)[D / 16], const uint16_t* qrow) {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) x[s] = *(const uint4*)(qrow + 16 * s);
+}
+template <int D>
+__device__ __forceinline__ void pf_mask_q(s16x8 (&qf)[D / 16], const uint4 (&x)[D / 16], bool valid, uint32_t qflip) {
+    const uint32_t keep = valid ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+        uint4 y = x[s];
+        y.x = (y.x & keep) ^ qflip; y.y = (y.y & keep) ^ qflip;
+        y.z = (y.z & keep) ^ qflip; y.w = (y.w & keep) ^ qflip;
+        qf[s] = __builtin_bit_cast(s16x8, y);
+    }
+}
+
 // One lane's half of an output row: O^T tile dt holds d = 32 dt + 8 rq + 4 hf
 // .. +4 in registers 4 rq .. 4 rq + 3, each multiplied by inv and rounded
 // (NaN throughout when nan_row: a NaN or +inf sink).
@@ -770,6 +791,21 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
 }
 
 // ---------------------------------------------------------------------------- D = 256, paired waves
+// The pair's probability exchange: this lane's eight packed pairs into
+// Xp[pair][half][0][lane] and Xp[pair][half][1][lane], 1 KB apart. The two
+// LDS writes are issued from inline assembly: written in C++, the compiler
+// guards the second one against the direct-to-LDS loads in flight (it does not
+// tell them apart from the K/V tiles being filled) with a wait for every
+// outstanding load, which drains the prefetch once per step. Only the barrier
+// that follows orders them: barrier_lds waits for lgkmcnt(0), and its
+// compiler fences keep every read of the exchange area on its far side.
+__device__ __forceinline__ void xp_write(uint4* dst, const uint32_t (&pk)[8]) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dst;
+    const u32x4_t d0 = {pk[0], pk[1], pk[2], pk[3]}, d1 = {pk[4], pk[5], pk[6], pk[7]};
+    asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %2 offset:1024" ::"v"(a), "v"(d0), "v"(d1));
+}
+
 // prefill_pair: head_dim 256 at two waves per SIMD. A 32-row wave holding all
 // of Q and O for 256 dims needs about 460 registers, which leaves one wave per
 // SIMD and every stall exposed. Here the two waves of a pair share 32 query
@@ -1039,8 +1075,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pair(PrefillParams p) {
             if (s % 2 == 1) prob_pair(s / 2);
             sched_fence();
         }
-        Xp[pr][hh][0][lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        Xp[pr][hh][1][lane] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+        xp_write(&Xp[pr][hh][0][lane], pk);
         // V(j) in; both halves' P(j) written; every wave is past its reads of K(j+1).
         wait_vmcnt<2 * LPW>();
         barrier_lds();
@@ -1128,6 +1163,405 @@ __global__ __launch_bounds__(512, 1) void prefill_pair(PrefillParams p) {
         pf_store_o<BF16, NDH>(o, inv,
                               (uint16_t*)p.o + o_at + (int64_t)my_q * p.os.seq + (int64_t)h * p.os.head + 128 * hh, hf,
                               nan_row);
+}
+
+// ---------------------------------------------------------------------------- D = 256, paired waves, persistent
+// prefill_pair_items: prefill_pair as a persistent loop over q tiles, for the
+// launches whose q tiles all carry the same kind of work (a sliding window or
+// no mask over one fixed-size sequence per batch entry). A workgroup that ends
+// pays for its successor's first loads (Q and three K/V tiles, about 224 KB
+// per CU) before the successor's first MFMA, and for its own stores; measured
+// on the D = 256 window workload that is about a quarter of each workgroup's
+// time. Here one workgroup per CU takes the items (q tile, batch, q-head)
+// blockIdx.x, blockIdx.x + gridDim.x, ... and the key loop runs on from one
+// item into the next: the tile stream (V one tile ahead, K three ahead)
+// continues into the next item's first tiles, the next item's Q is loaded
+// right after the score MFMAs that last use the current Q (one step before
+// it is needed), and the finished item's O is stored while the next one
+// starts. Every item covers an even number of key tiles (host-checked), so
+// every item starts on the same buffer parity and the step sequence of an
+// item is: pairs of ordinary steps, then a step that loads the next Q, then
+// the step that ends the item. The host also requires seqlen_kv and the
+// call's first visible key to be multiples of 64, so every tile loaded lies
+// whole inside [first visible key, seqlen_kv) and no load needs clamping
+// (tile rows below an item's own first key are keys that earlier q tiles
+// see, masked for this item's rows). The arithmetic per row is prefill_pair's.
+constexpr int kStepPlain = 0, kStepNextQ = 1, kStepLast = 2;
+
+template <bool BF16, int MASK>
+__global__ __launch_bounds__(512, 1) void prefill_pair_items(PrefillParams p) {
+    static_assert(MASK != kMaskCausal, "causal q tiles differ in work: prefill_pair");
+    constexpr int D = 256;
+    constexpr int NW = 8;
+    constexpr int PF_BM = 128;
+    constexpr int PF_THREADS = 64 * NW;
+    constexpr int CPR = D / 8;
+    constexpr int TILE = PF_BN * D;
+    constexpr int LPW = TILE / 512 / NW;
+    constexpr int NS = D / 16;
+    constexpr int NDH = 4;
+    constexpr int NPV = 4 * NDH;
+    constexpr int VPRE = 4;
+    static_assert(LPW == 4 && NS % LPW == 0 && NPV % LPW == 0, "four direct loads per wave and tile");
+    __shared__ __attribute__((aligned(16))) uint16_t Ks0[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks1[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs0[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs1[TILE];
+    __shared__ __attribute__((aligned(16))) uint4 Xp[4][2][2][64];
+    __shared__ float Xm[4][2][32];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pr = w & 3;
+    const int hh = w >> 2;
+    const int l32 = lane & 31;
+    const int hf = lane >> 5;
+    const int g = lane >> 4;
+    const int r16 = lane & 15;
+
+    const int nbh = p.batch * p.n_q_heads;
+    const int total = p.n_q_tiles * nbh;
+    const int sq = p.seqlen_q, skv = p.seqlen_kv, off = skv - sq;
+    const int key_max = skv - 1;
+    const int P = (int)gridDim.x;
+    const int M = (total - (int)blockIdx.x + P - 1) / P;  // this workgroup's items (>= 1: the grid is <= total)
+
+    // Item m of this workgroup -> (q tile, batch, q-head) and its key tiles,
+    // in prefill_pair's logical order (XCD chunks included).
+    struct Item {
+        int b, h, hk, q0, jb, nt;
+    };
+    auto item = [&](int m) __attribute__((always_inline)) {
+        int wid = (int)blockIdx.x + m * P;
+        if (p.xcd_chunks) {
+            const int G = p.group, round = 8 * G;
+            const int full = (total / round) * round;
+            if (wid < full) {
+                const int xcd = wid & 7, k = wid >> 3;
+                wid = ((k / G) * 8 + xcd) * G + k % G;
+            }
+        }
+        Item it;
+        const int qt = p.n_q_tiles - 1 - wid / nbh;
+        const int bh = wid % nbh;
+        it.b = bh / p.n_q_heads;
+        it.h = bh % p.n_q_heads;
+        it.hk = it.h / p.group;
+        it.q0 = qt * PF_BM;
+        const int qlast = min(it.q0 + PF_BM, sq) - 1;
+        int kv_lo = 0, kv_hi = skv;
+        if (MASK >= kMaskCausal) kv_hi = min(kv_hi, qlast + off + 1);
+        if (MASK == kMaskCausalWindow) kv_lo = max(0, it.q0 + off - p.window + 1);
+        it.jb = kv_lo / PF_BN;
+        it.nt = (kv_hi + PF_BN - 1) / PF_BN - it.jb;  // even and >= 2 (host-checked)
+        return it;
+    };
+    // This lane's row of an item: validity, positions, visible key range.
+    struct Rows {
+        int my_q, wpos0, wpos1, key_lo;
+        uint32_t key_span;
+        bool live;
+    };
+    auto rows_of = [&](const Item& it) __attribute__((always_inline)) {
+        Rows R;
+        const int wq0 = it.q0 + 32 * pr;
+        const int wq1 = min(wq0 + 31, sq - 1);
+        R.live = wq0 < sq;
+        R.my_q = wq0 + l32;
+        const int my_pos = R.my_q + off;
+        R.wpos0 = wq0 + off;
+        R.wpos1 = wq1 + off;
+        int key_hi = skv - 1, key_lo = 0;
+        if (MASK >= kMaskCausal) key_hi = min(key_hi, my_pos);
+        if (MASK == kMaskCausalWindow) key_lo = max(key_lo, my_pos - p.window + 1);
+        const bool none_visible = key_hi < key_lo;
+        R.key_span = none_visible ? 0u : (uint32_t)(key_hi - key_lo);
+        R.key_lo = none_visible ? INT_MIN / 2 : key_lo;
+        return R;
+    };
+    auto kbase_of = [&](const Item& it) __attribute__((always_inline)) {
+        return (const uint16_t*)p.k + (int64_t)it.b * p.ks.batch + (int64_t)it.hk * p.ks.head;
+    };
+    auto vbase_of = [&](const Item& it) __attribute__((always_inline)) {
+        return (const uint16_t*)p.v + (int64_t)it.b * p.vs.batch + (int64_t)it.hk * p.vs.head;
+    };
+    auto qrow_of = [&](const Item& it, const Rows& R) __attribute__((always_inline)) {
+        return (const uint16_t*)p.q + (int64_t)it.b * p.qs.batch + (int64_t)min(R.my_q, sq - 1) * p.qs.seq +
+               (int64_t)it.h * p.qs.head + 8 * hf;
+    };
+
+    // K/V staging as in prefill_pair, every tile whole (see above): one
+    // descriptor per tile, lane offsets computed once.
+    constexpr int RPL = 64 / CPR;
+    const int lrow = lane / CPR, lcs = lane % CPR;
+    const uint32_t kx = 16u * (uint32_t)(lcs ^ lrow);
+    const uint32_t vx = 16u * (uint32_t)(lcs ^ (4 * lrow));
+    const uint32_t kl = 2u * (uint32_t)lrow * (uint32_t)p.ks.seq, vl = 2u * (uint32_t)lrow * (uint32_t)p.vs.seq;
+    uint32_t kvo[LPW], vvo[LPW];
+#pragma unroll
+    for (int ii = 0; ii < LPW; ++ii) {
+        const int i = w * LPW + ii;
+        const uint32_t uk = (2 * i) & 15;
+        const uint32_t uv = 4 * ((2 * i) & 3);
+        uint32_t ko = kl + (kx ^ (16u * uk)) + (uint32_t)(2 * RPL * i) * (uint32_t)p.ks.seq;
+        uint32_t vo = vl + (vx ^ (16u * uv)) + (uint32_t)(2 * RPL * i) * (uint32_t)p.vs.seq;
+        asm volatile("" : "+v"(ko), "+v"(vo));
+        kvo[ii] = ko;
+        vvo[ii] = vo;
+    }
+    auto k_rsrc = [&](const Item& it, int j) __attribute__((always_inline)) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(kbase_of(it) + (int64_t)j * PF_BN * p.ks.seq), (short)0,
+                                                 0x7fffffff, 0x00020000);
+    };
+    auto v_rsrc = [&](const Item& it, int j) __attribute__((always_inline)) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(vbase_of(it) + (int64_t)j * PF_BN * p.vs.seq), (short)0,
+                                                 0x7fffffff, 0x00020000);
+    };
+    auto load_part = [&](uint16_t* dst, __amdgpu_buffer_rsrc_t rs, uint32_t voff, int ii) __attribute__((always_inline)) {
+        const int i = w * LPW + ii;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 512 * i), 16, voff, 0, 0, 0);
+    };
+    auto load_k_tile = [&](uint16_t* dst, const Item& it, int j) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rs = k_rsrc(it, j);
+#pragma unroll
+        for (int ii = 0; ii < LPW; ++ii) load_part(dst, rs, kvo[ii], ii);
+    };
+    auto load_v_tile = [&](uint16_t* dst, const Item& it, int j) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rs = v_rsrc(it, j);
+#pragma unroll
+        for (int ii = 0; ii < LPW; ++ii) load_part(dst, rs, vvo[ii], ii);
+    };
+
+    constexpr float kLazyRescale = 8.0f;
+    float m_i = kMaxInit, l_i = 0.f;
+    f32x16 o[NDH];
+#pragma unroll
+    for (int dt = 0; dt < NDH; ++dt) o[dt] = f32x16{};
+    const uint32_t one2 = BF16 ? 0x3F803F80u : 0x3C003C00u;
+
+    auto tile_full = [&](int j, const Rows& R) __attribute__((always_inline)) {
+        const int kv0 = j * PF_BN;
+        bool f = kv0 + PF_BN <= skv;
+        if (MASK >= kMaskCausal) f &= kv0 + PF_BN - 1 <= R.wpos0;
+        if (MASK == kMaskCausalWindow) f &= kv0 >= R.wpos1 - p.window + 1;
+        return f;
+    };
+    const uint32_t kfrag = ((uint32_t)(l32 * D * 2) | (16u * (uint32_t)(hf ^ pf_kswz<D>(l32)))) + (uint32_t)hh * (32u * D * 2);
+    const int vr0 = 4 * hf + (r16 >> 2);
+    const int vcl = 2 * (g & 1) + ((r16 & 3) >> 1);
+    const uint32_t vfrag = ((uint32_t)(vr0 * D * 2) | (16u * (uint32_t)(vcl ^ pf_vswz<D>(vr0))) | (8u * (r16 & 1))) ^
+                           (256u * (uint32_t)hh);
+    auto opaque = [](uint32_t x) __attribute__((always_inline)) {
+        asm volatile("" : "+v"(x));
+        return x;
+    };
+    auto lds_frag8 = [](const uint16_t* base, uint32_t byte_off) __attribute__((always_inline)) {
+        return *(const s16x8*)((const char*)base + byte_off);
+    };
+    auto mask_block = [&](f32x16& sacc, int kv0, const Rows& R) __attribute__((always_inline)) {
+        const int base = kv0 + 32 * hh + 4 * hf - R.key_lo;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint32_t d = (uint32_t)(base + 8 * (r >> 2) + (r & 3));
+            sacc[r] = d <= R.key_span ? sacc[r] : kMaskedScore;
+        }
+    };
+    auto max_block = [&](const f32x16& sc) __attribute__((always_inline)) {
+        float mx = kMaskedScore;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = max3f(mx, sc[r], sc[r + 1]);
+        return max_with_other_half(mx);
+    };
+    auto rescale = [&](float mx) __attribute__((always_inline)) {
+        const float m_cand = mx * p.c;
+        const bool grow = m_cand > m_i + kLazyRescale;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float m_new = grow ? m_cand : m_i;
+            const float alpha = fast_exp2(m_i - m_new);
+            m_i = m_new;
+            l_i *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDH; ++dt) o[dt] *= alpha;
+        }
+    };
+    auto exchange_max = [&](float mx) __attribute__((always_inline)) {
+        if (hf == 0) Xm[pr][hh][l32] = mx;
+        return mx;
+    };
+    // The finished item's output (and log-sum-exp), then a fresh softmax state.
+    auto finish = [&](const Item& it, const Rows& R) __attribute__((always_inline)) {
+        float l_tot = sum_with_other_half(l_i);
+        float m_fin = m_i;
+        const float sink = p.sinks ? p.sinks[it.h] : -__builtin_inff();
+        const bool nan_row = sink_gives_nan(sink);
+        const float osc = p.sinks ? fold_sink(sink * kLog2e, m_fin, l_tot) : 1.f;
+        const float inv = l_tot > 0.f ? osc / l_tot : 0.f;
+        if (p.lse && hh == 0 && hf == 0 && R.live && R.my_q < sq)
+            pf_store_lse(&p.lse[((int64_t)it.b * sq + R.my_q) * p.n_q_heads + it.h], m_fin, l_tot, nan_row);
+        if (R.live && R.my_q < sq)
+            pf_store_o<BF16, NDH>(o, inv,
+                                  (uint16_t*)p.o + (int64_t)it.b * p.os.batch + (int64_t)R.my_q * p.os.seq +
+                                      (int64_t)it.h * p.os.head + 128 * hh,
+                                  hf, nan_row);
+#pragma unroll
+        for (int dt = 0; dt < NDH; ++dt) o[dt] = f32x16{};
+        l_i = 0.f;
+        m_i = kMaxInit;
+    };
+
+    s16x8 qf[NS];
+    Item cur = item(0);
+    Rows cr = rows_of(cur);
+    Item nx = M > 1 ? item(1) : cur;  // the current item stands in for a missing next one
+    Rows nr = rows_of(nx);
+    int m_cur = 0;
+
+    // Step r of item cur (prefill_pair's step): the score MFMAs of the tile
+    // after r (the next item's first tile in the last step, with the next Q
+    // and masked for the next item's rows) beside the exponentials of tile r;
+    // P exchange; P V of tile r; row sums; the tile max of the tile after r;
+    // then, in the last step, the item's output and a fresh state before m
+    // is settled for the next item. Loads: V one tile ahead and K three
+    // ahead in the stream of tiles (cur's, then nx's, then the item after
+    // nx when nx has two tiles); the step before the last also loads the
+    // next item's Q, and its waits allow for those NS loads.
+    auto step = [&](int kind, int r, f32x16& c, f32x16& n, uint16_t* Kn, uint16_t* Vc, uint16_t* Vl)
+                    __attribute__((always_inline)) {
+        const int j = cur.jb + r;
+        const uint32_t kf = opaque(kfrag);
+        const uint32_t vf = opaque(vfrag);
+        s16x8 ka[NS];
+        s16x8 vb[NPV];
+        uint32_t pk[8];
+        auto kread = [&](int s) __attribute__((always_inline)) { ka[s] = lds_frag8(Kn, kf ^ (32u * s)); };
+        auto vread = [&](int i) __attribute__((always_inline)) {
+            const int u = i / NDH, dt = i % NDH;
+            const char* vb0 = (const char*)Vc + (vf ^ (64u * dt));
+            vb[i] = concat4(lds_read_tr16((const uint16_t*)(vb0 + 2 * D * (16 * u))),
+                            lds_read_tr16((const uint16_t*)(vb0 + 2 * D * (16 * u + 8))));
+        };
+        const float neg_m = -m_i;
+        auto prob_pair = [&](int i) __attribute__((always_inline)) {
+            pk[i] = pack2_16<BF16>(fast_exp2(fmaf(c[2 * i], p.c, neg_m)), fast_exp2(fmaf(c[2 * i + 1], p.c, neg_m)));
+            asm volatile("" ::"v"(pk[i]));
+        };
+        // the V tile one ahead and the K tile three ahead in the stream
+        const __amdgpu_buffer_rsrc_t vrs = kind == kStepLast ? v_rsrc(nx, nx.jb) : v_rsrc(cur, j + 1);
+        __amdgpu_buffer_rsrc_t krs;
+        if (kind == kStepPlain) {
+            krs = r + 3 < cur.nt ? k_rsrc(cur, j + 3) : k_rsrc(nx, nx.jb);
+        } else if (kind == kStepNextQ) {
+            krs = k_rsrc(nx, nx.jb + 1);
+        } else if (nx.nt > 2) {
+            krs = k_rsrc(nx, nx.jb + 2);
+        } else {
+            const Item n2 = m_cur + 2 < M ? item(m_cur + 2) : nx;
+            krs = k_rsrc(n2, n2.jb);
+        }
+        kread(0);
+        kread(1);
+        sched_fence();
+        n = f32x16{};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            n = mfma32x32x16<BF16>(ka[s], qf[s], n);
+            if (s % (NS / LPW) == 0) load_part(Vl, vrs, vvo[s / (NS / LPW)], s / (NS / LPW));
+            if (s + 2 < NS) kread(s + 2);
+            if (s % 2 == 1) prob_pair(s / 2);
+            sched_fence();
+        }
+        if (kind == kStepNextQ) pf_load_q<D>(qf, qrow_of(nx, nr), nr.my_q < sq, p.qflip);
+        xp_write(&Xp[pr][hh][0][lane], pk);
+        // V(j) in; both halves' P(j) written; every wave is past its reads of the K tile after j.
+        if (kind == kStepNextQ) wait_vmcnt<2 * LPW + NS>(); else wait_vmcnt<2 * LPW>();
+        barrier_lds();
+        uint4 pq[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pq[e] = Xp[pr][e >> 1][e & 1][lane];
+#pragma unroll
+        for (int i = 0; i < VPRE; ++i) vread(i);
+        sched_fence();
+        float mx = kMaskedScore;
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            const int u = i / NDH, dt = i % NDH;
+            o[dt] = mfma32x32x16<BF16>(vb[i], __builtin_bit_cast(s16x8, pq[u]), o[dt]);
+            if (i % (NPV / LPW) == 0) load_part(Kn, krs, kvo[i / (NPV / LPW)], i / (NPV / LPW));
+            if (i + VPRE < NPV) vread(i + VPRE);
+            if (i % 2 == 0) mx = max3f(mx, n[i], n[i + 1]);
+            sched_fence();
+        }
+        const uint32_t* pw = (const uint32_t*)pq;
+        float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+            ps0 = dot2_16<BF16>(pw[e], one2, ps0);
+            ps1 = dot2_16<BF16>(pw[e + 1], one2, ps1);
+        }
+        l_i += ps0 + ps1;
+        mx = max_with_other_half(mx);
+        const Rows& sr = kind == kStepLast ? nr : cr;
+        const int sj = kind == kStepLast ? nx.jb : j + 1;
+        if (!(sr.live && tile_full(sj, sr))) {
+            mask_block(n, sj * PF_BN, sr);
+            mx = fminf(mx, max_block(n));
+        }
+        exchange_max(mx);
+        // The K tile two ahead is in; both halves' tile maxima written; every wave is past its reads of V(j).
+        if (kind == kStepNextQ) wait_vmcnt<2 * LPW + NS>(); else wait_vmcnt<2 * LPW>();
+        barrier_lds();
+        if (kind == kStepLast) finish(cur, cr);
+        rescale(fmaxf(mx, Xm[pr][hh ^ 1][l32]));
+    };
+
+    // Prologue (the first item): K(jb) and Q first, then V(jb) and K(jb+1);
+    // the first scores and their m; then the K tile two ahead.
+    f32x16 sa, sb;
+#pragma unroll
+    for (int c = tid; c < TILE / 8; c += PF_THREADS) *(uint4*)(Vs1 + 8 * c) = make_uint4(0, 0, 0, 0);
+    {
+        uint4 qraw[NS];
+        load_k_tile(Ks0, cur, cur.jb);
+        pf_load_q_raw<D>(qraw, qrow_of(cur, cr));
+        sched_fence();
+        load_v_tile(Vs0, cur, cur.jb);
+        load_k_tile(Ks1, cur, cur.jb + 1);
+        wait_vmcnt<2 * LPW>();
+        barrier_lds();
+        pf_mask_q<D>(qf, qraw, cr.my_q < sq, p.qflip);
+    }
+    {
+        const uint32_t kf = opaque(kfrag);
+        sa = f32x16{};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) sa = mfma32x32x16<BF16>(lds_frag8(Ks0, kf ^ (32u * s)), qf[s], sa);
+    }
+    if (!(cr.live && tile_full(cur.jb, cr))) mask_block(sa, cur.jb * PF_BN, cr);
+    {
+        const float mx = exchange_max(max_block(sa));
+        wait_vmcnt<0>();
+        barrier_lds();
+        rescale(fmaxf(mx, Xm[pr][hh ^ 1][l32]));
+    }
+    if (cur.nt > 2) load_k_tile(Ks0, cur, cur.jb + 2);
+    else load_k_tile(Ks0, nx, nx.jb);
+
+    for (int m = 0; m < M; ++m) {
+        const int nt = cur.nt;
+        for (int r = 0; r < nt - 2; r += 2) {
+            step(kStepPlain, r, sa, sb, Ks1, Vs0, Vs1);
+            step(kStepPlain, r + 1, sb, sa, Ks0, Vs1, Vs0);
+        }
+        step(kStepNextQ, nt - 2, sa, sb, Ks1, Vs0, Vs1);
+        step(kStepLast, nt - 1, sb, sa, Ks0, Vs1, Vs0);
+        cur = nx;
+        cr = nr;
+        m_cur = m + 1;
+        nx = m + 2 < M ? item(m + 2) : cur;
+        nr = rows_of(nx);
+    }
+    wait_vmcnt<0>();
 }
 
 // ---------------------------------------------------------------------------- FP8 K/V
@@ -1505,9 +1939,45 @@ static hipError_t launch_mfma_nw(PrefillParams p, int mask, hipStream_t s) {
 // halve that waste (measured 8% faster on 16 prompts of 256..4096 tokens).
 constexpr int kPrefillWideMinWorkgroups = 512;
 
+// The persistent D = 256 kernel runs one workgroup per CU (MI355X: 256 CUs, a
+// multiple of the 8 XCDs, so every item of a workgroup stays on the XCD the
+// plain launch would give it) when there are at least two items per CU, the
+// launch is dense with no per-row positions, the mask is a window or none (q
+// tiles of like work), and every q tile covers an even number (>= 2) of
+// 64-key tiles.
+constexpr int kPairItemsWorkgroups = 256;
+
+static bool pair_items_ok(const PrefillParams& p, int mask) {
+    if (p.cu_seqlens_q || p.positions || mask == kMaskCausal || p.seqlen_kv <= 0 || p.seqlen_kv % 64 != 0) return false;
+    if ((long)p.n_q_tiles * p.batch * p.n_q_heads < 2L * kPairItemsWorkgroups) return false;
+    const int sq = p.seqlen_q, skv = p.seqlen_kv, off = skv - sq;
+    // the call's first visible key (the first row's window start) on a tile boundary
+    if (mask == kMaskCausalWindow && std::max(0, off - p.window + 1) % 64 != 0) return false;
+    for (int t = 0; t < p.n_q_tiles; ++t) {
+        const int q0 = t * 128, qlast = std::min(q0 + 128, sq) - 1;
+        int kv_lo = 0, kv_hi = skv;
+        if (mask == kMaskCausalWindow) {
+            kv_hi = std::min(kv_hi, qlast + off + 1);
+            kv_lo = std::max(0, q0 + off - p.window + 1);
+        }
+        if (kv_hi <= kv_lo) return false;
+        const int nt = (kv_hi + 63) / 64 - kv_lo / 64;
+        if (nt < 2 || nt % 2 != 0) return false;
+    }
+    return true;
+}
+
 template <bool BF16>
 static hipError_t launch_pair(PrefillParams p, int mask, hipStream_t s) {
     p.n_q_tiles = (p.seqlen_q + 127) / 128;
+    if (pair_items_ok(p, mask)) {
+        const dim3 grid((unsigned)kPairItemsWorkgroups), block(512);
+        if (mask == kMaskCausalWindow)
+            hipLaunchKernelGGL((prefill_pair_items<BF16, kMaskCausalWindow>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((prefill_pair_items<BF16, kMaskNone>), grid, block, 0, s, p);
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)p.n_q_tiles * p.batch * p.n_q_heads), block(512);
     switch (mask) {
         case kMaskNone: hipLaunchKernelGGL((prefill_pair<BF16, kMaskNone>), grid, block, 0, s, p); break;
