@@ -37,7 +37,8 @@ CONTEXT = "f16_gqa7_causal_2k"  # the 7B-shaped 2K prefill the minfer page times
 PAGES_CONTEXT_MS_PER_LAYER = 8.5   # minfer 8n page, results: 7B @2K prefill attention, on its own (NVIDIA) GPU
 DEFAULT_SPLIT_LEN = 4096  # decode keys per split (timed sweep on the paged workload: 416 us against 420 at 2048
                           # and 448 at 1024 with four kv-heads per workgroup)
-FP8_SPLIT_LEN = 1024      # the FP8 split measured best at 1024 (4096: 4% slower)
+FP8_SPLIT_LEN = 2048      # FP8 split sweep (eight kv-heads per workgroup): 1536: 234 us, 1792: 214, 2048: 218,
+                          # 2304: 247, 4096: 250; four kv-heads per workgroup: 230 us at 512, 233 at 1024
 
 
 def visible_pairs(spec) -> int:

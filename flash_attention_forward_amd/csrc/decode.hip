@@ -135,12 +135,19 @@ template <int D>
 constexpr int dc_max_heads() {
     return D >= 256 ? 1 : 4;
 }
-// decode_split_f8 holds one 16-bit V tile and one byte K tile per wave (24 KB *
-// D / 128), so four kv-heads fit under the same 64 KB (two at D = 256).
+// decode_split_f8 holds one 16-bit V tile and one byte K tile per wave (12 KB *
+// D / 128). Eight kv-heads (97 KB at D = 128, one workgroup per CU) read each
+// token's whole row of the paged FP8 workload (1 KB) together; four (two
+// workgroups per CU) read it in two halves. Eight measured 5-7% faster with
+// 1792- to 2048-token splits on the paged workload and 8% slower with
+// 512-token splits, so the launch takes eight only on grids of at least
+// kDecodeF8WideGrid workgroups (with fewer, eight-wave workgroups leave CUs
+// idle). D = 256 holds two.
 template <int D>
 constexpr int dc_max_heads_f8() {
-    return D >= 256 ? 2 : 4;
+    return D >= 256 ? 2 : 8;
 }
+constexpr int64_t kDecodeF8WideGrid = 512;
 
 // 16-byte chunk swizzle of a K row in LDS: the 16 lanes of a fragment read hit
 // rows r..r+15 at one chunk, spread over 16 bank groups.
@@ -849,7 +856,8 @@ template <bool BF16, int D, int QB>
 static void launch_decode_q(const DecodeParams& p, hipStream_t s) {
     if (p.kv_fp8) {
         constexpr int MH = dc_max_heads_f8<D>();
-        if (MH >= 8 && p.n_kv_heads % 8 == 0) launch_decode_f8_hw<BF16, D, (MH >= 8 ? 8 : 1), QB>(p, s);
+        const bool wide = (int64_t)p.batch * p.max_splits * (p.n_kv_heads / 8) >= kDecodeF8WideGrid;
+        if (MH >= 8 && p.n_kv_heads % 8 == 0 && wide) launch_decode_f8_hw<BF16, D, (MH >= 8 ? 8 : 1), QB>(p, s);
         else if (MH >= 4 && p.n_kv_heads % 4 == 0) launch_decode_f8_hw<BF16, D, (MH >= 4 ? 4 : 1), QB>(p, s);
         else if (MH >= 2 && p.n_kv_heads % 2 == 0) launch_decode_f8_hw<BF16, D, (MH >= 2 ? 2 : 1), QB>(p, s);
         else launch_decode_f8_hw<BF16, D, 1, QB>(p, s);

@@ -93,6 +93,32 @@ def test_fp8_decode_flat_matches_paged_bitwise():
     check(a, oracle_fp8(inp), "bf16", "fp8 flat")
 
 
+def test_fp8_decode_eight_and_four_head_workgroups_bitwise():
+    """The launch takes eight kv-heads per workgroup on grids of at least 512 workgroups and four
+    below; a workspace with more splits than needed widens the grid (the extra splits are empty), so
+    the same call runs both shapes, which must give the same bits (each wave's arithmetic is the same)."""
+    import flash_attention_forward_amd as F
+
+    torch = torch_cuda()
+    inp = small(7, batch=8, len_lo=1, len_hi=4000)
+    s = inp.spec
+    say("fp8 decode eight vs four heads per workgroup")
+    t = fp8_tensors(inp)
+    maxlen = s.max_pages_per_seq * s.page_size
+    ms = F.attn.max_splits_for(maxlen, 256)
+    assert s.batch * ms * (s.n_kv_heads // 8) < 512 <= s.batch * 64 * (s.n_kv_heads // 8)
+    outs = []
+    for splits in (ms, 64):
+        ws = F.DecodeWorkspace(s.batch, s.s_active, s.n_q_heads, s.head_dim, splits, "cuda")
+        o = F.decode(t["q"], t["k"], t["v"], t["cache_len"], block_table=t["block_table"], scale=s.scale_f32,
+                     split_len=256, max_len=maxlen, workspace=ws, k_scale=s.k_scale, v_scale=s.v_scale)
+        torch.cuda.synchronize()
+        outs.append(host64(o, s.dtype))
+    np.testing.assert_array_equal(outs[0], outs[1])
+    ref, bound = decode_with_bound(inp)
+    check(outs[1], ref, s.dtype, "fp8 eight heads per workgroup", bound=bound)
+
+
 def test_fp8_decode_full_size_every_sequence():
     """The paged-decode workload with an FP8 cache, launched as the benchmark launches it, against
     the oracle on all 32 sequences."""
