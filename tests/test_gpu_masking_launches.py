@@ -1,7 +1,7 @@
 """Mask index logic of the prefill, bit-exact, on the launch shapes the full-size
 workloads take: the eight-wave 256-row launch (D = 64 and 128, with and without
 the kv-head chunking across XCDs), the four-wave launch at D = 64 and 128, the
-paired-wave D = 256 launch,
+paired-wave D = 256 launch and its persistent form,
 causal and sliding-window masks, Sq < Skv, packed sequences and FP8 K/V.
 
 * Masked-key poison inside loaded tiles. Keys above a cut (causal) and below a
@@ -47,7 +47,20 @@ LAUNCHES = {
     # the four-wave launch of the 2K f16 prefill (one round of causal row tiles), and D64 with a window
     "wave4_f16_gqa_causal_2k": W.PrefillSpec(1, 8, 2, 2048, 2048, 128, "f16", causal=True),
     "wave4_bf16_d64_window_1k": W.PrefillSpec(2, 4, 2, 1200, 1200, 64, "bf16", causal=True, window=400),
+    # the persistent D = 256 launch (512 q tiles, one workgroup per CU walking its tiles): a window
+    # that is not a multiple of 64, and a cached prefix whose first visible key is past 0
+    "persistent_d256_window1000_4k": W.PrefillSpec(2, 8, 4, 4096, 4096, 256, "bf16", causal=True, window=1000),
+    "persistent_d256_prefix_window385": W.PrefillSpec(2, 8, 4, 4096, 4608, 256, "bf16", causal=True, window=385),
 }
+PERSISTENT = [n for n in LAUNCHES if n.startswith("persistent")]
+
+
+@pytest.mark.parametrize("name", PERSISTENT)
+def test_persistent_shapes_take_the_persistent_launch(name):
+    from test_gpu_prefill_d256_persistent import eligible
+
+    s = LAUNCHES[name]
+    assert eligible(s.batch, s.n_q_heads, s.seqlen_q, s.seqlen_kv, s.window)
 
 
 def random_finite(rng, shape, dtype):
