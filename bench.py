@@ -229,7 +229,7 @@ def cpu_baseline(inp, seconds_target: float = 15.0, what: str = "the 32768-token
         dt = time.perf_counter() - t
         return len(rows), dt, 4.0 * s.head_dim * row_pairs(s, rows)
 
-    n, dt, fl = run(min(256, total))
+    n, dt, fl = run(min(4096, total))  # a pilot large enough that the per-row time is not its start-up cost
     if n < total:
         n, dt, fl = run(int(min(total, 200000, max(256, n * seconds_target / max(dt, 1e-3)))))
     sample = "all" if n >= total else f"{n} random"
@@ -742,7 +742,7 @@ def main():
         fo_timed = fo.cpu()
         log("cpu baseline (oracle)")
         line["cpu_model"] = cpu_model()
-        line["cpu_baseline"] = cpu_baseline(pin, seconds_target=10.0)
+        line["cpu_baseline"] = cpu_baseline(pin, seconds_target=12.0)
         line["cpu_baseline_decode"] = cpu_baseline_decode(din)
         line["cpu_baselines"] = {
             "fp32_d64_s256": cpu_baseline(fin, 3.0, "the fp32 256-token workload"),
