@@ -175,10 +175,10 @@ __device__ __forceinline__ void widen_e4m3x16(uint4 x, uint4& lo, uint4& hi) {
 // for scale times its value; the host folds K's scale into c, V's scale
 // multiplies the output) -- the decode page's quantised cache read by a
 // prefill. Eight waves and D = 128 only. The codes of each tile go HBM->LDS
-// into a staging area with the same direct loads, each lane's 16 bytes to its
-// own 16-byte slot; at the end of the step before the tile is needed the same
-// lane widens them (exactly) and writes them into the 16-bit tile layout
-// below, and the end-of-step barrier publishes them. A lane only reads back
+// into a staging area with the same direct loads, each wave's load to its own
+// kilobyte (8 rows); at the end of the step before the tile is needed the
+// same wave widens them (exactly) and writes them into the 16-bit tile layout
+// below, and the end-of-step barrier publishes them. A wave only reads back
 // what its own load wrote, so the staging needs no barrier of its own, and
 // the 16-bit tiles, the fragment reads and all of the math are the 16-bit
 // path's.
@@ -386,10 +386,15 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
 
     // FP8 codes (KV8): one direct load per wave, tensor and tile; lane
     // c8 = 64 w + lane takes codes 16 (c8 % 8) .. +16 of tile row c8 / 8 into
-    // staging bytes 16 c8 .. +16, and later widens exactly those into the
-    // swizzled 16-bit tile. Range-limited loads of the last tile drop the rows
-    // past key_max, whose staging bytes keep the codes of an earlier tile
-    // (visible keys: finite), masked like every row past the end.
+    // staging bytes 16 c8 .. +16, so wave w's kilobyte holds rows 8w .. 8w + 7.
+    // The wave widens them in another order: lane l takes codes
+    // 8 (l % 16) .. +8 of rows 8w + l / 16 and 8w + 4 + l / 16, so the 16 lanes
+    // of each 16-byte store write the 16 chunks of one row (16 distinct bank
+    // groups; the load order, two adjacent chunks of two rows per 16 lanes, put
+    // two lanes on each even group of the V tile). Range-limited loads of the
+    // last tile drop the rows past key_max, whose staging bytes keep the codes
+    // of an earlier tile (visible keys: finite), masked like every row past
+    // the end.
     const int c8 = 64 * w + lane, row8 = c8 >> 3, col8 = 16 * (c8 & 7);
     const uint8_t* const kbase8 = (const uint8_t*)p.k + k_at + (int64_t)hk * p.ks.head;
     const uint8_t* const vbase8 = (const uint8_t*)p.v + v_at + (int64_t)hk * p.vs.head;
@@ -417,15 +422,20 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 1024 * w), 16,
                                                  (uint32_t)(key - kv0) * (uint32_t)seq + (uint32_t)col8, 0, 0, 0);
     };
-    auto stage_read = [&](const uint8_t* src) __attribute__((always_inline)) { return *(const uint4*)(src + 16 * c8); };
+    const int wr0 = 8 * w + (lane >> 4), wch = lane & 15;
+    auto stage_read = [&](const uint8_t* src) __attribute__((always_inline)) {
+        const uint8_t* b0 = src + 1024 * w + 128 * (lane >> 4) + 8 * wch;
+        const uint2 a = *(const uint2*)b0, b = *(const uint2*)(b0 + 512);
+        return make_uint4(a.x, a.y, b.x, b.y);
+    };
     auto widen_store = [&](uint16_t* dst, uint4 x, bool is_k) __attribute__((always_inline)) {
         uint4 lo, hi;
         widen_e4m3x16<BF16>(x, lo, hi);
-        char* drow = (char*)dst + row8 * D * 2;
-        const int sw = is_k ? pf_kswz<D>(row8) : pf_vswz<D>(row8);
-        const int cc = c8 & 7;
-        *(uint4*)(drow + 16 * ((2 * cc) ^ sw)) = lo;
-        *(uint4*)(drow + 16 * ((2 * cc + 1) ^ sw)) = hi;
+        const int r1 = wr0 + 4;
+        const int s0 = is_k ? pf_kswz<D>(wr0) : pf_vswz<D>(wr0);
+        const int s1 = is_k ? pf_kswz<D>(r1) : pf_vswz<D>(r1);
+        *(uint4*)((char*)dst + wr0 * D * 2 + 16 * (wch ^ s0)) = lo;
+        *(uint4*)((char*)dst + r1 * D * 2 + 16 * (wch ^ s1)) = hi;
     };
     auto widen_tile = [&](uint16_t* dst, const uint8_t* src, bool is_k) __attribute__((always_inline)) {
         widen_store(dst, stage_read(src), is_k);
