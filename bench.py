@@ -568,15 +568,18 @@ def main():
     dlse = torch.empty((dspec.batch, dspec.s_active, dspec.n_q_heads), dtype=torch.float32, device=dev)
     for _ in range(2):
         F.attn_prefill_fwd_ex(q, k, v, o, pspec.scale_f32, True, 0, plse, psinks)
-    # back-to-back launches between two events (the host stays ahead of the GPU)
+    # groups of back-to-back launches between two events (the host stays ahead of the GPU),
+    # alternating with the same number of plain launches, so that both run at the same clock
+    # (back-to-back prefills draw more power than the main loop's, and the clock drifts over
+    # the run): medians of three groups each
     n_ex = 8
-    pev = [ev(), ev()]
-    pev[0].record(stream)
-    for _ in range(n_ex):
-        F.attn_prefill_fwd_ex(q, k, v, o, pspec.scale_f32, True, 0, plse, psinks)
-    pev[1].record(stream)
-    torch.cuda.synchronize()
-    pre_ex_ms = pev[0].elapsed_time(pev[1]) / n_ex
+    ex_groups, plain_groups = [], []
+    for _ in range(3):
+        plain_groups.append(back_to_back(lambda: F.attn_prefill_fwd(q, k, v, o, pspec.scale_f32, True, 0), n=n_ex))
+        ex_groups.append(back_to_back(lambda: F.attn_prefill_fwd_ex(q, k, v, o, pspec.scale_f32, True, 0, plse, psinks),
+                                      n=n_ex))
+    pre_ex_ms = float(np.median(ex_groups))
+    pre_plain_alt_ms = float(np.median(plain_groups))
     # the combine takes a few microseconds, less than one host call: each timed
     # group of combines is queued behind a split, so the GPU never waits for the host
     comb_ex = []
@@ -708,9 +711,12 @@ def main():
         },
         "sinks_and_lse": {
             "prefill_ex_ms": round(pre_ex_ms, 4),
+            "prefill_plain_ms_alternating": round(pre_plain_alt_ms, 4),
             "prefill_ex_tflops": round(prefill_flops(pspec) / (pre_ex_ms * 1e-3) / 1e12, 2),
             "decode_combine_ex_us": round(comb_ex_us, 2),
-            "note": "attn_prefill_fwd_ex / attn_decode_combine_ex with one sink per q-head and the lse output",
+            "note": "attn_prefill_fwd_ex / attn_decode_combine_ex with one sink per q-head and the lse output; "
+                    "the prefill timed in groups of back-to-back launches alternating with groups of the plain "
+                    "prefill (prefill_plain_ms_alternating), medians of three groups each",
         },
         "decode_variants": {
             "speculative_s_active4_us": round(spec_us, 2),
