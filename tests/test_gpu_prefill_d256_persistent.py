@@ -27,6 +27,8 @@ SHAPES = {
     "bf16_nomask_16k_1k": (1, 4, 2, 16384, 1024, "bf16", 0),
     "f16_window1024_mha_4k": (1, 16, 16, 4096, 4096, "f16", 1024),
     "bf16_prefix_window385": (2, 8, 4, 4096, 4608, "bf16", 385),
+    # a ragged last q tile (rows 3968..3999): three of its four wave pairs hold no rows
+    "bf16_nomask_ragged_4000": (1, 16, 8, 4000, 1024, "bf16", 0),
 }
 
 
@@ -63,7 +65,8 @@ def test_shapes_take_the_persistent_launch(name):
     assert eligible(B, Hq, Sq, Skv, w)
 
 
-@pytest.mark.parametrize("name", ["bf16_window1024_8k", "bf16_nomask_16k_1k", "bf16_prefix_window385"])
+@pytest.mark.parametrize("name", ["bf16_window1024_8k", "bf16_nomask_16k_1k", "bf16_prefix_window385",
+                                  "bf16_nomask_ragged_4000"])
 def test_persistent_equals_the_per_tile_kernel(name):
     torch = torch_cuda()
     import flash_attention_forward_amd as F
