@@ -745,8 +745,13 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             // V(j_begin) and K(j_begin + 1) arrive behind them.
             load_k_tile(Ks0, j_begin);
             pf_load_q<D>(qf, qrow, my_q < sq, p.qflip);
-            load_v_tile(Vs0, j_begin);
-            load_k_tile(Ks1, min(j_begin + 1, j_last));
+            if constexpr (NB == 2) {
+                load_k_tile(Ks1, min(j_begin + 1, j_last));
+                load_v_tile(Vs0, j_begin);
+            } else {
+                load_v_tile(Vs0, j_begin);
+                load_k_tile(Ks1, min(j_begin + 1, j_last));
+            }
             wait_vmcnt<2 * LPW>();
         }
         barrier_lds();
@@ -757,8 +762,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
         }
         rescale(max_tile(sa0, sa1));
         if constexpr (!KV8) {
-            // V(j_begin) and K(j_begin + 1) in; every wave is past its reads of K(j_begin)
-            wait_vmcnt<0>();
+            // K(j_begin + 1) in (two buffers: V(j_begin) may still be in flight;
+            // step 0's mid-step wait covers it); every wave is past its reads of K(j_begin)
+            if constexpr (NB == 2) wait_vmcnt<LPW>(); else wait_vmcnt<0>();
             barrier_lds();
         }
         if constexpr (KV8) {
