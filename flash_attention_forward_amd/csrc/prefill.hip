@@ -196,10 +196,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     // cover reads of the other: two of each (two barriers per key tile) for
     // four waves, three of each (one barrier per key tile) for eight, whose
     // one workgroup per CU has the LDS for them.
-    constexpr int NB = NW == 8 ? 3 : 2;
+    constexpr int NB = NW == 8 ? 3 : 2;                  // V buffers
+    constexpr int NBK = NW == 8 || D <= 128 ? 3 : 2;     // K buffers: three give one barrier per key tile
     __shared__ __attribute__((aligned(16))) uint16_t Ks0[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Ks1[TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t Ks2[NB == 3 ? TILE : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks2[NBK == 3 ? TILE : 8];
     __shared__ __attribute__((aligned(16))) uint16_t Vs0[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Vs1[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Vs2[NB == 3 ? TILE : 8];
@@ -668,9 +669,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             for (int i = s * PQ / NS; i < (s + 1) * PQ / NS; ++i) prob_pair(i);
             sched_fence();
         }
-        if constexpr (NB == 2) {
+        if constexpr (NBK == 2) {
             // V(j) in; every wave is past its reads of K(j+1) (with three
-            // buffers both hold at the end-of-step barrier of step j-1).
+            // K buffers both hold at the end-of-step barrier of step j-1).
             wait_vmcnt<2 * LPW>();
             barrier_lds();
         }
@@ -717,8 +718,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             mx = fminf(mx, max_tile(n0, n1));  // masking only lowers the max
         }
         rescale(mx);
-        // K(j+2) in; every wave is past its reads of V(j).
-        if constexpr (!KV8) wait_vmcnt<2 * LPW>();
+        // K(j+2) in (and V(j+1) with two V buffers and three K buffers:
+        // only K(j+3) may still be in flight); every wave is past its reads of V(j).
+        if constexpr (!KV8) wait_vmcnt<(NBK == 3 && NB == 2 ? 1 : 2) * LPW>();
         barrier_lds();
     };
 
@@ -764,7 +766,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
         if constexpr (!KV8) {
             // K(j_begin + 1) in (two buffers: V(j_begin) may still be in flight;
             // step 0's mid-step wait covers it); every wave is past its reads of K(j_begin)
-            if constexpr (NB == 2) wait_vmcnt<LPW>(); else wait_vmcnt<0>();
+            if constexpr (NBK == 2) wait_vmcnt<LPW>(); else wait_vmcnt<0>();
             barrier_lds();
         }
         if constexpr (KV8) {
@@ -775,6 +777,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             // K(j_begin + 2) and V(j_begin + 1) into buffers no wave has read yet
             load_k_tile(Ks2, min(j_begin + 2, j_last));
             load_v_tile(Vs1, min(j_begin + 1, j_last));
+        } else if constexpr (NBK == 3) {
+            // K(j_begin + 2) into the third K buffer; V(j_begin + 1) is step 0's load
+            load_k_tile(Ks2, min(j_begin + 2, j_last));
         } else {
             load_k_tile(Ks0, min(j_begin + 2, j_last));
         }
@@ -796,6 +801,19 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             if (r + 3 < nt) step(j_begin + r + 3, sb0, sb1, sa0, sa1, Ks1, Ks0, Vs0, Vs2, Ks2, Vs1, Sk1, Sk0, Sv0, Sv1);
             if (r + 4 < nt) step(j_begin + r + 4, sa0, sa1, sb0, sb1, Ks2, Ks1, Vs1, Vs0, Ks0, Vs2, Sk0, Sk1, Sv1, Sv0);
             if (r + 5 < nt) step(j_begin + r + 5, sb0, sb1, sa0, sa1, Ks0, Ks2, Vs2, Vs1, Ks1, Vs0, Sk1, Sk0, Sv0, Sv1);
+        }
+    } else if constexpr (NBK == 3) {
+        // Three K buffers, two V buffers (four waves): step r reads K(j+1) from
+        // K buffer (r+1)%3 and V(j) from V buffer r%2, refills K buffer r%3 with
+        // K(j+3) and V buffer (r+1)%2 with V(j+1); one barrier per step, at its
+        // end. Unrolled by six (3 K buffers, 2 V buffers, 2 score sets).
+        for (int r = 0; r < nt; r += 6) {
+            step(j_begin + r, sa0, sa1, sb0, sb1, Ks1, Ks0, Vs0, Vs1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+            if (r + 1 < nt) step(j_begin + r + 1, sb0, sb1, sa0, sa1, Ks2, Ks1, Vs1, Vs0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+            if (r + 2 < nt) step(j_begin + r + 2, sa0, sa1, sb0, sb1, Ks0, Ks2, Vs0, Vs1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+            if (r + 3 < nt) step(j_begin + r + 3, sb0, sb1, sa0, sa1, Ks1, Ks0, Vs1, Vs0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+            if (r + 4 < nt) step(j_begin + r + 4, sa0, sa1, sb0, sb1, Ks2, Ks1, Vs0, Vs1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+            if (r + 5 < nt) step(j_begin + r + 5, sb0, sb1, sa0, sa1, Ks0, Ks2, Vs1, Vs0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
         }
     } else {
         // Step r = j - j_begin: K(j+1) sits in buffer (r+1)%2, V(j) in buffer r%2.
