@@ -19,8 +19,10 @@ from .attn import (  # noqa: F401
     attn_prefill_varlen_fwd,
     auto_split_len,
     decode,
+    decode_heads_per_workgroup,
     lib,
     max_splits_for,
     prefill,
+    prefill_kernel,
     prefill_varlen,
 )

@@ -23,7 +23,8 @@ ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "kernel launch failed"}
 SYMBOLS = ("attn_prefill_fwd", "attn_prefill_fwd_ex", "attn_prefill_fwd_fp8kv", "attn_prefill_varlen_fwd", "attn_decode_fwd", "attn_decode_fwd_fp8kv",
            "attn_decode_combine", "attn_decode_combine_ex", "attn_decode_validate_pages", "attn_decode_workspace_size",
-           "attn_decode_fwd_noalloc", "attn_status_string")
+           "attn_decode_fwd_noalloc", "attn_status_string", "attn_prefill_kernel_for", "attn_prefill_kernel_name",
+           "attn_decode_heads_per_workgroup")
 # Bytes of the library's device array for attn_decode_fwd_noalloc's partials (ATTN_DECODE_NOALLOC_MAX_BYTES).
 DECODE_NOALLOC_MAX_BYTES = 32 << 20
 
@@ -48,6 +49,10 @@ def lib() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m flash_attention_forward_amd.build`")
+    # torch first: its HIP runtime then satisfies the library's libamdhip64 dependency. Loaded the other
+    # way round, the process holds two HIP runtimes, and a launch on a stream of torch's fails.
+    import torch  # noqa: F401
+
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     L.attn_prefill_fwd.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides, i32, i32, i32, i32, i32,
@@ -82,6 +87,12 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_fwd_noalloc.restype = i32
     L.attn_status_string.argtypes = [i32]
     L.attn_status_string.restype = ctypes.c_char_p
+    L.attn_prefill_kernel_for.argtypes = [i32] * 12
+    L.attn_prefill_kernel_for.restype = i32
+    L.attn_prefill_kernel_name.argtypes = [i32]
+    L.attn_prefill_kernel_name.restype = ctypes.c_char_p
+    L.attn_decode_heads_per_workgroup.argtypes = [i32] * 5
+    L.attn_decode_heads_per_workgroup.restype = i32
     _lib = L
     return L
 
@@ -358,6 +369,25 @@ def attn_decode_validate_pages(block_table, cache_len, page_size: int, num_pages
 
 
 # ----------------------------------------------------------------------------- conveniences
+def prefill_kernel(dtype: str, batch: int, n_q_heads: int, n_kv_heads: int, seqlen_q: int, seqlen_kv: int,
+                   head_dim: int, causal: bool, window: int = 0, fp8_kv: bool = False, packed: bool = False,
+                   positions: bool = False) -> str:
+    """Name of the kernel the prefill entry points launch for these sizes (attn_prefill_kernel_for:
+    host arithmetic only, the same choice the launch makes). dtype is "f32", "f16" or "bf16"."""
+    code = {"f32": ATTN_F32, "f16": ATTN_F16, "bf16": ATTN_BF16}[dtype]
+    k = lib().attn_prefill_kernel_for(code, int(fp8_kv), int(packed), int(positions), batch, n_q_heads, n_kv_heads,
+                                      seqlen_q, seqlen_kv, head_dim, int(bool(causal)), int(window))
+    if k < 0:
+        raise AttnError("attn_prefill_kernel_for", -k)
+    return lib().attn_prefill_kernel_name(k).decode() if k > 0 else ""
+
+
+def decode_heads_per_workgroup(batch: int, n_kv_heads: int, head_dim: int, max_splits: int,
+                               fp8_kv: bool = False) -> int:
+    """Kv-heads per workgroup of the decode split kernel for these sizes (attn_decode_heads_per_workgroup)."""
+    return lib().attn_decode_heads_per_workgroup(int(fp8_kv), batch, n_kv_heads, head_dim, max_splits)
+
+
 def default_scale(head_dim: int) -> float:
     return 1.0 / math.sqrt(head_dim)
 

@@ -52,6 +52,49 @@ int status_of(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH
 
 extern "C" {
 
+static_assert((int)ATTN_PREFILL_F32 == attn::kPrefillF32 && (int)ATTN_PREFILL_MFMA_4W == attn::kPrefillMfma4 &&
+                  (int)ATTN_PREFILL_MFMA_8W == attn::kPrefillMfma8 && (int)ATTN_PREFILL_PAIR == attn::kPrefillPair &&
+                  (int)ATTN_PREFILL_PAIR_ITEMS == attn::kPrefillPairItems &&
+                  (int)ATTN_PREFILL_MFMA_8W_FP8 == attn::kPrefillMfma8Kv8 && (int)ATTN_PREFILL_FP8_4W == attn::kPrefillF8kv4,
+              "the C ABI's kernel ids are the dispatch's");
+
+int attn_prefill_kernel_for(attn_dtype dtype, int fp8_kv, int packed, int has_positions, int batch,
+                            int n_q_heads, int n_kv_heads, int seqlen_q, int seqlen_kv, int head_dim,
+                            int causal, int window) {
+    // the entry points' checks that depend on these arguments alone (prefill_impl)
+    if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return -ATTN_ERR_INVALID;
+    if (batch < 0 || n_q_heads < 0 || n_kv_heads < 0 || seqlen_q < 0 || seqlen_kv < 0 || head_dim <= 0)
+        return -ATTN_ERR_INVALID;
+    if (batch == 0 || n_q_heads == 0 || seqlen_q == 0) return 0;
+    if (n_kv_heads == 0 || n_q_heads % n_kv_heads != 0) return -ATTN_ERR_INVALID;
+    if (!supported_head_dim(head_dim)) return -ATTN_ERR_UNSUPPORTED;
+    if (window > 0 && !causal) return -ATTN_ERR_UNSUPPORTED;
+    if (fp8_kv && dtype == ATTN_F32) return -ATTN_ERR_UNSUPPORTED;
+    const int w = window > 0 ? window : 0;
+    const int mask = !causal ? attn::kMaskNone : (w > 0 ? attn::kMaskCausalWindow : attn::kMaskCausal);
+    const attn::PrefillShape sh{(int)dtype, fp8_kv != 0, packed != 0, has_positions != 0, batch, n_q_heads,
+                                seqlen_q, seqlen_kv, head_dim, mask, w};
+    return attn::prefill_kernel(sh);
+}
+
+const char* attn_prefill_kernel_name(int kernel) {
+    switch (kernel) {
+        case ATTN_PREFILL_F32: return "prefill_f32";
+        case ATTN_PREFILL_MFMA_4W: return "prefill_mfma (4 waves)";
+        case ATTN_PREFILL_MFMA_8W: return "prefill_mfma (8 waves)";
+        case ATTN_PREFILL_PAIR: return "prefill_pair";
+        case ATTN_PREFILL_PAIR_ITEMS: return "prefill_pair_items";
+        case ATTN_PREFILL_MFMA_8W_FP8: return "prefill_mfma (8 waves, FP8 K/V)";
+        case ATTN_PREFILL_FP8_4W: return "prefill_f8kv";
+        default: return "?";
+    }
+}
+
+int attn_decode_heads_per_workgroup(int fp8_kv, int batch, int n_kv_heads, int head_dim, int max_splits) {
+    if (batch <= 0 || n_kv_heads <= 0 || max_splits <= 0 || !supported_head_dim(head_dim)) return 0;
+    return attn::decode_heads_per_workgroup(fp8_kv != 0, head_dim, n_kv_heads, batch, max_splits);
+}
+
 const char* attn_status_string(int status) {
     switch (status) {
         case ATTN_OK: return "ok";

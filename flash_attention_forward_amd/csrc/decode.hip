@@ -852,20 +852,38 @@ static void launch_decode_f8_hw(const DecodeParams& p, hipStream_t s) {
 
 // Waves per workgroup: the largest power of two up to the LDS-bound maximum
 // that divides n_kv_heads (decode_split_f8 holds one V tile per wave, decode_split four).
+template <int D>
+static int decode_heads_d(bool fp8, int n_kv_heads, int batch, int max_splits) {
+    const int mh = fp8 ? dc_max_heads_f8<D>() : dc_max_heads<D>();
+    const bool wide = (int64_t)batch * max_splits * (n_kv_heads / 8) >= kDecodeF8WideGrid;
+    if (fp8 && mh >= 8 && n_kv_heads % 8 == 0 && wide) return 8;
+    if (mh >= 4 && n_kv_heads % 4 == 0) return 4;
+    if (mh >= 2 && n_kv_heads % 2 == 0) return 2;
+    return 1;
+}
+
+int decode_heads_per_workgroup(bool fp8, int head_dim, int n_kv_heads, int batch, int max_splits) {
+    switch (head_dim) {
+        case 64: return decode_heads_d<64>(fp8, n_kv_heads, batch, max_splits);
+        case 128: return decode_heads_d<128>(fp8, n_kv_heads, batch, max_splits);
+        default: return decode_heads_d<256>(fp8, n_kv_heads, batch, max_splits);
+    }
+}
+
 template <bool BF16, int D, int QB>
 static void launch_decode_q(const DecodeParams& p, hipStream_t s) {
+    const int hw = decode_heads_d<D>(p.kv_fp8, p.n_kv_heads, p.batch, p.max_splits);
     if (p.kv_fp8) {
         constexpr int MH = dc_max_heads_f8<D>();
-        const bool wide = (int64_t)p.batch * p.max_splits * (p.n_kv_heads / 8) >= kDecodeF8WideGrid;
-        if (MH >= 8 && p.n_kv_heads % 8 == 0 && wide) launch_decode_f8_hw<BF16, D, (MH >= 8 ? 8 : 1), QB>(p, s);
-        else if (MH >= 4 && p.n_kv_heads % 4 == 0) launch_decode_f8_hw<BF16, D, (MH >= 4 ? 4 : 1), QB>(p, s);
-        else if (MH >= 2 && p.n_kv_heads % 2 == 0) launch_decode_f8_hw<BF16, D, (MH >= 2 ? 2 : 1), QB>(p, s);
+        if (MH >= 8 && hw == 8) launch_decode_f8_hw<BF16, D, (MH >= 8 ? 8 : 1), QB>(p, s);
+        else if (MH >= 4 && hw == 4) launch_decode_f8_hw<BF16, D, (MH >= 4 ? 4 : 1), QB>(p, s);
+        else if (MH >= 2 && hw == 2) launch_decode_f8_hw<BF16, D, (MH >= 2 ? 2 : 1), QB>(p, s);
         else launch_decode_f8_hw<BF16, D, 1, QB>(p, s);
         return;
     }
     constexpr int MH = dc_max_heads<D>();
-    if (MH >= 4 && p.n_kv_heads % 4 == 0) launch_decode_hw<BF16, D, (MH >= 4 ? 4 : 1), QB>(p, s);
-    else if (MH >= 2 && p.n_kv_heads % 2 == 0) launch_decode_hw<BF16, D, (MH >= 2 ? 2 : 1), QB>(p, s);
+    if (MH >= 4 && hw == 4) launch_decode_hw<BF16, D, (MH >= 4 ? 4 : 1), QB>(p, s);
+    else if (MH >= 2 && hw == 2) launch_decode_hw<BF16, D, (MH >= 2 ? 2 : 1), QB>(p, s);
     else launch_decode_hw<BF16, D, 1, QB>(p, s);
 }
 

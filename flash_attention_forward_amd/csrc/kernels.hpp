@@ -75,6 +75,26 @@ constexpr int kDecodeMaxSplitPages = 256;
 enum MaskMode { kMaskNone = 0, kMaskCausal = 1, kMaskCausalWindow = 2 };
 enum DType { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
+// The kernel a prefill call launches, chosen from its sizes and flags alone
+// (host code; the launch functions below dispatch on this same choice).
+enum PrefillKernel {
+    kPrefillF32 = 1,        // prefill_f32
+    kPrefillMfma4 = 2,      // prefill_mfma, four waves (128 rows)
+    kPrefillMfma8 = 3,      // prefill_mfma, eight waves (256 rows)
+    kPrefillPair = 4,       // prefill_pair (D = 256), one workgroup per q tile
+    kPrefillPairItems = 5,  // prefill_pair_items (D = 256), persistent
+    kPrefillMfma8Kv8 = 6,   // prefill_mfma, eight waves, FP8 K/V staging
+    kPrefillF8kv4 = 7,      // prefill_f8kv, four waves
+};
+struct PrefillShape {
+    int dtype;
+    bool fp8, packed, positions;  // FP8 K/V codes; cu_seqlens given; per-row positions given
+    int batch, n_q_heads, seqlen_q, seqlen_kv, head_dim, mask, window;
+};
+int prefill_kernel(const PrefillShape& s);
+// Kv-heads (waves) per workgroup of the decode split kernel for these sizes.
+int decode_heads_per_workgroup(bool fp8, int head_dim, int n_kv_heads, int batch, int max_splits);
+
 // Each returns the hipError_t of its launch (hipSuccess on success).
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int mask, hipStream_t s);
 // K and V as FP8 E4M3 codes (k/v strides in bytes); dtype (f16/bf16) is Q's and O's.

@@ -1997,18 +1997,20 @@ constexpr int kPrefillWideMinWorkgroups = 512;
 // 64-key tiles.
 constexpr int kPairItemsWorkgroups = 256;
 
-static bool pair_items_ok(const PrefillParams& p, int mask) {
-    if (p.cu_seqlens_q || p.positions || mask == kMaskCausal || p.seqlen_kv <= 0 || p.seqlen_kv % 64 != 0) return false;
-    if ((long)p.n_q_tiles * p.batch * p.n_q_heads < 2L * kPairItemsWorkgroups) return false;
-    const int sq = p.seqlen_q, skv = p.seqlen_kv, off = skv - sq;
+static bool pair_items_ok(const PrefillShape& s) {
+    const int mask = s.mask;
+    if (s.packed || s.positions || mask == kMaskCausal || s.seqlen_kv <= 0 || s.seqlen_kv % 64 != 0) return false;
+    const int n_q_tiles = (s.seqlen_q + 127) / 128;
+    if ((long)n_q_tiles * s.batch * s.n_q_heads < 2L * kPairItemsWorkgroups) return false;
+    const int sq = s.seqlen_q, skv = s.seqlen_kv, off = skv - sq;
     // the call's first visible key (the first row's window start) on a tile boundary
-    if (mask == kMaskCausalWindow && std::max(0, off - p.window + 1) % 64 != 0) return false;
-    for (int t = 0; t < p.n_q_tiles; ++t) {
+    if (mask == kMaskCausalWindow && std::max(0, off - s.window + 1) % 64 != 0) return false;
+    for (int t = 0; t < n_q_tiles; ++t) {
         const int q0 = t * 128, qlast = std::min(q0 + 128, sq) - 1;
         int kv_lo = 0, kv_hi = skv;
         if (mask == kMaskCausalWindow) {
             kv_hi = std::min(kv_hi, qlast + off + 1);
-            kv_lo = std::max(0, q0 + off - p.window + 1);
+            kv_lo = std::max(0, q0 + off - s.window + 1);
         }
         if (kv_hi <= kv_lo) return false;
         const int nt = (kv_hi + 63) / 64 - kv_lo / 64;
@@ -2017,10 +2019,27 @@ static bool pair_items_ok(const PrefillParams& p, int mask) {
     return true;
 }
 
+// Eight-wave grids: at least kPrefillWideMinWorkgroups 256-row workgroups.
+static bool prefill_wide(const PrefillShape& s) {
+    return (long)((s.seqlen_q + 255) / 256) * s.batch * s.n_q_heads >= kPrefillWideMinWorkgroups;
+}
+
+int prefill_kernel(const PrefillShape& s) {
+    if (s.fp8) return s.head_dim == 128 && prefill_wide(s) ? kPrefillMfma8Kv8 : kPrefillF8kv4;
+    if (s.dtype == kF32) return kPrefillF32;
+    if (s.head_dim == 256) return pair_items_ok(s) ? kPrefillPairItems : kPrefillPair;
+    return !s.packed && prefill_wide(s) ? kPrefillMfma8 : kPrefillMfma4;
+}
+
+static PrefillShape shape_of(const PrefillParams& p, int dtype, int head_dim, int mask, bool fp8) {
+    return PrefillShape{dtype, fp8, p.cu_seqlens_q != nullptr, p.positions != nullptr, p.batch, p.n_q_heads,
+                        p.seqlen_q, p.seqlen_kv, head_dim, mask, p.window};
+}
+
 template <bool BF16>
-static hipError_t launch_pair(PrefillParams p, int mask, hipStream_t s) {
+static hipError_t launch_pair(PrefillParams p, bool items, int mask, hipStream_t s) {
     p.n_q_tiles = (p.seqlen_q + 127) / 128;
-    if (pair_items_ok(p, mask)) {
+    if (items) {
         const dim3 grid((unsigned)kPairItemsWorkgroups), block(512);
         if (mask == kMaskCausalWindow)
             hipLaunchKernelGGL((prefill_pair_items<BF16, kMaskCausalWindow>), grid, block, 0, s, p);
@@ -2038,12 +2057,10 @@ static hipError_t launch_pair(PrefillParams p, int mask, hipStream_t s) {
 }
 
 template <bool BF16, int D>
-static hipError_t launch_mfma_mask(PrefillParams p, int mask, hipStream_t s) {
-    if constexpr (D == 256) return launch_pair<BF16>(p, mask, s);
+static hipError_t launch_mfma_mask(PrefillParams p, int kernel, int mask, hipStream_t s) {
+    if constexpr (D == 256) return launch_pair<BF16>(p, kernel == kPrefillPairItems, mask, s);
     if constexpr (D <= 128) {
-        if (p.cu_seqlens_q) return launch_mfma_nw<BF16, D, 4>(p, mask, s);
-        const long wide = (long)((p.seqlen_q + 255) / 256) * p.batch * p.n_q_heads;
-        if (wide >= kPrefillWideMinWorkgroups) return launch_mfma_nw<BF16, D, 8>(p, mask, s);
+        if (kernel == kPrefillMfma8) return launch_mfma_nw<BF16, D, 8>(p, mask, s);
     }
     return launch_mfma_nw<BF16, D, 4>(p, mask, s);
 }
@@ -2075,45 +2092,48 @@ static hipError_t launch_f8kv_nw(PrefillParams p, int mask, hipStream_t s) {
 // On the grids where the 16-bit prefill takes eight waves (D = 128), its
 // pipelined kernel with FP8 staging; prefill_f8kv otherwise.
 template <bool BF16, int D>
-static hipError_t launch_f8kv_mask(PrefillParams p, int mask, hipStream_t s) {
+static hipError_t launch_f8kv_mask(PrefillParams p, int kernel, int mask, hipStream_t s) {
     if constexpr (D == 128) {
-        const long wide = (long)((p.seqlen_q + 255) / 256) * p.batch * p.n_q_heads;
-        if (wide >= kPrefillWideMinWorkgroups) return launch_mfma_nw<BF16, D, 8, true>(p, mask, s);
+        if (kernel == kPrefillMfma8Kv8) return launch_mfma_nw<BF16, D, 8, true>(p, mask, s);
     }
     return launch_f8kv_nw<BF16, D, 4>(p, mask, s);
 }
 
 template <bool BF16>
-static hipError_t launch_f8kv_d(const PrefillParams& p, int head_dim, int mask, hipStream_t s) {
+static hipError_t launch_f8kv_d(const PrefillParams& p, int kernel, int head_dim, int mask, hipStream_t s) {
     switch (head_dim) {
-        case 64: return launch_f8kv_mask<BF16, 64>(p, mask, s);
-        case 128: return launch_f8kv_mask<BF16, 128>(p, mask, s);
-        default: return launch_f8kv_mask<BF16, 256>(p, mask, s);
+        case 64: return launch_f8kv_mask<BF16, 64>(p, kernel, mask, s);
+        case 128: return launch_f8kv_mask<BF16, 128>(p, kernel, mask, s);
+        default: return launch_f8kv_mask<BF16, 256>(p, kernel, mask, s);
     }
 }
 
 hipError_t launch_prefill_f8kv(const PrefillParams& p, int dtype, int head_dim, int mask, hipStream_t s) {
-    return dtype == kBF16 ? launch_f8kv_d<true>(p, head_dim, mask, s) : launch_f8kv_d<false>(p, head_dim, mask, s);
+    const int kernel = prefill_kernel(shape_of(p, dtype, head_dim, mask, true));
+    return dtype == kBF16 ? launch_f8kv_d<true>(p, kernel, head_dim, mask, s)
+                          : launch_f8kv_d<false>(p, kernel, head_dim, mask, s);
 }
 
 template <bool BF16>
-static hipError_t launch_mfma_d(const PrefillParams& p, int head_dim, int mask, hipStream_t s) {
+static hipError_t launch_mfma_d(const PrefillParams& p, int kernel, int head_dim, int mask, hipStream_t s) {
     switch (head_dim) {
-        case 64: return launch_mfma_mask<BF16, 64>(p, mask, s);
-        case 128: return launch_mfma_mask<BF16, 128>(p, mask, s);
-        default: return launch_mfma_mask<BF16, 256>(p, mask, s);
+        case 64: return launch_mfma_mask<BF16, 64>(p, kernel, mask, s);
+        case 128: return launch_mfma_mask<BF16, 128>(p, kernel, mask, s);
+        default: return launch_mfma_mask<BF16, 256>(p, kernel, mask, s);
     }
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int mask, hipStream_t s) {
-    if (dtype == kF32) {
+    const int kernel = prefill_kernel(shape_of(p, dtype, head_dim, mask, false));
+    if (kernel == kPrefillF32) {
         switch (head_dim) {
             case 64: return launch_f32_mask<64>(p, mask, s);
             case 128: return launch_f32_mask<128>(p, mask, s);
             default: return launch_f32_mask<256>(p, mask, s);
         }
     }
-    return dtype == kBF16 ? launch_mfma_d<true>(p, head_dim, mask, s) : launch_mfma_d<false>(p, head_dim, mask, s);
+    return dtype == kBF16 ? launch_mfma_d<true>(p, kernel, head_dim, mask, s)
+                          : launch_mfma_d<false>(p, kernel, head_dim, mask, s);
 }
 
 }  // namespace attn

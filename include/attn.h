@@ -347,6 +347,31 @@ int attn_decode_fwd_noalloc(const void* q, attn_strides q_st,
 int attn_decode_workspace_size(int batch, int s_active, int n_q_heads, int head_dim, int max_splits,
                                size_t* part_o_bytes, size_t* part_lse_bytes);
 
+/* Which kernel the prefill entry points launch for a call of these sizes. It is host
+ * arithmetic only (no HIP call, no device memory): the entry points take their launch
+ * from this same choice, so a caller or a test can see which kernel a shape exercises.
+ * fp8_kv: K/V as FP8 codes (attn_prefill_fwd_fp8kv); packed: cumulative offsets given
+ * (attn_prefill_varlen_fwd); has_positions: per-row positions given. Returns an
+ * attn_prefill_kernel value (> 0), or minus ATTN_ERR_INVALID / ATTN_ERR_UNSUPPORTED for
+ * arguments the entry points reject with that status, or 0 for an empty call. */
+typedef enum {
+    ATTN_PREFILL_F32 = 1,         /* fp32 on the vector ALUs */
+    ATTN_PREFILL_MFMA_4W = 2,     /* 16-bit, four waves per 128-row q tile */
+    ATTN_PREFILL_MFMA_8W = 3,     /* 16-bit, eight waves per 256-row q tile (wide grids) */
+    ATTN_PREFILL_PAIR = 4,        /* head_dim 256, paired waves, one workgroup per q tile */
+    ATTN_PREFILL_PAIR_ITEMS = 5,  /* head_dim 256, paired waves, one persistent workgroup per CU */
+    ATTN_PREFILL_MFMA_8W_FP8 = 6, /* FP8 K/V staged and widened in LDS, eight waves (wide grids, head_dim 128) */
+    ATTN_PREFILL_FP8_4W = 7       /* FP8 K/V widened in registers, four waves */
+} attn_prefill_kernel;
+int attn_prefill_kernel_for(attn_dtype dtype, int fp8_kv, int packed, int has_positions, int batch,
+                            int n_q_heads, int n_kv_heads, int seqlen_q, int seqlen_kv, int head_dim,
+                            int causal, int window);
+/* Name of an attn_prefill_kernel value ("?" for others). Never NULL. */
+const char* attn_prefill_kernel_name(int kernel);
+/* Kv-heads per workgroup of the decode split kernel (attn_decode_fwd, _fp8kv) for these
+ * sizes: 1, 2, 4 or 8. Host arithmetic only, as above; 0 for sizes it does not cover. */
+int attn_decode_heads_per_workgroup(int fp8_kv, int batch, int n_kv_heads, int head_dim, int max_splits);
+
 /* Static description of a status code. Never NULL. */
 const char* attn_status_string(int status);
 

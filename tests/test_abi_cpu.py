@@ -359,3 +359,15 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     t = torch.zeros(1, 1, 1, 64)
     with pytest.raises((RuntimeError, ValueError)):
         A.prefill(t, t, t)
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """The library and torch share one HIP runtime, also when the library is loaded before torch is
+    imported (two runtimes in one process make every launch on a torch stream fail)."""
+    code = ("from flash_attention_forward_amd import attn as A\n"
+            "A.lib()\n"
+            "import torch\n"
+            "maps = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(maps))\n")
+    out = subprocess.run(["python3", "-c", code], cwd=ROOT, capture_output=True, text=True, check=True).stdout
+    assert out.split()[-1] == "1"

@@ -106,7 +106,8 @@ def test_fp8_decode_eight_and_four_head_workgroups_bitwise():
     t = fp8_tensors(inp)
     maxlen = s.max_pages_per_seq * s.page_size
     ms = F.attn.max_splits_for(maxlen, 256)
-    assert s.batch * ms * (s.n_kv_heads // 8) < 512 <= s.batch * 64 * (s.n_kv_heads // 8)
+    assert F.decode_heads_per_workgroup(s.batch, s.n_kv_heads, s.head_dim, ms, fp8_kv=True) == 4
+    assert F.decode_heads_per_workgroup(s.batch, s.n_kv_heads, s.head_dim, 64, fp8_kv=True) == 8
     outs = []
     for splits in (ms, 64):
         ws = F.DecodeWorkspace(s.batch, s.s_active, s.n_q_heads, s.head_dim, splits, "cuda")

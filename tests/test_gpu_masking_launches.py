@@ -57,10 +57,11 @@ PERSISTENT = [n for n in LAUNCHES if n.startswith("persistent")]
 
 @pytest.mark.parametrize("name", PERSISTENT)
 def test_persistent_shapes_take_the_persistent_launch(name):
-    from test_gpu_prefill_d256_persistent import eligible
+    import flash_attention_forward_amd as F
 
     s = LAUNCHES[name]
-    assert eligible(s.batch, s.n_q_heads, s.seqlen_q, s.seqlen_kv, s.window)
+    assert F.prefill_kernel(s.dtype, s.batch, s.n_q_heads, s.n_kv_heads, s.seqlen_q, s.seqlen_kv, s.head_dim, s.causal,
+                            s.window) == "prefill_pair_items"
 
 
 def random_finite(rng, shape, dtype):

@@ -61,8 +61,11 @@ def make(name, seed):
 
 @pytest.mark.parametrize("name", list(SHAPES))
 def test_shapes_take_the_persistent_launch(name):
+    import flash_attention_forward_amd as F
+
     B, Hq, Hkv, Sq, Skv, dt, w = SHAPES[name]
     assert eligible(B, Hq, Sq, Skv, w)
+    assert F.prefill_kernel(dt, B, Hq, Hkv, Sq, Skv, 256, w > 0, w) == "prefill_pair_items"
 
 
 @pytest.mark.parametrize("name", ["bf16_window1024_8k", "bf16_nomask_16k_1k", "bf16_prefix_window385",
