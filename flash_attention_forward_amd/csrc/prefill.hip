@@ -577,11 +577,15 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     // the last tile, never used).
     // The step body is laid out by hand in stages separated by scheduling
     // fences: stage s of the QK part issues the two MFMAs of K chunk s, the
-    // LDS reads of chunk s+2 and its share of the probabilities; stage i of
-    // the P V part issues MFMA i, the transpose reads of MFMA i+4 and its
+    // LDS reads of chunk s+KPD and its share of the probabilities; stage i of
+    // the P V part issues MFMA i, the transpose reads of MFMA i+VPRE and its
     // share of the remaining probabilities and of the raw row max of tile
-    // j+1. LDS reads thus run two stages (at least 128 MFMA cycles) ahead of
-    // their use. The row sums of P(j) (v_dot2c, which stalls when mixed with
+    // j+1. LDS reads thus run at least 128 MFMA cycles ahead of their use:
+    // KPD = 2 stages and VPRE = 4 MFMAs at eight waves; at four waves, whose
+    // heavy causal tiles often run alone on their SIMD (their partner
+    // workgroup done), 3 stages and 6 MFMAs (1-2% faster on the 2K prefill and
+    // the packed prompts, same bits; the eight-wave kernel measured no
+    // change). The row sums of P(j) (v_dot2c, which stalls when mixed with
     // MFMAs) come after the last MFMA, in two independent chains.
     //
     // Loads and barriers (two buffers): step j issues V(j+1) at its start
@@ -597,7 +601,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     // K(j+2), V(j+1), K(j+3), ...), and each barrier waits with vmcnt = the
     // loads issued after the one it needs.
     constexpr int NPV = 4 * NDT;        // P V MFMAs per tile
-    constexpr int VPRE = 4;             // P V MFMAs whose fragments are in flight
+    constexpr int VPRE = NW == 4 ? 6 : 4;  // P V MFMAs whose fragments are in flight (see above)
     constexpr int PQ = 12;              // probability pairs (of 16) made in the QK part
     constexpr int NPV_EARLY = NPV - NDT;  // P V MFMAs before the last key chunk's
     static_assert(NS >= 4, "the V prefetch is issued in the last two QK stages");
@@ -645,8 +649,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             pk[i] = pack2_16<BF16>(fast_exp2(fmaf(sc[r], p.c, neg_m)), fast_exp2(fmaf(sc[r + 1], p.c, neg_m)));
             asm volatile("" ::"v"(pk[i]));  // computed here, not sunk into a later stage
         };
-        kread(0);
-        kread(1);
+        constexpr int KPD = NW == 4 ? 3 : 2;  // QK stages whose K fragments are in flight
+#pragma unroll
+        for (int s = 0; s < KPD; ++s) kread(s);
         sched_fence();
         n0 = f32x16{};
         n1 = f32x16{};
@@ -664,7 +669,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             } else if (s % (NS / LPW) == 0) {
                 load_part(Vl, vrs, vvo[s / (NS / LPW)], s / (NS / LPW));
             }
-            if (s + 2 < NS) kread(s + 2);
+            if (s + KPD < NS) kread(s + KPD);
 #pragma unroll
             for (int i = s * PQ / NS; i < (s + 1) * PQ / NS; ++i) prob_pair(i);
             sched_fence();
