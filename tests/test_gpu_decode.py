@@ -77,7 +77,7 @@ def test_decode_flat_cache():
 
 def test_decode_full_size_every_sequence():
     """The full paged-decode workload, launched as the benchmark does, against the oracle on all
-    32 sequences (spec tolerances and the derived per-element bound)."""
+    32 sequences (the fixed tolerances and the derived per-element bound)."""
     name = "paged_decode_b32_d128"
     inp = W.make_decode(C5, W.WORKLOAD_SEEDS[name])
     say("decode full size", int(inp.cache_len.sum()))

@@ -58,7 +58,7 @@ def test_prefill_parity_small(name):
 @pytest.mark.parametrize("name", ["f16_gqa7_causal_2k", "bf16_swa1024_d256_8k"])
 def test_prefill_parity_full_size_every_row(name):
     """Full-size workloads, launched as the benchmark launches them, against the oracle on every
-    output element (spec tolerances and the derived per-element bound)."""
+    output element (the fixed tolerances and the derived per-element bound)."""
     spec = WL[name]
     inp = W.make_prefill(spec, seed=W.WORKLOAD_SEEDS[name])
     say("prefill full-size, every row", name)
