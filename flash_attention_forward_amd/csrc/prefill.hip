@@ -183,7 +183,8 @@ __device__ __forceinline__ void widen_e4m3x16(uint4 x, uint4& lo, uint4& hi) {
 // the 16-bit tiles, the fragment reads and all of the math are the 16-bit
 // path's.
 template <bool BF16, int D, int MASK, int NW, bool KV8 = false>
-__global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefill_mfma(PrefillParams p) {
+__global__ __launch_bounds__(64 * NW, (NW == 8 ? 1 : 2)) void prefill_mfma(PrefillParams p) {
+    static_assert(D == 64 || D == 128, "head_dim 256 takes prefill_pair / prefill_pair_items");
     static_assert(!KV8 || (NW == 8 && D == 128), "FP8 K/V: eight waves, D = 128");
     constexpr int PF_BM = PF_ROWS_PER_WAVE * NW;  // query rows per workgroup
     constexpr int PF_THREADS = 64 * NW;
@@ -193,14 +194,13 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     static_assert(LPW >= 1, "every wave loads part of each tile");
     constexpr int NDT = D / 32;             // 32-wide d tiles of O^T
     // K and V tiles, separate objects so waits on one buffer's refill never
-    // cover reads of the other: two of each (two barriers per key tile) for
-    // four waves, three of each (one barrier per key tile) for eight, whose
-    // one workgroup per CU has the LDS for them.
+    // cover reads of the other: three K buffers (one barrier per key tile),
+    // and three V buffers for eight waves (whose one workgroup per CU has the
+    // LDS for them), two for four (80 KB at D = 128: two workgroups per CU).
     constexpr int NB = NW == 8 ? 3 : 2;                  // V buffers
-    constexpr int NBK = NW == 8 || D <= 128 ? 3 : 2;     // K buffers: three give one barrier per key tile
     __shared__ __attribute__((aligned(16))) uint16_t Ks0[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Ks1[TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t Ks2[NBK == 3 ? TILE : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks2[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Vs0[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Vs1[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t Vs2[NB == 3 ? TILE : 8];
@@ -331,8 +331,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
 #pragma unroll
             for (int ii = 0; ii < LPW; ++ii) {
                 const int i = w * LPW + ii;
-                const uint32_t u = is_k ? (D == 64 ? (4 * i) & 7 : (D == 128 ? (4 * i) & 15 : (2 * i) & 15))
-                                        : (D <= 128 ? 0 : 4 * ((2 * i) & 3));
+                const uint32_t u = is_k ? (D == 64 ? (4 * i) & 7 : (4 * i) & 15) : 0;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 512 * i), 16,
                                                          lane_row_off + (lane_chunk_off ^ (16u * u)),
                                                          (uint32_t)(2 * RPL * i) * (uint32_t)seq, 0, 0);
@@ -366,8 +365,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
 #pragma unroll
     for (int ii = 0; ii < (KV8 ? 0 : LPW); ++ii) {
         const int i = w * LPW + ii;
-        const uint32_t uk = D == 64 ? (4 * i) & 7 : (D == 128 ? (4 * i) & 15 : (2 * i) & 15);
-        const uint32_t uv = D <= 128 ? 0 : 4 * ((2 * i) & 3);
+        const uint32_t uk = D == 64 ? (4 * i) & 7 : (4 * i) & 15;
+        const uint32_t uv = 0;
         uint32_t ko = kl + (kx ^ (16u * uk)) + (uint32_t)(2 * RPL * i) * (uint32_t)p.ks.seq;
         uint32_t vo = vl + (vx ^ (16u * uv)) + (uint32_t)(2 * RPL * i) * (uint32_t)p.vs.seq;
         asm volatile("" : "+v"(ko), "+v"(vo));
@@ -475,12 +474,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     // fragment of d tile dt sits at vfrag ^ 64dt plus a row offset that is a
     // compile-time constant (vswz depends on the row only through row % 4 for
     // D >= 128 and (row / 2) % 2 for D = 64, which the u and +8 row steps
-    // leave unchanged). For D <= 128 every fragment offset is computed once
-    // and kept in its own register (made opaque so the compiler cannot
-    // recompute it in the loop); the buffer and row steps are constants
-    // folded into the LDS instructions' offset fields. For D = 256 (twice as
-    // many fragments and no spare VGPRs) the XOR is redone at each use from
-    // one opaque register per tensor.
+    // leave unchanged). Every fragment offset is computed once and kept in
+    // its own register (made opaque so the compiler cannot recompute it in
+    // the loop); the buffer and row steps are constants folded into the LDS
+    // instructions' offset fields.
     const uint32_t kfrag = (uint32_t)(l32 * D * 2) | (16u * (uint32_t)(hf ^ pf_kswz<D>(l32)));
     const int vr0 = 4 * hf + (r16 >> 2);                  // V^T row of this lane in chunk 0
     const int vcl = 2 * (g & 1) + ((r16 & 3) >> 1);       // chunk within a 32-wide d tile
@@ -493,14 +490,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
         return *(const s16x8*)((const char*)base + byte_off);
     };
     constexpr int NS = D / 16;          // K chunks of 16 along d
-    constexpr bool PRE = D <= 128;      // per-fragment offset registers
-    uint32_t koff[PRE ? NS : 1], voff[PRE ? NDT : 1];
-    if constexpr (PRE) {
+    uint32_t koff[NS], voff[NDT];       // per-fragment offset registers
 #pragma unroll
-        for (int s = 0; s < NS; ++s) koff[s] = opaque(kfrag ^ (32u * s));
+    for (int s = 0; s < NS; ++s) koff[s] = opaque(kfrag ^ (32u * s));
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) voff[dt] = opaque(vfrag ^ (64u * dt));
-    }
+    for (int dt = 0; dt < NDT; ++dt) voff[dt] = opaque(vfrag ^ (64u * dt));
 
     // S^T of one 64-key tile: two 32-key blocks x 32 queries; lane holds keys
     // 32t + 8(r/4) + 4hf + r%4 of its query row in register r of block t.
@@ -591,18 +585,15 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
     // change). The row sums of P(j) (v_dot2c, which stalls when mixed with
     // MFMAs) come after the last MFMA, in two independent chains.
     //
-    // Loads and barriers (two buffers): step j issues V(j+1) at its start
-    // (into the buffer of V(j-1)) and K(j+3) after a mid-step barrier that
-    // follows the QK part (into the buffer of K(j+1), which that part has just
-    // read). The mid-step barrier also publishes V(j), the end-of-step barrier
-    // K(j+2): every tile has about one and a half steps to arrive. With three
-    // buffers there is no mid-step barrier: step j issues V(j+2) at its start
-    // and K(j+3) in its P V part, and the end-of-step barrier publishes K(j+2)
-    // and V(j+1), whose buffers no wave reads in step j. Tile indices past
-    // the last tile are clamped to it, so every step issues the same loads
-    // and each wait is a fixed count: loads complete in issue order (V(j),
-    // K(j+2), V(j+1), K(j+3), ...), and each barrier waits with vmcnt = the
-    // loads issued after the one it needs.
+    // Loads and barriers (three K buffers, one barrier per step, at its end):
+    // step j issues K(j+3) in its P V part, into the buffer of K(j), which no
+    // wave has read since step j-1. With three V buffers it issues V(j+2) at
+    // its start and the barrier publishes K(j+2) and V(j+1); with two (four
+    // waves) it issues V(j+1) at its start, into the buffer of V(j-1), and the
+    // barrier publishes K(j+2) and that V(j+1). Tile indices past the last
+    // tile are clamped to it, so every step issues the same loads and each
+    // wait is a fixed count: loads complete in issue order, and the barrier
+    // waits with vmcnt = the loads issued after the one it needs.
     constexpr int NPV = 4 * NDT;        // P V MFMAs per tile
     constexpr int VPRE = NW == 4 ? 6 : 4;  // P V MFMAs whose fragments are in flight (see above)
     constexpr int PQ = NW == 4 ? 16 : 12;  // probability pairs (of 16) made in the QK part
@@ -624,23 +615,17 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
                     uint16_t* Vl, uint16_t* K3, uint16_t* V3, uint8_t* Ska, uint8_t* Skb, uint8_t* Sva,
                     uint8_t* Svb) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(vbase, p.vs.seq, min(j + NB - 1, j_last));
-        const uint32_t kf = PRE ? 0u : opaque(kfrag);
-        const uint32_t vf = PRE ? 0u : opaque(vfrag);
         s16x8 ka[NS][2];
         s16x8 vb[NPV];
         uint32_t pk[16];
         uint4 x8;  // KV8: one lane's staged codes between their read and their widening
         auto kread = [&](int s) __attribute__((always_inline)) {
-            uint32_t off;
-            if constexpr (PRE) off = koff[s]; else off = kf ^ (32u * s);
-            ka[s][0] = lds_frag8(Kn, off);
-            ka[s][1] = lds_frag8(Kn + 32 * D, off);
+            ka[s][0] = lds_frag8(Kn, koff[s]);
+            ka[s][1] = lds_frag8(Kn + 32 * D, koff[s]);
         };
         auto vread = [&](int i) __attribute__((always_inline)) {
             const int u = i / NDT, dt = i % NDT;
-            uint32_t off;
-            if constexpr (PRE) off = voff[dt]; else off = vf ^ (64u * dt);
-            const char* vb0 = (const char*)Vc + off;
+            const char* vb0 = (const char*)Vc + voff[dt];
             vb[i] = concat4(lds_read_tr16((const uint16_t*)(vb0 + 2 * D * (16 * u))),
                             lds_read_tr16((const uint16_t*)(vb0 + 2 * D * (16 * u + 8))));
         };
@@ -676,12 +661,6 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
 #pragma unroll
             for (int i = s * PQ / NS; i < (s + 1) * PQ / NS; ++i) prob_pair(i);
             sched_fence();
-        }
-        if constexpr (NBK == 2) {
-            // V(j) in; every wave is past its reads of K(j+1) (with three
-            // K buffers both hold at the end-of-step barrier of step j-1).
-            wait_vmcnt<2 * LPW>();
-            barrier_lds();
         }
         const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kbase, p.ks.seq, min(j + 3, j_last));
 #pragma unroll
@@ -728,7 +707,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
         rescale(mx);
         // K(j+2) in (and V(j+1) with two V buffers and three K buffers:
         // only K(j+3) may still be in flight); every wave is past its reads of V(j).
-        if constexpr (!KV8) wait_vmcnt<(NBK == 3 && NB == 2 ? 1 : 2) * LPW>();
+        if constexpr (!KV8) wait_vmcnt<(NB == 2 ? 1 : 2) * LPW>();
         barrier_lds();
     };
 
@@ -772,9 +751,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
         }
         rescale(max_tile(sa0, sa1));
         if constexpr (!KV8) {
-            // K(j_begin + 1) in (two buffers: V(j_begin) may still be in flight;
-            // step 0's mid-step wait covers it); every wave is past its reads of K(j_begin)
-            if constexpr (NBK == 2) wait_vmcnt<LPW>(); else wait_vmcnt<0>();
+            // K(j_begin + 1) and V(j_begin) in; every wave is past its reads of K(j_begin)
+            wait_vmcnt<0>();
             barrier_lds();
         }
         if constexpr (KV8) {
@@ -785,16 +763,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             // K(j_begin + 2) and V(j_begin + 1) into buffers no wave has read yet
             load_k_tile(Ks2, min(j_begin + 2, j_last));
             load_v_tile(Vs1, min(j_begin + 1, j_last));
-        } else if constexpr (NBK == 3) {
+        } else {
             // K(j_begin + 2) into the third K buffer; V(j_begin + 1) is step 0's load
             load_k_tile(Ks2, min(j_begin + 2, j_last));
-        } else {
-            load_k_tile(Ks0, min(j_begin + 2, j_last));
         }
     }
-    // Step r = j - j_begin: K(j+1) sits in buffer (r+1)%2, V(j) in buffer r%2.
-    // Unrolled by two so that every LDS access names its buffer (the compiler
-    // then waits on a refill only before reads of the buffer being refilled).
     if constexpr (NB == 3) {
         // Step r = j - j_begin: K(j+1) sits in buffer (r+1)%3, V(j) in buffer
         // r%3; the step refills K buffer r%3 with K(j+3) and V buffer (r+2)%3
@@ -810,7 +783,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             if (r + 4 < nt) step(j_begin + r + 4, sa0, sa1, sb0, sb1, Ks2, Ks1, Vs1, Vs0, Ks0, Vs2, Sk0, Sk1, Sv1, Sv0);
             if (r + 5 < nt) step(j_begin + r + 5, sb0, sb1, sa0, sa1, Ks0, Ks2, Vs2, Vs1, Ks1, Vs0, Sk1, Sk0, Sv0, Sv1);
         }
-    } else if constexpr (NBK == 3) {
+    } else {
         // Three K buffers, two V buffers (four waves): step r reads K(j+1) from
         // K buffer (r+1)%3 and V(j) from V buffer r%2, refills K buffer r%3 with
         // K(j+3) and V buffer (r+1)%2 with V(j+1); one barrier per step, at its
@@ -822,16 +795,6 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 || D >= 256 ? 1 : 2)) void prefil
             if (r + 3 < nt) step(j_begin + r + 3, sb0, sb1, sa0, sa1, Ks1, Ks0, Vs1, Vs0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
             if (r + 4 < nt) step(j_begin + r + 4, sa0, sa1, sb0, sb1, Ks2, Ks1, Vs0, Vs1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
             if (r + 5 < nt) step(j_begin + r + 5, sb0, sb1, sa0, sa1, Ks0, Ks2, Vs1, Vs0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
-        }
-    } else {
-        // Step r = j - j_begin: K(j+1) sits in buffer (r+1)%2, V(j) in buffer r%2.
-        // Unrolled by two so that every LDS access names its buffer (the compiler
-        // then waits on a refill only before reads of the buffer being refilled).
-        for (int r = 0; r < nt; r += 2) {
-            step(j_begin + r, sa0, sa1, sb0, sb1, Ks1, Ks1, Vs0, Vs1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
-            if (r + 1 < nt)
-                step(j_begin + r + 1, sb0, sb1, sa0, sa1, Ks0, Ks0, Vs1, Vs0, nullptr, nullptr, nullptr, nullptr, nullptr,
-                     nullptr);
         }
     }
     wait_vmcnt<0>();  // nothing is left in flight when the wave ends
@@ -2066,11 +2029,12 @@ static hipError_t launch_pair(PrefillParams p, bool items, int mask, hipStream_t
 
 template <bool BF16, int D>
 static hipError_t launch_mfma_mask(PrefillParams p, int kernel, int mask, hipStream_t s) {
-    if constexpr (D == 256) return launch_pair<BF16>(p, kernel == kPrefillPairItems, mask, s);
-    if constexpr (D <= 128) {
+    if constexpr (D == 256) {
+        return launch_pair<BF16>(p, kernel == kPrefillPairItems, mask, s);
+    } else {
         if (kernel == kPrefillMfma8) return launch_mfma_nw<BF16, D, 8>(p, mask, s);
+        return launch_mfma_nw<BF16, D, 4>(p, mask, s);
     }
-    return launch_mfma_nw<BF16, D, 4>(p, mask, s);
 }
 
 template <int D>
