@@ -351,7 +351,8 @@ int attn_decode_workspace_size(int batch, int s_active, int n_q_heads, int head_
  * arithmetic only (no HIP call, no device memory): the entry points take their launch
  * from this same choice, so a caller or a test can see which kernel a shape exercises.
  * fp8_kv: K/V as FP8 codes (attn_prefill_fwd_fp8kv); packed: cumulative offsets given
- * (attn_prefill_varlen_fwd); has_positions: per-row positions given. Returns an
+ * (attn_prefill_varlen_fwd, whose batch, max_seqlen_q and max_seqlen_kv are then batch,
+ * seqlen_q and seqlen_kv here); has_positions: per-row positions given. Returns an
  * attn_prefill_kernel value (> 0), or minus ATTN_ERR_INVALID / ATTN_ERR_UNSUPPORTED for
  * arguments the entry points reject with that status, or 0 for an empty call. */
 typedef enum {
